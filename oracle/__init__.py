@@ -1,0 +1,8 @@
+"""fp64 CPU oracle for the Gated DeltaNet token mixer.
+
+Test infrastructure only: imported by tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py, never by the product path.
+"""
+from .gdn_oracle import chunk_factors, chunked, decode_step, recurrent, sequence_bounds, unrolled
+
+__all__ = ["recurrent", "chunked", "chunk_factors", "unrolled", "decode_step", "sequence_bounds"]

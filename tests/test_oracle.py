@@ -1,0 +1,318 @@
+"""Pins for the fp64 oracle: closed forms, identities and brute force.
+
+None of these re-types the oracle's update: each compares it against a
+statement that holds for the gated delta rule independently of how the oracle
+is written (special cases with a closed form, the semantic properties the
+podcast transcript's cue 14 states, a brute-force product form, algebraic
+invariants).  A dropped term, a wrong sign, a transposed state or a shifted
+index in the oracle fails at least one of them.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import chunk_factors, chunked, decode_step, recurrent, unrolled
+
+RTOL = 1e-11
+
+
+def rand_inputs(rng, B=1, T=16, Hqk=1, Hv=1, dk=8, dv=8, unit_keys=True, gate_scale=0.3):
+    q = rng.standard_normal((B, T, Hqk, dk))
+    k = rng.standard_normal((B, T, Hqk, dk))
+    if unit_keys:
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+        q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, Hv, dv))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, Hv))))
+    g = -gate_scale * np.logaddexp(0.0, rng.standard_normal((B, T, Hv)))
+    return q, k, v, g, beta
+
+
+def close(a, b, tol=RTOL):
+    a, b = np.asarray(a), np.asarray(b)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    scale = max(1.0, float(np.max(np.abs(b)))) if b.size else 1.0
+    np.testing.assert_allclose(a, b, rtol=0, atol=tol * scale)
+
+
+# ---------------------------------------------------------------- P1, P2 ----
+def test_p1_identity_gate_zero_write_keeps_state():
+    """alpha = 1, beta = 0: the state never changes and o_t = M0^T q_t."""
+    rng = np.random.default_rng(1)
+    q, k, v, g, beta = rand_inputs(rng, T=11, Hqk=2, Hv=4, dk=6, dv=5)
+    g[:] = 0.0
+    beta[:] = 0.0
+    S0 = rng.standard_normal((1, 4, 6, 5))
+    o, fin = recurrent(q, k, v, g, beta, initial_state=S0)
+    close(fin, S0)
+    head_of = np.arange(4) // 2
+    expect = np.einsum("thi,hij->thj", q[0][:, head_of], S0[0])
+    close(o[0], expect)
+
+
+def test_p2_pure_decay_scales_state_by_cumulative_gate():
+    """beta = 0: M_t = exp(sum_{s<=t} g_s) M0, o_t = exp(G_t) M0^T q_t (G across chunks)."""
+    rng = np.random.default_rng(2)
+    q, k, v, g, beta = rand_inputs(rng, T=40, Hqk=1, Hv=2, dk=4, dv=7)
+    beta[:] = 0.0
+    S0 = rng.standard_normal((1, 2, 4, 7))
+    G = np.cumsum(g[0], axis=0)  # [T, Hv]
+    expect_o = np.exp(G)[:, :, None] * np.einsum("ti,hij->thj", q[0, :, 0], S0[0])
+    expect_M = np.exp(G[-1])[:, None, None] * S0[0]
+    for fn in (lambda: recurrent(q, k, v, g, beta, initial_state=S0),
+               lambda: chunked(q, k, v, g, beta, 16, initial_state=S0)):
+        o, fin = fn()
+        close(o[0], expect_o)
+        close(fin[0], expect_M)
+
+
+# ------------------------------------------------------------ P3, P4, P5 ----
+def orthonormal_keys(rng, n, dk):
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    return Qm[:, :n].T  # n orthonormal rows
+
+
+def test_p3_orthonormal_keys_retrieve_stored_values_exactly():
+    """beta = 1, alpha = 1, orthonormal keys, M0 = 0: M_n^T k_j = v_j for all j."""
+    rng = np.random.default_rng(3)
+    dk, dv, n = 8, 5, 6
+    keys = orthonormal_keys(rng, n, dk)
+    k = keys[None, :, None, :]
+    q = rng.standard_normal((1, n, 1, dk))
+    v = rng.standard_normal((1, n, 1, dv))
+    g = np.zeros((1, n, 1))
+    beta = np.ones((1, n, 1))
+    _, fin = recurrent(q, k, v, g, beta)
+    close(keys @ fin[0, 0], v[0, :, 0])
+
+
+def test_p3_with_decay_retrieval_is_scaled_by_later_gates():
+    """Same, with decay: M_n^T k_j = prod_{s>j} alpha_s v_j."""
+    rng = np.random.default_rng(4)
+    dk, dv, n = 8, 3, 5
+    keys = orthonormal_keys(rng, n, dk)
+    k = keys[None, :, None, :]
+    q = rng.standard_normal((1, n, 1, dk))
+    v = rng.standard_normal((1, n, 1, dv))
+    g = -0.2 * rng.random((1, n, 1))
+    beta = np.ones((1, n, 1))
+    _, fin = recurrent(q, k, v, g, beta)
+    later = np.array([np.exp(g[0, j + 1:, 0].sum()) for j in range(n)])
+    close(keys @ fin[0, 0], later[:, None] * v[0, :, 0])
+
+
+def test_p4_query_equal_to_key_reads_back_the_written_value():
+    """beta_t = 1, |k_t| = 1, q_t = k_t: o_t = v_t for any history and any alpha."""
+    rng = np.random.default_rng(5)
+    q, k, v, g, beta = rand_inputs(rng, T=30, Hqk=1, Hv=1, dk=6, dv=4)
+    beta[:] = 1.0
+    S0 = rng.standard_normal((1, 1, 6, 4))
+    o, _ = recurrent(k, k, v, g, beta, initial_state=S0)
+    close(o, v)
+
+
+def test_p5_same_key_twice_leaves_one_corrected_note():
+    """beta = 1, alpha = 1, one unit key written with v1 then v2, from zero: M = k v2^T."""
+    rng = np.random.default_rng(6)
+    key = rng.standard_normal(7)
+    key /= np.linalg.norm(key)
+    v1, v2 = rng.standard_normal(3), rng.standard_normal(3)
+    k = np.stack([key, key])[None, :, None, :]
+    v = np.stack([v1, v2])[None, :, None, :]
+    q = rng.standard_normal((1, 2, 1, 7))
+    _, fin = recurrent(q, k, v, np.zeros((1, 2, 1)), np.ones((1, 2, 1)))
+    close(fin[0, 0], np.outer(key, v2))
+
+
+def test_hand_worked_two_token_example():
+    """Two tokens, dk = dv = 2, worked by hand.
+
+    alpha = 1/2 for both, beta = 1/2 for both, k1 = e1, k2 = e2, v1 = (2, 0),
+    v2 = (0, 4), q = k, M0 = [[1, 1], [1, 1]] (stored layout, rows = key dim).
+    Token 1: decayed M = [[.5, .5], [.5, .5]]; read under e1 = (.5, .5);
+      error = (1.5, -.5); write .5 * e1 (1.5, -.5) -> M1 = [[1.25, .25], [.5, .5]];
+      o1 = M1^T e1 = (1.25, .25).
+    Token 2: decayed M = [[.625, .125], [.25, .25]]; read under e2 = (.25, .25);
+      error = (-.25, 3.75); write .5 * e2 (-.25, 3.75) -> M2 = [[.625, .125], [.125, 2.125]];
+      o2 = M2^T e2 = (.125, 2.125).
+    """
+    q = np.array([[1.0, 0.0], [0.0, 1.0]])[None, :, None, :]
+    v = np.array([[2.0, 0.0], [0.0, 4.0]])[None, :, None, :]
+    g = np.log(np.full((1, 2, 1), 0.5))
+    beta = np.full((1, 2, 1), 0.5)
+    S0 = np.ones((1, 1, 2, 2))
+    for fn in (lambda: recurrent(q, q, v, g, beta, initial_state=S0),
+               lambda: chunked(q, q, v, g, beta, 2, initial_state=S0),
+               lambda: unrolled(q, q, v, g, beta, initial_state=S0)):
+        o, fin = fn()
+        close(o[0, :, 0], [[1.25, 0.25], [0.125, 2.125]], 1e-14)
+        close(fin[0, 0], [[0.625, 0.125], [0.125, 2.125]], 1e-14)
+
+
+# ------------------------------------------------------------------- P6 ----
+@pytest.mark.parametrize("dk,dv,T", [(5, 5, 8), (6, 3, 7), (3, 7, 5), (4, 4, 1)])
+def test_p6_unrolled_products_match_recurrence(dk, dv, T):
+    rng = np.random.default_rng(10 + dk * 10 + dv)
+    q, k, v, g, beta = rand_inputs(rng, T=T, Hqk=1, Hv=2, dk=dk, dv=dv, unit_keys=False, gate_scale=0.5)
+    S0 = rng.standard_normal((1, 2, dk, dv))  # non-symmetric, and dk != dv pins the orientation
+    o1, f1 = unrolled(q, k, v, g, beta, initial_state=S0, scale=0.7)
+    o2, f2 = recurrent(q, k, v, g, beta, initial_state=S0, scale=0.7)
+    close(o2, o1)
+    close(f2, f1)
+
+
+# ------------------------------------------------------------------- P7 ----
+@pytest.mark.parametrize("C", [1, 2, 3, 7, 16, 64, 100])
+def test_p7_chunked_matches_recurrence_at_any_chunk_size(C):
+    rng = np.random.default_rng(20 + C)
+    q, k, v, g, beta = rand_inputs(rng, B=2, T=100, Hqk=2, Hv=4, dk=8, dv=6)
+    S0 = rng.standard_normal((2, 4, 8, 6))
+    o1, f1 = recurrent(q, k, v, g, beta, initial_state=S0, scale=0.9)
+    o2, f2 = chunked(q, k, v, g, beta, C, initial_state=S0, scale=0.9)
+    close(o2, o1, 1e-10)
+    close(f2, f1, 1e-10)
+
+
+def test_p7_chunked_with_strong_gates_has_no_overflow():
+    """Large negative log-gates: exp(G_i - G_j) above the diagonal would overflow."""
+    rng = np.random.default_rng(27)
+    q, k, v, g, beta = rand_inputs(rng, T=64, dk=4, dv=4)
+    g[:] = -30.0
+    with np.errstate(over="raise"):
+        o2, f2 = chunked(q, k, v, g, beta, 64)
+    o1, f1 = recurrent(q, k, v, g, beta)
+    close(o2, o1, 1e-10)
+    close(f2, f1, 1e-10)
+
+
+# ------------------------------------------------------------------- P8 ----
+def test_p8_composition_and_decode_continuity():
+    rng = np.random.default_rng(30)
+    q, k, v, g, beta = rand_inputs(rng, T=50, Hqk=1, Hv=2, dk=5, dv=4)
+    S0 = rng.standard_normal((1, 2, 5, 4))
+    o_all, f_all = recurrent(q, k, v, g, beta, initial_state=S0)
+    o_a, f_a = chunked(q[:, :23], k[:, :23], v[:, :23], g[:, :23], beta[:, :23], 8, initial_state=S0)
+    o_b, f_b = chunked(q[:, 23:], k[:, 23:], v[:, 23:], g[:, 23:], beta[:, 23:], 8, initial_state=f_a)
+    close(np.concatenate([o_a, o_b], axis=1), o_all, 1e-10)
+    close(f_b, f_all, 1e-10)
+    state = S0[0][None]
+    for t in range(50):
+        o_t, state = decode_step(q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], state)
+        close(o_t[0], o_all[0, t], 1e-10)
+    close(state, f_all, 1e-10)
+
+
+# ------------------------------------------------------------------- P9 ----
+def test_p9_packed_equals_separate_and_batch_equals_separate():
+    rng = np.random.default_rng(40)
+    lens = [5, 0, 17, 1, 9]
+    T = sum(lens)
+    q, k, v, g, beta = rand_inputs(rng, T=T, Hqk=1, Hv=2, dk=4, dv=3)
+    S0 = rng.standard_normal((len(lens), 2, 4, 3))
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    o, fin = chunked(q, k, v, g, beta, 4, initial_state=S0, cu_seqlens=cu)
+    for n in range(len(lens)):
+        s, e = cu[n], cu[n + 1]
+        o_n, f_n = recurrent(q[:, s:e], k[:, s:e], v[:, s:e], g[:, s:e], beta[:, s:e], initial_state=S0[n:n + 1])
+        close(o[:, s:e], o_n, 1e-10)
+        close(fin[n], f_n[0], 1e-10)
+    close(fin[1], S0[1])  # empty sequence: final == initial (R15)
+    qb, kb, vb, gb, bb = rand_inputs(rng, B=3, T=10, Hqk=1, Hv=1, dk=4, dv=4)
+    ob, fb = recurrent(qb, kb, vb, gb, bb)
+    for b in range(3):
+        o1, f1 = recurrent(qb[b:b + 1], kb[b:b + 1], vb[b:b + 1], gb[b:b + 1], bb[b:b + 1])
+        close(ob[b:b + 1], o1)
+        close(fb[b], f1[0])
+
+
+# ------------------------------------------------------------------ P10 ----
+def test_p10_grouped_heads_equal_explicit_repeat():
+    rng = np.random.default_rng(50)
+    q, k, v, g, beta = rand_inputs(rng, T=12, Hqk=2, Hv=6, dk=4, dv=3)
+    o1, f1 = recurrent(q, k, v, g, beta)
+    rep = lambda x: np.repeat(x, 3, axis=2)  # v head h -> q/k head h // 3
+    o2, f2 = recurrent(rep(q), rep(k), v, g, beta)
+    close(o1, o2)
+    close(f1, f2)
+
+
+# ------------------------------------------------------------------ P11 ----
+def test_p11_value_columns_evolve_independently():
+    rng = np.random.default_rng(60)
+    q, k, v, g, beta = rand_inputs(rng, T=20, Hqk=1, Hv=1, dk=5, dv=6)
+    S0 = rng.standard_normal((1, 1, 5, 6))
+    o, fin = recurrent(q, k, v, g, beta, initial_state=S0)
+    cols = [1, 4]
+    o_c, f_c = recurrent(q, k, v[..., cols], g, beta, initial_state=S0[..., cols])
+    close(o[..., cols], o_c)
+    close(fin[..., cols], f_c)
+
+
+# ------------------------------------------------------------------ P12 ----
+def test_p12_chunk_transition_equals_product_of_token_transitions():
+    """exp(G_L) I - Ktilde^T W == A_L ... A_1 with A_t = alpha_t (I - beta_t k_t k_t^T), stored layout."""
+    rng = np.random.default_rng(70)
+    L, dk = 9, 6
+    K = rng.standard_normal((1, L, dk))
+    K /= np.linalg.norm(K, axis=-1, keepdims=True)
+    g = -0.3 * rng.random((1, L))
+    beta = rng.random((1, L))
+    f = chunk_factors(K, np.zeros((1, L, 1)), g, beta)
+    G = f["G"][0]
+    Kt = np.exp(G[-1] - G)[:, None] * K[0]
+    phi = np.exp(G[-1]) * np.eye(dk) - Kt.T @ f["W"][0]
+    prod = np.eye(dk)
+    for t in range(L):  # stored layout: M_t = A_t M_{t-1}, so the product grows on the left
+        prod = np.exp(g[0, t]) * (np.eye(dk) - beta[0, t] * np.outer(K[0, t], K[0, t])) @ prod
+    close(phi, prod)
+    # and T really inverts I + A
+    close(f["T"][0] @ (np.eye(L) + f["A"][0]), np.eye(L))
+
+
+# ------------------------------------------------------------------ P13 ----
+def test_p13_linear_in_state_and_values_and_in_query():
+    rng = np.random.default_rng(80)
+    q, k, v, g, beta = rand_inputs(rng, T=15, Hqk=1, Hv=2, dk=4, dv=3)
+    S0a, S0b = rng.standard_normal((2, 1, 2, 4, 3))
+    va = v
+    vb = rng.standard_normal(v.shape)
+    a, b = 0.7, -1.3
+    oa, fa = recurrent(q, k, va, g, beta, initial_state=S0a)
+    ob, fb = recurrent(q, k, vb, g, beta, initial_state=S0b)
+    oc, fc = recurrent(q, k, a * va + b * vb, g, beta, initial_state=a * S0a + b * S0b)
+    close(oc, a * oa + b * ob)
+    close(fc, a * fa + b * fb)
+    o2, _ = recurrent(q, k, va, g, beta, initial_state=S0a, scale=2.5)
+    close(o2, 2.5 * oa)
+
+
+# ------------------------------------------------------------------ P14 ----
+def test_p14_zero_values_contract_the_state():
+    rng = np.random.default_rng(90)
+    q, k, v, g, beta = rand_inputs(rng, T=25, Hqk=1, Hv=1, dk=6, dv=6)
+    v[:] = 0.0
+    state = rng.standard_normal((1, 1, 6, 6))
+    for t in range(25):
+        prev = np.linalg.norm(state)
+        _, state = decode_step(q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], state)
+        assert np.linalg.norm(state) <= np.exp(g[0, t, 0]) * prev * (1 + 1e-12)
+
+
+def test_inputs_module_recipe():
+    """The shared generator: unit q/k, beta in (0,1), g <= 0, lengths in range, determinism."""
+    import torch
+    from linear_attention_token_chunked_amd.inputs import make_decode, make_prefill
+
+    a = make_prefill(1, 64, 2, 4, 16, 8, "bf16", init_state=True, num_packed=5, seed=3)
+    b = make_prefill(1, 64, 2, 4, 16, 8, "bf16", init_state=True, num_packed=5, seed=3)
+    for key in a:
+        assert torch.equal(a[key], b[key])
+    cu = a["cu_seqlens"].numpy()
+    lens = np.diff(cu)
+    assert cu[0] == 0 and np.all(lens >= 16) and np.all(lens <= 32768)
+    assert a["q"].shape == (1, int(cu[-1]), 2, 16) and a["initial_state"].shape == (5, 4, 16, 8)
+    nrm = a["k"].float().norm(dim=-1)
+    assert torch.allclose(nrm, torch.ones_like(nrm), atol=1e-2)
+    assert float(a["beta"].min()) > 0 and float(a["beta"].max()) < 1 and float(a["g"].max()) <= 0
+    d = make_decode(3, 1, 2, 8, 8, steps=4, dtype="fp32")
+    assert d["q"].shape == (4, 3, 1, 8) and d["state"].shape == (3, 2, 8, 8)
