@@ -1,0 +1,135 @@
+/*
+ * gdn.h - C ABI of the MI355X (gfx950) Gated DeltaNet (GDN) token mixer.
+ *
+ * The operation is the gated delta rule that the podcast transcript on
+ * "On the Design of Qwen3.8-Next Architecture" describes in cue 14: per token,
+ * a decay alpha shrinks the whole per-head state, the rule reads what the state
+ * holds under the current key, and writes back only the error between the new
+ * value and that reading, scaled by a write strength beta.  Cue 4 of the same
+ * transcript: the state has a fixed size per head and the cost is linear in the
+ * sequence length.  For one head, in math layout (S is dv x dk):
+ *
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t (scale * q_t).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - States are stored transposed, M = S^T, as fp32 [N, Hv, dk, dv] row-major:
+ *    element (n, h, i, j) = S_{n,h}[j][i], i over the key dim, j over the value dim.
+ *  - g is log(alpha) (fp32, <= 0 for a decaying gate); beta is the write strength
+ *    after any sigmoid (fp32).  Both are per value head.
+ *  - Value head h reads query/key head h / (Hv / Hqk)  (Hv must be a multiple of Hqk).
+ *  - q, k, v, o are dtype (fp32 or bf16, see gdn_dtype_t); o is rounded from fp32
+ *    accumulators to nearest even.  All tensors are dense, row-major and contiguous.
+ *  - Every pointer except `d` is a DEVICE pointer owned by the caller.  The library
+ *    allocates no device memory, keeps no mutable global state and may be called
+ *    concurrently from several host threads on different streams.
+ *  - Work is enqueued asynchronously on `stream` (0 = the null stream); buffers must
+ *    stay alive until the stream has passed the work.
+ *  - Errors: every call returns a status and never throws, aborts or prints.  All
+ *    host-visible arguments are validated before any HIP call.  A failed launch
+ *    returns GDN_STATUS_HIP_ERROR; faults inside kernels surface at the caller's
+ *    next synchronisation.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN_STATUS_SUCCESS = 0,
+  GDN_STATUS_INVALID_VALUE = 1,          /* null required pointer, bad dimension, bad combination */
+  GDN_STATUS_NOT_SUPPORTED = 2,          /* valid but not built: head dims, chunk size, dtype */
+  GDN_STATUS_MISALIGNED = 3,             /* a pointer is not aligned as documented */
+  GDN_STATUS_WORKSPACE_TOO_SMALL = 4,    /* workspace_bytes < gdn_fwd_chunked_workspace_size() */
+  GDN_STATUS_HIP_ERROR = 5               /* a HIP runtime call or kernel launch failed */
+} gdn_status_t;
+
+typedef enum { GDN_DTYPE_FLOAT32 = 0, GDN_DTYPE_BFLOAT16 = 1 } gdn_dtype_t;
+
+typedef struct {
+  int32_t batch;        /* B: batch rows of q/k/v/o; must be 1 when cu_seqlens is given   */
+  int32_t seqlen;       /* T: tokens per row (total packed tokens with cu_seqlens); >= 0  */
+  int32_t num_seqs;     /* N: number of sequences = B, or len(cu_seqlens) - 1             */
+  int32_t num_qk_heads; /* Hqk >= 1                                                       */
+  int32_t num_v_heads;  /* Hv >= 1, a multiple of Hqk                                     */
+  int32_t head_dim_k;   /* dk: 64 or 128                                                  */
+  int32_t head_dim_v;   /* dv: 64 or 128 (prefill: dv == dk)                              */
+  int32_t chunk_size;   /* prefill chunk length C; 64 is the one built                    */
+  float scale;          /* multiplies q; 1.0 gives o_t = S_t q_t                          */
+  gdn_dtype_t dtype;    /* element type of q, k, v, o                                     */
+} gdn_dims_t;
+
+/*
+ * Bytes of device workspace gdn_fwd_chunked needs for these dims (0 when none).
+ * Returns 0 as well for dims that gdn_fwd_chunked would reject.
+ */
+size_t gdn_fwd_chunked_workspace_size(const gdn_dims_t* d);
+
+/*
+ * Chunked-parallel prefill: runs the recurrence above over every sequence.
+ *
+ * The sequence is cut into chunks of C tokens (restarting at every sequence
+ * start; the last chunk may be short).  Per chunk and value head, with M the
+ * state entering the chunk and G the inclusive in-chunk cumulative sum of g,
+ * the chunk is applied as the UT/WY form of the same recurrence:
+ *   A = strict_lower(diag(beta) (exp(G_i - G_j) * K K^T)),  T = (I + A)^-1,
+ *   W = T diag(beta exp G) K,  U = T diag(beta) V - W M,
+ *   O = scale (diag(exp G) Q M + lower_incl_diag(exp(G_i - G_j) * Q K^T) U),
+ *   M <- exp(G_C) M + (diag(exp(G_C - G)) K)^T U.
+ *
+ *   q, k           [B, T, Hqk, dk]  dtype, 16-byte aligned
+ *   v              [B, T, Hv, dv]   dtype, 16-byte aligned
+ *   g, beta        [B, T, Hv]       fp32, 4-byte aligned
+ *   initial_state  [N, Hv, dk, dv]  fp32, 16-byte aligned, or NULL for zeros
+ *   cu_seqlens     [N + 1] int32 on the device, or NULL.  With it B must be 1 and
+ *                  sequence n is tokens [cu[n], cu[n+1]).  Its contents are the
+ *                  caller's contract and are not checked: cu[0] = 0, non-decreasing,
+ *                  cu[N] = T.  Empty sequences are allowed (final = initial).
+ *   o              [B, T, Hv, dv]   dtype, 16-byte aligned; every token is written
+ *   final_state    [N, Hv, dk, dv]  fp32, 16-byte aligned, or NULL (not written).
+ *                  It may be the same buffer as initial_state (in-place update);
+ *                  any other overlap of an output with an input is undefined.
+ *   workspace      device buffer of at least gdn_fwd_chunked_workspace_size(d)
+ *                  bytes, 256-byte aligned (may be NULL when that size is 0).
+ * Supported: dk = dv in {64, 128}, C = 64, dtype fp32 or bf16.
+ */
+gdn_status_t gdn_fwd_chunked(const gdn_dims_t* d, const void* q, const void* k, const void* v,
+                             const float* g, const float* beta, const float* initial_state,
+                             const int32_t* cu_seqlens, void* o, float* final_state,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Single-token recurrent decode step for N independent sequences, updating the
+ * state in place.  Per (sequence, value head), in stored layout:
+ *   r = M^T k,  p = M^T q,  u = beta (v - alpha r),
+ *   o = scale (alpha p + (k . q) u),  M <- alpha M + k u^T,
+ * which is exactly one step of the recurrence above, with o read after the write.
+ *
+ *   d->num_seqs = N, d->batch must equal N, d->seqlen must be 1; chunk_size is ignored.
+ *   q, k   [N, Hqk, dk]       dtype, 16-byte aligned
+ *   v      [N, Hv, dv]        dtype, 16-byte aligned
+ *   g, beta [N, Hv]           fp32
+ *   state  [N, Hv, dk, dv]    fp32, 16-byte aligned, read and written in place
+ *   o      [N, Hv, dv]        dtype, 16-byte aligned
+ * Supported: dk, dv in {64, 128}, dtype fp32 or bf16.
+ */
+gdn_status_t gdn_decode_step(const gdn_dims_t* d, const void* q, const void* k, const void* v,
+                             const float* g, const float* beta, float* state, void* o,
+                             hipStream_t stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* gdn_status_string(gdn_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

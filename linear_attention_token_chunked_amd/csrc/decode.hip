@@ -1,0 +1,148 @@
+// Single-token decode step of the gated delta rule (one workgroup per
+// (sequence, value head)), gfx950.
+//
+// The step is the recurrence from the podcast transcript on "On the Design of
+// Qwen3.8-Next Architecture" (cue 14: decay the state, read under the key,
+// write the error), applied in the stored layout M = S^T (dk x dv):
+//   r = M^T k, p = M^T q            (one read pass over M)
+//   u = beta (v - alpha r)
+//   o = scale (alpha p + (k.q) u)   (= M_new^T q)
+//   M <- alpha M + k u^T            (one write pass)
+// Each state element is read once and written once, so the kernel is bound by
+// HBM bandwidth: a workgroup streams its dk x dv fp32 slice (64 KiB at 128x128)
+// with 16-byte loads, keeps it in registers across the dk-reduction, and
+// writes it back.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace gdn {
+namespace {
+
+constexpr int kDecodeThreads = 256;
+
+template <class T, int DK, int DV>
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
+    T* __restrict__ o, int Hqk, int Hv, float scale) {
+  constexpr int TPR = DV / 4;                  // threads per state row (one float4 each)
+  constexpr int RG = kDecodeThreads / TPR;     // row groups
+  constexpr int RPT = DK / RG;                 // rows per thread: rg, rg + RG, ...
+  constexpr int GPW = 64 / TPR;                // row groups inside one wavefront
+  constexpr int NWAVE = kDecodeThreads / 64;
+  static_assert(DK % RG == 0 && GPW >= 1, "shape");
+
+  const int unit = blockIdx.x;  // n * Hv + h
+  const int n = unit / Hv;
+  const int h = unit - n * Hv;
+  const int hq = h / (Hv / Hqk);
+  const int tid = threadIdx.x;
+  const int cg = tid % TPR;
+  const int rg = tid / TPR;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  __shared__ float sk[DK];
+  __shared__ float sq[DK];
+  __shared__ floatx4 red_r[NWAVE][TPR];
+  __shared__ floatx4 red_p[NWAVE][TPR];
+  __shared__ float red_kq[NWAVE];
+
+  // Issue the whole state slice first: these loads dominate the run time.
+  float* M = state + static_cast<size_t>(unit) * DK * DV;
+  floatx4 m[RPT];
+#pragma unroll
+  for (int r = 0; r < RPT; ++r)
+    m[r] = *reinterpret_cast<const floatx4*>(M + static_cast<size_t>(rg + RG * r) * DV + 4 * cg);
+
+  const T* kp = k + (static_cast<size_t>(n) * Hqk + hq) * DK;
+  const T* qp = q + (static_cast<size_t>(n) * Hqk + hq) * DK;
+  for (int i = tid; i < DK; i += kDecodeThreads) {
+    sk[i] = to_float(kp[i]);
+    sq[i] = to_float(qp[i]);
+  }
+  const float alpha = expf(g[unit]);
+  const float b = beta[unit];
+  const T* vp = v + static_cast<size_t>(unit) * DV + 4 * cg;
+  const float v0 = to_float(vp[0]), v1 = to_float(vp[1]), v2 = to_float(vp[2]), v3 = to_float(vp[3]);
+  __syncthreads();
+
+  floatx4 r = zero4(), p = zero4();
+  float kq = 0.f;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const float ki = sk[rg + RG * i], qi = sq[rg + RG * i];
+    r += ki * m[i];
+    p += qi * m[i];
+    kq += ki * qi;
+  }
+  // Sum over the row groups inside the wavefront ...
+#pragma unroll
+  for (int off = TPR; off < 64; off <<= 1) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      r[c] += __shfl_xor(r[c], off);
+      p[c] += __shfl_xor(p[c], off);
+    }
+    kq += __shfl_xor(kq, off);
+  }
+  // ... then across wavefronts through LDS.
+  if (lane < TPR) {
+    red_r[wave][cg] = r;
+    red_p[wave][cg] = p;
+    if (lane == 0) red_kq[wave] = kq;
+  }
+  __syncthreads();
+  r = red_r[0][cg];
+  p = red_p[0][cg];
+  kq = red_kq[0];
+#pragma unroll
+  for (int w = 1; w < NWAVE; ++w) {
+    r += red_r[w][cg];
+    p += red_p[w][cg];
+    kq += red_kq[w];
+  }
+  floatx4 u;
+  u[0] = b * (v0 - alpha * r[0]);
+  u[1] = b * (v1 - alpha * r[1]);
+  u[2] = b * (v2 - alpha * r[2]);
+  u[3] = b * (v3 - alpha * r[3]);
+
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const float ki = sk[rg + RG * i];
+    *reinterpret_cast<floatx4*>(M + static_cast<size_t>(rg + RG * i) * DV + 4 * cg) = alpha * m[i] + ki * u;
+  }
+  if (rg == 0) {
+    const floatx4 ov = scale * (alpha * p + kq * u);
+    *reinterpret_cast<typename Vec4<T>::type*>(o + static_cast<size_t>(unit) * DV + 4 * cg) =
+        pack4<T>(ov[0], ov[1], ov[2], ov[3]);
+  }
+}
+
+template <class T, int DK, int DV>
+hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
+  const int units = a.num_seqs * a.Hv;
+  if (units == 0) return hipSuccess;
+  decode_kernel<T, DK, DV><<<dim3(units), dim3(kDecodeThreads), 0, stream>>>(
+      static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.g, a.beta,
+      a.state, static_cast<T*>(a.o), a.Hqk, a.Hv, a.scale);
+  return hipGetLastError();
+}
+
+template <class T>
+hipError_t dispatch_dims(const DecodeArgs& a, hipStream_t stream) {
+  if (a.dk == 128 && a.dv == 128) return launch<T, 128, 128>(a, stream);
+  if (a.dk == 64 && a.dv == 64) return launch<T, 64, 64>(a, stream);
+  if (a.dk == 128 && a.dv == 64) return launch<T, 128, 64>(a, stream);
+  if (a.dk == 64 && a.dv == 128) return launch<T, 64, 128>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  return a.bf16 ? dispatch_dims<bf16>(a, stream) : dispatch_dims<float>(a, stream);
+}
+
+}  // namespace gdn

@@ -1,0 +1,128 @@
+// C ABI of libgdn: argument validation and dispatch to the gfx950 launchers.
+// Every host-visible argument is checked before the first HIP call, so invalid
+// calls never touch the device.  Nothing here allocates, logs or keeps state.
+#include "gdn.h"
+
+#include <stdint.h>
+
+#include "launch.hpp"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+
+// Checks shared by both entry points.
+gdn_status_t check_common(const gdn_dims_t* d) {
+  if (!d) return GDN_STATUS_INVALID_VALUE;
+  if (d->num_qk_heads < 1 || d->num_v_heads < 1 || d->head_dim_k < 1 || d->head_dim_v < 1 || d->num_seqs < 0)
+    return GDN_STATUS_INVALID_VALUE;
+  if (d->num_v_heads % d->num_qk_heads != 0) return GDN_STATUS_INVALID_VALUE;
+  if (d->dtype != GDN_DTYPE_FLOAT32 && d->dtype != GDN_DTYPE_BFLOAT16) return GDN_STATUS_INVALID_VALUE;
+  if (!head_dim_ok(d->head_dim_k) || !head_dim_ok(d->head_dim_v)) return GDN_STATUS_NOT_SUPPORTED;
+  return GDN_STATUS_SUCCESS;
+}
+
+gdn_status_t from_hip(hipError_t e) { return e == hipSuccess ? GDN_STATUS_SUCCESS : GDN_STATUS_HIP_ERROR; }
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn_fwd_chunked_workspace_size(const gdn_dims_t* d) {
+  (void)d;
+  return 0;  // the fused prefill keeps every intermediate in LDS and registers
+}
+
+gdn_status_t gdn_fwd_chunked(const gdn_dims_t* d, const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, const float* initial_state, const int32_t* cu_seqlens, void* o,
+                             float* final_state, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  gdn_status_t st = check_common(d);
+  if (st != GDN_STATUS_SUCCESS) return st;
+  if (d->batch < 0 || d->seqlen < 0) return GDN_STATUS_INVALID_VALUE;
+  if (cu_seqlens) {
+    if (d->batch != 1) return GDN_STATUS_INVALID_VALUE;
+  } else if (d->num_seqs != d->batch) {
+    return GDN_STATUS_INVALID_VALUE;
+  }
+  if (d->chunk_size != 64) return GDN_STATUS_NOT_SUPPORTED;
+  if (d->head_dim_k != d->head_dim_v) return GDN_STATUS_NOT_SUPPORTED;
+  if (d->dtype == GDN_DTYPE_FLOAT32 && d->head_dim_k != 64) return GDN_STATUS_NOT_SUPPORTED;
+  const bool has_tokens = static_cast<int64_t>(d->batch) * d->seqlen > 0;
+  if (has_tokens && (!q || !k || !v || !g || !beta || !o)) return GDN_STATUS_INVALID_VALUE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(g, 4) ||
+      !aligned(beta, 4) || !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(cu_seqlens, 4) ||
+      !aligned(workspace, 256))
+    return GDN_STATUS_MISALIGNED;
+  if (workspace_bytes < gdn_fwd_chunked_workspace_size(d)) return GDN_STATUS_WORKSPACE_TOO_SMALL;
+  if (d->num_seqs == 0) return GDN_STATUS_SUCCESS;
+  // Token indices are 32-bit inside the kernels.
+  if (static_cast<int64_t>(d->batch) * d->seqlen >= (int64_t(1) << 31)) return GDN_STATUS_NOT_SUPPORTED;
+
+  gdn::PrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.initial_state = initial_state;
+  a.cu_seqlens = cu_seqlens;
+  a.o = o;
+  a.final_state = final_state;
+  a.batch = d->batch;
+  a.seqlen = d->seqlen;
+  a.num_seqs = d->num_seqs;
+  a.Hqk = d->num_qk_heads;
+  a.Hv = d->num_v_heads;
+  a.dk = d->head_dim_k;
+  a.dv = d->head_dim_v;
+  a.chunk = d->chunk_size;
+  a.scale = d->scale;
+  a.bf16 = d->dtype == GDN_DTYPE_BFLOAT16;
+  return from_hip(gdn::launch_prefill(a, stream));
+}
+
+gdn_status_t gdn_decode_step(const gdn_dims_t* d, const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, float* state, void* o, hipStream_t stream) {
+  gdn_status_t st = check_common(d);
+  if (st != GDN_STATUS_SUCCESS) return st;
+  if (d->seqlen != 1 || d->batch != d->num_seqs) return GDN_STATUS_INVALID_VALUE;
+  if (d->num_seqs == 0) return GDN_STATUS_SUCCESS;
+  if (!q || !k || !v || !g || !beta || !state || !o) return GDN_STATUS_INVALID_VALUE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(state, 16) ||
+      !aligned(g, 4) || !aligned(beta, 4))
+    return GDN_STATUS_MISALIGNED;
+  if (static_cast<int64_t>(d->num_seqs) * d->num_v_heads >= (int64_t(1) << 31)) return GDN_STATUS_NOT_SUPPORTED;
+
+  gdn::DecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.state = state;
+  a.o = o;
+  a.num_seqs = d->num_seqs;
+  a.Hqk = d->num_qk_heads;
+  a.Hv = d->num_v_heads;
+  a.dk = d->head_dim_k;
+  a.dv = d->head_dim_v;
+  a.scale = d->scale;
+  a.bf16 = d->dtype == GDN_DTYPE_BFLOAT16;
+  return from_hip(gdn::launch_decode(a, stream));
+}
+
+const char* gdn_status_string(gdn_status_t s) {
+  switch (s) {
+    case GDN_STATUS_SUCCESS: return "GDN_STATUS_SUCCESS";
+    case GDN_STATUS_INVALID_VALUE: return "GDN_STATUS_INVALID_VALUE: invalid argument";
+    case GDN_STATUS_NOT_SUPPORTED: return "GDN_STATUS_NOT_SUPPORTED: configuration not built";
+    case GDN_STATUS_MISALIGNED: return "GDN_STATUS_MISALIGNED: pointer not aligned";
+    case GDN_STATUS_WORKSPACE_TOO_SMALL: return "GDN_STATUS_WORKSPACE_TOO_SMALL";
+    case GDN_STATUS_HIP_ERROR: return "GDN_STATUS_HIP_ERROR: HIP call or kernel launch failed";
+  }
+  return "GDN_STATUS_UNKNOWN";
+}
+
+}  // extern "C"

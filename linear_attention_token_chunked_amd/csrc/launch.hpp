@@ -1,0 +1,36 @@
+// Internal interface between the C ABI (gdn_api.cpp) and the kernel launchers.
+// Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct DecodeArgs {
+  const void *q, *k, *v;
+  const float *g, *beta;
+  float* state;
+  void* o;
+  int num_seqs, Hqk, Hv, dk, dv;
+  float scale;
+  bool bf16;
+};
+
+struct PrefillArgs {
+  const void *q, *k, *v;
+  const float *g, *beta;
+  const float* initial_state;  // may be null (zeros)
+  const int32_t* cu_seqlens;   // may be null (batch rows are the sequences)
+  void* o;
+  float* final_state;          // may be null
+  int batch, seqlen, num_seqs, Hqk, Hv, dk, dv, chunk;
+  float scale;
+  bool bf16;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace gdn

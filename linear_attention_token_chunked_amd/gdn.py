@@ -1,0 +1,186 @@
+"""Thin ctypes binding of libgdn.so (the C ABI in include/gdn.h).
+
+Argument marshalling only: shapes and dtypes are checked, outputs are
+allocated with torch on the inputs' device, and the call is enqueued on
+torch's current HIP stream.  Every step of the mixer runs in the library's
+gfx950 kernels; there is no other implementation behind these functions, and
+importing this module fails loudly when the library has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
+
+STATUS_SUCCESS = 0
+
+
+class Dims(ctypes.Structure):
+    """Mirror of gdn_dims_t."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("seqlen", ctypes.c_int32),
+        ("num_seqs", ctypes.c_int32),
+        ("num_qk_heads", ctypes.c_int32),
+        ("num_v_heads", ctypes.c_int32),
+        ("head_dim_k", ctypes.c_int32),
+        ("head_dim_v", ctypes.c_int32),
+        ("chunk_size", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("dtype", ctypes.c_int),
+    ]
+
+
+DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1}
+
+EXPORTED = ("gdn_fwd_chunked_workspace_size", "gdn_fwd_chunked", "gdn_decode_step", "gdn_status_string")
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build it first (python -m linear_attention_token_chunked_amd.build)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, fp, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t
+    lib.gdn_fwd_chunked_workspace_size.argtypes = [ctypes.POINTER(Dims)]
+    lib.gdn_fwd_chunked_workspace_size.restype = sz
+    lib.gdn_fwd_chunked.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, fp, fp, fp, vp, vp, fp, vp, sz, vp]
+    lib.gdn_fwd_chunked.restype = ctypes.c_int
+    lib.gdn_decode_step.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, fp, fp, fp, vp, vp]
+    lib.gdn_decode_step.restype = ctypes.c_int
+    lib.gdn_status_string.argtypes = [ctypes.c_int]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def status_string(code: int) -> str:
+    return lib.gdn_status_string(code).decode()
+
+
+def _check(code: int):
+    if code != STATUS_SUCCESS:
+        raise RuntimeError(status_string(code))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, device, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def make_dims(B, T, N, Hqk, Hv, dk, dv, chunk_size, scale, dtype) -> Dims:
+    return Dims(B, T, N, Hqk, Hv, dk, dv, chunk_size, float(scale), DTYPE_CODE[dtype])
+
+
+def fwd_chunked_workspace_size(dims: Dims) -> int:
+    return int(lib.gdn_fwd_chunked_workspace_size(ctypes.byref(dims)))
+
+
+def fwd_chunked(q, k, v, g, beta, *, initial_state=None, cu_seqlens=None, chunk_size=64, scale=1.0,
+                output_final_state=True, out=None, final_state=None):
+    """Chunked prefill: (o, final_state) for q, k [B, T, Hqk, dk], v [B, T, Hv, dv], g, beta [B, T, Hv].
+
+    initial_state / final_state are fp32 [N, Hv, dk, dv]; cu_seqlens is int32 [N + 1] on the device
+    (then B must be 1).  ``out`` and ``final_state`` may be given to reuse buffers; final_state may be
+    the initial_state tensor itself for an in-place update.
+    """
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    _need(q, "q", q.dtype, dev, 4)
+    if q.dtype not in DTYPE_CODE:
+        raise TypeError("q, k, v must be float32 or bfloat16")
+    B, T, Hqk, dk = q.shape
+    _need(k, "k", q.dtype, dev, 4)
+    _need(v, "v", q.dtype, dev, 4)
+    Hv, dv = v.shape[2], v.shape[3]
+    if k.shape != q.shape or v.shape[:2] != (B, T):
+        raise ValueError("q, k, v shapes disagree")
+    _need(g, "g", torch.float32, dev, 3)
+    _need(beta, "beta", torch.float32, dev, 3)
+    if g.shape != (B, T, Hv) or beta.shape != (B, T, Hv):
+        raise ValueError("g and beta must be [B, T, Hv]")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev, 1)
+        N = cu_seqlens.shape[0] - 1
+    else:
+        N = B
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, dev, 4)
+        if initial_state.shape != (N, Hv, dk, dv):
+            raise ValueError("initial_state must be [N, Hv, dk, dv]")
+    if out is None:
+        out = torch.empty((B, T, Hv, dv), dtype=q.dtype, device=dev)
+    else:
+        _need(out, "out", q.dtype, dev, 4)
+        if out.shape != (B, T, Hv, dv):
+            raise ValueError("out must be [B, T, Hv, dv]")
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, dev, 4)
+        if final_state.shape != (N, Hv, dk, dv):
+            raise ValueError("final_state must be [N, Hv, dk, dv]")
+    dims = make_dims(B, T, N, Hqk, Hv, dk, dv, chunk_size, scale, q.dtype)
+    ws_bytes = fwd_chunked_workspace_size(dims)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    with torch.cuda.device(dev):
+        code = lib.gdn_fwd_chunked(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                   _ptr(initial_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state), _ptr(ws),
+                                   ctypes.c_size_t(ws_bytes), _stream(dev))
+    _check(code)
+    return out, final_state
+
+
+def decode_step(q, k, v, g, beta, state, *, scale=1.0, out=None):
+    """One decode step for N sequences; updates ``state`` [N, Hv, dk, dv] fp32 in place, returns o [N, Hv, dv]."""
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    if q.dtype not in DTYPE_CODE:
+        raise TypeError("q, k, v must be float32 or bfloat16")
+    _need(q, "q", q.dtype, dev, 3)
+    N, Hqk, dk = q.shape
+    _need(k, "k", q.dtype, dev, 3)
+    _need(v, "v", q.dtype, dev, 3)
+    Hv, dv = v.shape[1], v.shape[2]
+    if k.shape != q.shape or v.shape[0] != N:
+        raise ValueError("q, k, v shapes disagree")
+    _need(g, "g", torch.float32, dev, 2)
+    _need(beta, "beta", torch.float32, dev, 2)
+    _need(state, "state", torch.float32, dev, 4)
+    if g.shape != (N, Hv) or beta.shape != (N, Hv) or state.shape != (N, Hv, dk, dv):
+        raise ValueError("g, beta must be [N, Hv] and state [N, Hv, dk, dv]")
+    if out is None:
+        out = torch.empty((N, Hv, dv), dtype=q.dtype, device=dev)
+    else:
+        _need(out, "out", q.dtype, dev, 3)
+    dims = make_dims(N, 1, N, Hqk, Hv, dk, dv, 64, scale, q.dtype)
+    with torch.cuda.device(dev):
+        code = lib.gdn_decode_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                                   _ptr(out), _stream(dev))
+    _check(code)
+    return out

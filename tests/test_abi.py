@@ -1,0 +1,136 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects invalid arguments before making any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+LIB = os.path.join(ROOT, "linear_attention_token_chunked_amd", "libgdn.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libgdn.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gdn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_four_entry_points():
+    assert declared_functions() == sorted(
+        ["gdn_decode_step", "gdn_fwd_chunked", "gdn_fwd_chunked_workspace_size", "gdn_status_string"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    from linear_attention_token_chunked_amd import gdn as m
+
+    return m
+
+
+def dims(gdn, **kw):
+    base = dict(B=1, T=128, N=1, Hqk=2, Hv=4, dk=128, dv=128, chunk_size=64, scale=1.0)
+    base.update(kw)
+    dtype = kw.pop("dtype", None)
+    import torch
+
+    d = gdn.make_dims(base["B"], base["T"], base["N"], base["Hqk"], base["Hv"], base["dk"], base["dv"],
+                      base["chunk_size"], base["scale"], torch.bfloat16)
+    if dtype is not None:
+        d.dtype = dtype
+    return d
+
+
+FAKE = 1 << 20  # an aligned, never-dereferenced address: validation must reject before using it
+
+
+def call_fwd(gdn, d, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=0, cu=0, o=FAKE, hT=0, ws=0, ws_bytes=0):
+    P = ctypes.c_void_p
+    return gdn.lib.gdn_fwd_chunked(ctypes.byref(d), P(q), P(k), P(v), P(g), P(beta), P(h0), P(cu), P(o), P(hT), P(ws),
+                                   ctypes.c_size_t(ws_bytes), P(0))
+
+
+def call_dec(gdn, d, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, state=FAKE, o=FAKE):
+    P = ctypes.c_void_p
+    return gdn.lib.gdn_decode_step(ctypes.byref(d), P(q), P(k), P(v), P(g), P(beta), P(state), P(o), P(0))
+
+
+INVALID, NOT_SUPPORTED, MISALIGNED = 1, 2, 3
+
+
+def test_status_strings(gdn):
+    for code in range(6):
+        assert gdn.status_string(code).startswith("GDN_STATUS_")
+    assert gdn.status_string(77) == "GDN_STATUS_UNKNOWN"
+
+
+def test_null_dims_rejected(gdn):
+    P = ctypes.c_void_p
+    assert gdn.lib.gdn_fwd_chunked(None, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(0), P(0), P(FAKE), P(0),
+                                   P(0), ctypes.c_size_t(0), P(0)) == INVALID
+    assert gdn.lib.gdn_decode_step(None, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                                   P(0)) == INVALID
+    assert gdn.lib.gdn_fwd_chunked_workspace_size(None) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hv=3), INVALID),                 # Hv not a multiple of Hqk
+    (dict(Hqk=0), INVALID),
+    (dict(N=2), INVALID),                  # N != B without cu_seqlens
+    (dict(T=-1), INVALID),
+    (dict(dk=96, dv=96), NOT_SUPPORTED),   # head dims not built
+    (dict(dk=128, dv=64), NOT_SUPPORTED),  # prefill needs dk == dv
+    (dict(chunk_size=32), NOT_SUPPORTED),
+    (dict(dtype=7), INVALID),
+])
+def test_fwd_invalid_dims(gdn, kw, code):
+    assert call_fwd(gdn, dims(gdn, **kw)) == code
+
+
+def test_fwd_fp32_needs_dk64(gdn):
+    d = dims(gdn, dtype=0)
+    assert call_fwd(gdn, d) == NOT_SUPPORTED
+
+
+def test_fwd_null_and_misaligned_pointers(gdn):
+    d = dims(gdn)
+    assert call_fwd(gdn, d, q=0) == INVALID
+    assert call_fwd(gdn, d, o=0) == INVALID
+    assert call_fwd(gdn, d, g=0) == INVALID
+    assert call_fwd(gdn, d, v=FAKE + 8) == MISALIGNED
+    assert call_fwd(gdn, d, hT=FAKE + 4) == MISALIGNED
+    assert call_fwd(gdn, d, beta=FAKE + 2) == MISALIGNED
+
+
+def test_fwd_cu_seqlens_requires_batch_one(gdn):
+    d = dims(gdn, B=2, N=3)
+    assert call_fwd(gdn, d, cu=FAKE) == INVALID
+
+
+def test_fwd_empty_work_is_a_no_op_success(gdn):
+    # zero sequences: nothing to launch, so success without touching the device
+    assert call_fwd(gdn, dims(gdn, B=0, N=0)) == 0
+
+
+def test_decode_invalid(gdn):
+    assert call_dec(gdn, dims(gdn, T=2)) == INVALID           # one token per step
+    assert call_dec(gdn, dims(gdn, B=2, N=3, T=1)) == INVALID  # batch must equal N
+    assert call_dec(gdn, dims(gdn, T=1, Hv=5)) == INVALID
+    assert call_dec(gdn, dims(gdn, T=1, dk=32)) == NOT_SUPPORTED
+    assert call_dec(gdn, dims(gdn, T=1), state=0) == INVALID
+    assert call_dec(gdn, dims(gdn, T=1), state=FAKE + 4) == MISALIGNED
+    assert call_dec(gdn, dims(gdn, T=1, B=0, N=0)) == 0
+
+
+def test_workspace_size_is_zero_for_the_fused_prefill(gdn):
+    assert gdn.fwd_chunked_workspace_size(dims(gdn)) == 0

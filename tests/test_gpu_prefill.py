@@ -1,0 +1,204 @@
+"""GPU parity of gdn_fwd_chunked against the fp64 oracle (through the C ABI).
+
+Small cases compare every element of o and the final states with the oracle's
+token recurrence; they span several chunks and a ragged tail.  The full-size
+workloads run in the launch configuration the bench times and are compared on
+sampled (sequence, value head) units, each over its whole length.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import recurrent
+from parity import TOL, assert_close, f64, flush, rel_l2, to_dev, unit_oracle
+
+from linear_attention_token_chunked_amd.inputs import WORKLOADS, make_prefill
+
+pytestmark = pytest.mark.gpu
+DT = {"bf16": torch.bfloat16, "fp32": torch.float32}
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    from linear_attention_token_chunked_amd import gdn as m
+
+    return m
+
+
+def run_gpu(gdn, inp, **kw):
+    dev = to_dev(inp)
+    o, fin = gdn.fwd_chunked(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"],
+                             initial_state=dev.get("initial_state"), cu_seqlens=dev.get("cu_seqlens"), **kw)
+    torch.cuda.synchronize()
+    return o, fin
+
+
+def check_against_oracle(gdn, inp, dtype, scale=1.0, per_unit=True):
+    o, fin = run_gpu(gdn, inp, scale=scale)
+    ro, rf = recurrent(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], initial_state=inp.get("initial_state"),
+                       cu_seqlens=inp.get("cu_seqlens"), scale=scale)
+    tol = TOL[DT[dtype]]
+    go, gf = f64(o), f64(fin)
+    e_o = assert_close("o", go, ro, tol)
+    e_s = assert_close("final_state", gf, rf, tol)
+    if per_unit:  # a single broken head must not hide inside the global norm
+        Hv = go.shape[2]
+        for h in range(Hv):
+            if np.linalg.norm(ro[:, :, h]) > 0:
+                assert rel_l2(go[:, :, h], ro[:, :, h]) <= tol, f"o head {h}"
+        for n in range(gf.shape[0]):
+            for h in range(Hv):
+                if np.linalg.norm(rf[n, h]) > 0:
+                    assert rel_l2(gf[n, h], rf[n, h]) <= tol, f"state {(n, h)}"
+    flush(f"  rel-L2 o {e_o:.2e} state {e_s:.2e}")
+    return go, gf
+
+
+def test_tiny_fp32_workload(gdn):
+    """B=1, T=256, H=2, dk=dv=64, fp32, zero initial state, seed 0: tolerance 1e-5."""
+    w = WORKLOADS["tiny_fp32"]
+    flush(f"prefill {w.name}")
+    inp = make_prefill(w.B, w.T, w.Hqk, w.Hv, w.dk, w.dv, w.dtype, init_state=False, seed=0)
+    check_against_oracle(gdn, inp, "fp32")
+
+
+@pytest.mark.parametrize("dtype,B,T,Hqk,Hv,d,init", [
+    ("bf16", 2, 300, 2, 4, 128, True),    # several chunks + a ragged tail, grouped heads
+    ("bf16", 1, 200, 1, 1, 128, False),
+    ("bf16", 2, 130, 2, 2, 64, True),
+    ("fp32", 2, 257, 1, 2, 64, True),
+    ("fp32", 1, 1, 1, 1, 64, True),       # one token
+    ("bf16", 1, 64, 4, 8, 128, True),     # exactly one chunk
+])
+def test_small_shapes(gdn, dtype, B, T, Hqk, Hv, d, init):
+    flush(f"prefill small {dtype} B={B} T={T} Hqk={Hqk} Hv={Hv} d={d} init={init}")
+    inp = make_prefill(B, T, Hqk, Hv, d, d, dtype, init_state=init, seed=B * 1000 + T)
+    check_against_oracle(gdn, inp, dtype, scale=0.9)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp32", 64)])
+def test_packed_ragged_lengths(gdn, dtype, d):
+    """Packed batch with empty, 1-token, chunk-boundary and ragged sequences."""
+    lens = [0, 1, 15, 16, 63, 64, 65, 129, 0, 200]
+    flush(f"prefill packed {dtype} d={d} lens={lens}")
+    inp = make_prefill(1, 0, 2, 4, d, d, dtype, init_state=True, lengths=lens, seed=5)
+    go, gf = check_against_oracle(gdn, inp, dtype)
+    s0 = f64(inp["initial_state"])
+    np.testing.assert_array_equal(gf[0], s0[0])  # empty sequence: final == initial, bit for bit
+    np.testing.assert_array_equal(gf[8], s0[8])
+
+
+def test_slow_decay_long_carry(gdn):
+    """log(alpha) scaled by 0.001: the state carries across all chunks and the initial state stays visible."""
+    flush("prefill slow decay")
+    inp = make_prefill(1, 1024, 1, 2, 128, 128, "bf16", init_state=True, seed=9, gate_scale=0.001)
+    check_against_oracle(gdn, inp, "bf16")
+
+
+def test_identity_gates_keep_state_and_read_it(gdn):
+    """alpha = 1, beta = 0: final == initial and o_t = M0^T q_t (fp32, tolerance 1e-5)."""
+    inp = make_prefill(1, 150, 1, 2, 64, 64, "fp32", init_state=True, seed=3)
+    inp["g"].zero_()
+    inp["beta"].zero_()
+    o, fin = run_gpu(gdn, inp)
+    s0 = f64(inp["initial_state"])
+    assert_close("final", f64(fin), s0, 1e-6)
+    expect = np.einsum("ti,hij->thj", f64(inp["q"])[0, :, 0], s0[0])
+    assert_close("o", f64(o)[0], expect, 1e-5)
+
+
+def test_query_equal_key_beta_one_reads_back_value(gdn):
+    """beta = 1, unit keys, q = k: o_t = v_t for any history (fp32)."""
+    inp = make_prefill(1, 200, 1, 1, 64, 64, "fp32", init_state=True, seed=4)
+    inp["beta"].fill_(1.0)
+    inp["q"] = inp["k"].clone()
+    o, _ = run_gpu(gdn, inp)
+    assert_close("o", f64(o), f64(inp["v"]), 1e-5)
+
+
+def test_in_place_state_and_no_final_state(gdn):
+    inp = make_prefill(2, 100, 1, 2, 128, 128, "bf16", init_state=True, seed=6)
+    dev = to_dev(inp)
+    o_ref, f_ref = gdn.fwd_chunked(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"],
+                                   initial_state=dev["initial_state"])
+    st = dev["initial_state"].clone()
+    o_inp, f_inp = gdn.fwd_chunked(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], initial_state=st,
+                                   final_state=st)
+    o_nf, f_nf = gdn.fwd_chunked(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"],
+                                 initial_state=dev["initial_state"], output_final_state=False)
+    torch.cuda.synchronize()
+    assert f_nf is None
+    assert torch.equal(o_ref, o_inp) and torch.equal(o_ref, o_nf)
+    assert torch.equal(f_ref, st)
+
+
+def test_composition_and_decode_continuity(gdn):
+    """prefill(T1) then prefill(T2, init = final) == prefill(T1 + T2); decode steps == prefill."""
+    inp = make_prefill(1, 160, 2, 2, 128, 128, "bf16", init_state=True, seed=8)
+    dev = to_dev(inp)
+    o_all, f_all = gdn.fwd_chunked(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"],
+                                   initial_state=dev["initial_state"])
+    sl = lambda x, a, b: x[:, a:b].contiguous()
+    o_a, f_a = gdn.fwd_chunked(*(sl(dev[x], 0, 70) for x in ("q", "k", "v", "g", "beta")),
+                               initial_state=dev["initial_state"])
+    o_b, f_b = gdn.fwd_chunked(*(sl(dev[x], 70, 160) for x in ("q", "k", "v", "g", "beta")), initial_state=f_a)
+    assert rel_l2(f64(torch.cat([o_a, o_b], 1)), f64(o_all)) < 5e-3
+    assert rel_l2(f64(f_b), f64(f_all)) < 5e-3
+    state = dev["initial_state"].clone()
+    outs = [gdn.decode_step(dev["q"][:, t].contiguous(), dev["k"][:, t].contiguous(), dev["v"][:, t].contiguous(),
+                            dev["g"][:, t].contiguous(), dev["beta"][:, t].contiguous(), state) for t in range(160)]
+    assert rel_l2(f64(torch.stack(outs, 1)), f64(o_all)) < 2e-2
+    assert rel_l2(f64(state), f64(f_all)) < 2e-2
+
+
+def test_deterministic(gdn):
+    inp = make_prefill(2, 300, 2, 4, 128, 128, "bf16", init_state=True, seed=12)
+    o1, f1 = run_gpu(gdn, inp)
+    o2, f2 = run_gpu(gdn, inp)
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+# ----------------------------------------------------------------------------- full sizes
+def sampled_units_check(gdn, w, units, seed=0):
+    inp = make_prefill(w.B, w.T, w.Hqk, w.Hv, w.dk, w.dv, w.dtype, init_state=w.init_state, seed=seed,
+                       num_packed=w.num_packed)
+    flush(f"  tokens {inp['q'].shape[0] * inp['q'].shape[1]}")
+    o, fin = run_gpu(gdn, inp)
+    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(fin).all())
+    cu = inp["cu_seqlens"].numpy() if inp["cu_seqlens"] is not None else None
+    if callable(units):
+        units = units(cu)
+    tol = TOL[DT[w.dtype]]
+    for n, h in units:
+        ro, rf = unit_oracle(inp, n, h, cu=cu)
+        if cu is not None:
+            go = f64(o[0, int(cu[n]):int(cu[n + 1]), h])
+        else:
+            go = f64(o[n, :, h])
+        e1 = assert_close(f"o unit {(n, h)}", go, ro, tol)
+        e2 = assert_close(f"state unit {(n, h)}", f64(fin[n, h]), rf, tol)
+        flush(f"  unit {(n, h)} len {len(ro)} rel-L2 o {e1:.2e} state {e2:.2e}")
+
+
+def test_full_prefill_b4_t4096(gdn):
+    w = WORKLOADS["prefill_b4_t4096"]
+    flush(f"prefill full {w.name}")
+    sampled_units_check(gdn, w, [(0, 0), (3, 15), (1, 7)])
+
+
+def test_full_prefill_t65536_gqa(gdn):
+    w = WORKLOADS["prefill_t65536_gqa"]
+    flush(f"prefill full {w.name}")
+    sampled_units_check(gdn, w, [(0, 0), (0, 31)])
+
+
+def test_full_varlen_64(gdn):
+    w = WORKLOADS["varlen_64"]
+    flush(f"prefill full {w.name}")
+
+    def pick(cu):
+        lens = np.diff(cu)
+        return [(int(np.argmax(lens)), 5), (int(np.argmin(lens)), 30), (17, 0)]
+
+    sampled_units_check(gdn, w, pick)
