@@ -106,4 +106,11 @@ __device__ __forceinline__ typename Mma<T>::frag lds_frag(const T* row, int kg, 
 
 __device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS (and
+// scalar) operations, then s_barrier.  Unlike __syncthreads() it does not wait
+// for outstanding global loads, so loads issued ahead of time (the next
+// chunk's operands) stay in flight across it.  The "memory" clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 }  // namespace gdn

@@ -17,10 +17,13 @@
 // head, dv-slice) and walks its chunks in order, holding the fp32 state slice
 // in registers the whole time, so the state never touches HBM between chunks
 // and no workspace exists.  Per chunk:
-//   phase 0  gates (wave-level prefix sum), K, K^T, Q, V^T of the chunk -> LDS
+//   phase 0  the chunk's K, K^T, Q, V^T and gate prefix sums -> LDS (the global
+//            loads were issued one chunk earlier and are already in registers);
+//            the next chunk's loads are issued here and land during phases 1-6
 //   phase 1  K K^T and Q K^T on the matrix cores, masked with the decay -> A, P
 //   phase 2  16x16 diagonal blocks of (I + A)^-1 by forward substitution (fp32)
-//   phase 3  off-diagonal blocks, block row by block row (fp32 matrix cores)
+//   phase 3  off-diagonal blocks, one block diagonal at a time (fp32 matrix
+//            cores); a transposed copy of T lives above the diagonal of A
 //   phase 4  T diag(beta exp G), T diag(beta) as matrix-core operands
 //   phase 5  W (negated) = T diag(beta exp G) K
 //   phase 6  per wavefront, on its own dv columns: Ut, U = Ut - W M, the output
@@ -29,6 +32,8 @@
 // bf16 inputs use v_mfma_f32_16x16x32_bf16 with fp32 accumulation (the state
 // is rounded to bf16 only as an operand); fp32 inputs use v_mfma_f32_16x16x4_f32
 // so that nothing is rounded below fp32.  The triangular solve is fp32 in both.
+// Decay factors are exp2 of log2(e)-scaled prefix sums, and exp(G_i - G_j) is
+// only ever formed for i >= j, where it is at most 1 for decaying gates.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -38,25 +43,25 @@ namespace {
 constexpr int C = 64;            // chunk length
 constexpr int NW = 4;            // wavefronts per workgroup
 constexpr int NTHREADS = 64 * NW;
+constexpr float kLog2e = 1.4426950408889634f;
 
 template <class T, int DK, int BV>
 struct Layout {
   static constexpr int EPB = 16 / sizeof(T);   // elements per 16 bytes
   static constexpr int NTW = BV / (16 * NW);   // 16-column tiles per wavefront
-  static constexpr int LDK = DK + EPB;         // row stride of [C][DK] tiles: sK, sQ, sW
+  static constexpr int LDK = DK + EPB;         // row stride of [C][DK] tiles: sK / sW, sQ
   static constexpr int LDC = C + EPB;          // row stride of [*][C] tiles: sKT, sVT, sTw, sTu, sP
   static constexpr int LDF = C + 4;            // row stride of the fp32 [C][C] tiles: sA, sT
-  static constexpr size_t oK = 0;
+  static constexpr size_t oK = 0;              // K rows; reused for -W once the Gram products are done
   static constexpr size_t oQ = oK + sizeof(T) * C * LDK;
   static constexpr size_t oKT = oQ + sizeof(T) * C * LDK;
   static constexpr size_t oVT = oKT + sizeof(T) * DK * LDC;
   static constexpr size_t oTw = oVT + sizeof(T) * BV * LDC;
   static constexpr size_t oTu = oTw + sizeof(T) * C * LDC;
   static constexpr size_t oP = oTu + sizeof(T) * C * LDC;
-  static constexpr size_t oA = oP + sizeof(T) * C * LDC;  // fp32 A; reused for W after the solve
-  static constexpr size_t szA = (4 * C * LDF > sizeof(T) * C * LDK) ? 4 * C * LDF : sizeof(T) * C * LDK;
-  static constexpr size_t oT = oA + szA;
-  static constexpr size_t oV = oT + 4 * C * LDF;         // five per-token fp32 vectors
+  static constexpr size_t oA = oP + sizeof(T) * C * LDC;  // fp32: A below the diagonal, T^T on and above
+  static constexpr size_t oT = oA + 4 * C * LDF;          // fp32: T row-major
+  static constexpr size_t oV = oT + 4 * C * LDF;          // five per-token fp32 vectors
   static constexpr size_t bytes = oV + 4 * 5 * C;
   static_assert(BV % (16 * NW) == 0, "dv-slice must give every wavefront whole 16-column tiles");
   static_assert(oQ % 16 == 0 && oKT % 16 == 0 && oVT % 16 == 0 && oTw % 16 == 0 && oP % 16 == 0 &&
@@ -73,16 +78,6 @@ struct Params {
   float scale;
 };
 
-// Logical contraction index stored at LDS position P (inverse of phys_k).
-template <class T>
-__device__ __forceinline__ int logical_k(int P);
-template <>
-__device__ __forceinline__ int logical_k<bf16>(int P) {
-  return (P & ~31) | (((P >> 2) & 1) << 4) | (((P >> 3) & 3) << 2) | (P & 3);
-}
-template <>
-__device__ __forceinline__ int logical_k<float>(int P) { return P; }
-
 // Operand fragment of k-group kg built from accumulator tiles tile(kg*TPG + t).
 template <class T, class F>
 __device__ __forceinline__ typename Mma<T>::frag chain_frag(F tile, int kg) {
@@ -94,8 +89,127 @@ __device__ __forceinline__ typename Mma<T>::frag chain_frag(F tile, int kg) {
 }
 
 template <class T>
-struct Raw16 {  // 16 bytes of T
-  typename Mma<T>::frag v;
+__device__ __forceinline__ typename Mma<T>::frag zero_frag() {
+  typename Mma<T>::frag z;
+#pragma unroll
+  for (int i = 0; i < 16 / static_cast<int>(sizeof(T)); ++i) z[i] = from_float<T>(0.f);
+  return z;
+}
+
+// The raw operands of one chunk, held in registers between the global loads
+// (issued one chunk ahead) and the LDS stores.  Tokens past the end of the
+// sequence load as zeros, and their gates as g = 0, beta = 0, which makes
+// them exact no-ops in every product.
+template <class T, int DK, int BV>
+struct ChunkRegs {
+  typedef typename Mma<T>::frag frag;
+  static constexpr int EPB = 16 / sizeof(T);
+  static constexpr int NKT = (C / 4) * (DK / EPB);  // K tasks: 4 token rows x EPB key columns
+  static constexpr int KIT = (NKT + NTHREADS - 1) / NTHREADS;
+  static constexpr int NQP = C * (DK / EPB);        // Q 16-byte pieces
+  static constexpr int QIT = (NQP + NTHREADS - 1) / NTHREADS;
+  static constexpr int NVT = (C / 4) * (BV / EPB);  // V tasks: 4 token rows x EPB value columns
+  static constexpr int VIT = (NVT + NTHREADS - 1) / NTHREADS;
+  frag k[KIT][4];
+  frag q[QIT];
+  frag v[VIT][4];
+  float g, b;
+
+  // kb, qb, vb point at the chunk's first token (head and column offsets applied).
+  __device__ __forceinline__ void load(const T* kb, const T* qb, const T* vb, size_t qk_tok, size_t v_tok,
+                                       const float* gb, const float* bb, size_t g_tok, int Lc, int tid) {
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+      const int t = tid + it * NTHREADS;
+      const int rg = t % (C / 4), cgp = t / (C / 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * rg + e;
+        k[it][e] = (t < NKT && r < Lc) ? *reinterpret_cast<const frag*>(kb + r * qk_tok + cgp * EPB)
+                                       : zero_frag<T>();
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < QIT; ++it) {
+      const int t = tid + it * NTHREADS;
+      const int r = t / (DK / EPB), cgp = t % (DK / EPB);
+      q[it] = (t < NQP && r < Lc) ? *reinterpret_cast<const frag*>(qb + r * qk_tok + cgp * EPB) : zero_frag<T>();
+    }
+#pragma unroll
+    for (int it = 0; it < VIT; ++it) {
+      const int t = tid + it * NTHREADS;
+      const int rg = t % (C / 4), cgp = t / (C / 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * rg + e;
+        v[it][e] = (t < NVT && r < Lc) ? *reinterpret_cast<const frag*>(vb + r * v_tok + cgp * EPB)
+                                       : zero_frag<T>();
+      }
+    }
+    g = 0.f;
+    b = 0.f;
+    if (tid < 64 && tid < Lc) {
+      g = gb[tid * g_tok];
+      b = bb[tid * g_tok];
+    }
+  }
+
+  // K -> sK (row layout) and sKT (transposed), Q -> sQ, V -> sVT (transposed).
+  // Contraction axes are stored in phys_k order (see device_common.hpp).
+  __device__ __forceinline__ void store(T* sK, T* sKT, T* sQ, T* sVT, int LDK, int LDC, int tid) const {
+    typedef typename Vec4<T>::type V4;
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+      const int t = tid + it * NTHREADS;
+      if (t < NKT) {
+        const int rg = t % (C / 4), cgp = t / (C / 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int u = 0; u < EPB / 4; ++u) {
+            V4 w4;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) w4[c] = k[it][e][4 * u + c];
+            *reinterpret_cast<V4*>(sK + (4 * rg + e) * LDK + Mma<T>::phys_k(cgp * EPB + 4 * u)) = w4;
+          }
+#pragma unroll
+        for (int c = 0; c < EPB; ++c) {
+          V4 col;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) col[e] = k[it][e][c];
+          *reinterpret_cast<V4*>(sKT + (cgp * EPB + c) * LDC + Mma<T>::phys_k(4 * rg)) = col;
+        }
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < QIT; ++it) {
+      const int t = tid + it * NTHREADS;
+      if (t < NQP) {
+        const int r = t / (DK / EPB), cgp = t % (DK / EPB);
+#pragma unroll
+        for (int u = 0; u < EPB / 4; ++u) {
+          V4 w4;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) w4[c] = q[it][4 * u + c];
+          *reinterpret_cast<V4*>(sQ + r * LDK + Mma<T>::phys_k(cgp * EPB + 4 * u)) = w4;
+        }
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < VIT; ++it) {
+      const int t = tid + it * NTHREADS;
+      if (t < NVT) {
+        const int rg = t % (C / 4), cgp = t / (C / 4);
+#pragma unroll
+        for (int c = 0; c < EPB; ++c) {
+          V4 col;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) col[e] = v[it][e][c];
+          *reinterpret_cast<V4*>(sVT + (cgp * EPB + c) * LDC + Mma<T>::phys_k(4 * rg)) = col;
+        }
+      }
+    }
+  }
 };
 
 template <class T, int DK, int DV, int BV>
@@ -104,11 +218,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_kernel(Params p) {
   using MM = Mma<T>;
   using frag = typename MM::frag;
   using V4 = typename Vec4<T>::type;
-  constexpr int EPB = L::EPB, NTW = L::NTW, LDK = L::LDK, LDC = L::LDC, LDF = L::LDF;
+  constexpr int NTW = L::NTW, LDK = L::LDK, LDC = L::LDC, LDF = L::LDF;
   constexpr int KT = DK / 16;  // key-dim tiles of the state
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   T* sK = reinterpret_cast<T*>(smem + L::oK);
+  T* sW = reinterpret_cast<T*>(smem + L::oK);
   T* sQ = reinterpret_cast<T*>(smem + L::oQ);
   T* sKT = reinterpret_cast<T*>(smem + L::oKT);
   T* sVT = reinterpret_cast<T*>(smem + L::oVT);
@@ -116,13 +231,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_kernel(Params p) {
   T* sTu = reinterpret_cast<T*>(smem + L::oTu);
   T* sP = reinterpret_cast<T*>(smem + L::oP);
   float* sA = reinterpret_cast<float*>(smem + L::oA);
-  T* sW = reinterpret_cast<T*>(smem + L::oA);
   float* sT = reinterpret_cast<float*>(smem + L::oT);
-  float* sG = reinterpret_cast<float*>(smem + L::oV);  // G
-  float* seG = sG + C;                                 // exp(G)
-  float* segl = seG + C;                               // exp(G_C - G)
-  float* sb = segl + C;                                // beta
-  float* sbg = sb + C;                                 // beta exp(G)
+  float* sGl = reinterpret_cast<float*>(smem + L::oV);  // G * log2(e)
+  float* seG = sGl + C;                                 // exp(G)
+  float* segl = seG + C;                                // exp(G_C - G)
+  float* sb = segl + C;                                 // beta
+  float* sbg = sb + C;                                  // beta exp(G)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -153,11 +267,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_kernel(Params p) {
   const int wcol = col0 + wave * 16 * NTW;     // first value column of this wavefront
 
   const T* qg = static_cast<const T*>(p.q);
-  const T* kg_ = static_cast<const T*>(p.k);
+  const T* kgp = static_cast<const T*>(p.k);
   const T* vg = static_cast<const T*>(p.v);
   T* og = static_cast<T*>(p.o);
   const size_t qk_tok = static_cast<size_t>(p.Hqk) * DK;  // token stride of q, k
   const size_t v_tok = static_cast<size_t>(p.Hv) * DV;    // token stride of v, o
+
+  ChunkRegs<T, DK, BV> pre;
+  auto issue_loads = [&](int cs) {
+    const size_t tq = static_cast<size_t>(cs) * qk_tok + static_cast<size_t>(hq) * DK;
+    const size_t tv = static_cast<size_t>(cs) * v_tok + static_cast<size_t>(h) * DV + col0;
+    const size_t tg = static_cast<size_t>(cs) * p.Hv + h;
+    pre.load(kgp + tq, qg + tq, vg + tv, qk_tok, v_tok, p.g + tg, p.beta + tg, p.Hv, min(C, eos - cs), tid);
+  };
+  if (bos < eos) issue_loads(bos);
 
   // State tiles: Ms[a][j] holds M[16a + 4lg + s][wcol + 16j + lr], s = 0..3.
   floatx4 Ms[KT][NTW];
@@ -174,190 +297,150 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_kernel(Params p) {
   for (int cs = bos; cs < eos; cs += C) {
     const int Lc = min(C, eos - cs);
 
-    // ---------------- phase 0: gates and operand tiles into LDS ----------------
+    // ---------------- phase 0: this chunk's operands into LDS; next chunk's loads issued ----------------
+    pre.store(sK, sKT, sQ, sVT, LDK, LDC, tid);
     if (wave == 0) {
-      float gt = 0.f, bt = 0.f;  // tokens past the end act as g = 0, beta = 0 (no-ops)
-      if (lane < Lc) {
-        gt = p.g[static_cast<size_t>(cs + lane) * p.Hv + h];
-        bt = p.beta[static_cast<size_t>(cs + lane) * p.Hv + h];
-      }
-      float G = gt;
+      // inclusive prefix sum of the log-gates over the chunk (G restarts every chunk)
+      float G = pre.g;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(G, off);
         if (lane >= off) G += y;
       }
-      const float GC = __shfl(G, 63);
-      const float eG = expf(G);
-      sG[lane] = G;
+      const float Gl = G * kLog2e;
+      const float GlC = __shfl(Gl, 63);
+      const float eG = __builtin_amdgcn_exp2f(Gl);
+      sGl[lane] = Gl;
       seG[lane] = eG;
-      segl[lane] = expf(GC - G);
-      sb[lane] = bt;
-      sbg[lane] = bt * eG;
+      segl[lane] = __builtin_amdgcn_exp2f(GlC - Gl);
+      sb[lane] = pre.b;
+      sbg[lane] = pre.b * eG;
     }
-    {
-      // K: row layout (sK) and transposed (sKT) from one pass of loads.  A task
-      // reads the EPB token rows that sit at LDS positions [EPB*pg, EPB*pg+EPB)
-      // of sKT's token axis and EPB key columns, then writes both layouts.
-      constexpr int NPG = C / EPB, NCG = DK / EPB;
-      const T* kb = kg_ + static_cast<size_t>(cs) * qk_tok + static_cast<size_t>(hq) * DK;
-      for (int task = tid; task < NPG * NCG; task += NTHREADS) {
-        const int pg = task / NCG, cgp = task - (task / NCG) * NCG;
-        Raw16<T> rows[EPB];
-#pragma unroll
-        for (int e = 0; e < EPB; ++e) {
-          const int r = logical_k<T>(pg * EPB + e);
-          if (r < Lc) {
-            rows[e].v = *reinterpret_cast<const frag*>(kb + r * qk_tok + cgp * EPB);
-          } else {
-#pragma unroll
-            for (int c = 0; c < EPB; ++c) rows[e].v[c] = from_float<T>(0.f);
-          }
-#pragma unroll
-          for (int u = 0; u < EPB / 4; ++u) {
-            V4 w4;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) w4[c] = rows[e].v[4 * u + c];
-            *reinterpret_cast<V4*>(sK + r * LDK + MM::phys_k(cgp * EPB + 4 * u)) = w4;
-          }
-        }
-#pragma unroll
-        for (int c = 0; c < EPB; ++c) {
-          Raw16<T> col;
-#pragma unroll
-          for (int e = 0; e < EPB; ++e) col.v[e] = rows[e].v[c];
-          *reinterpret_cast<frag*>(sKT + (cgp * EPB + c) * LDC + pg * EPB) = col.v;
-        }
-      }
-      // Q: row layout only.
-      const T* qb = qg + static_cast<size_t>(cs) * qk_tok + static_cast<size_t>(hq) * DK;
-      for (int task = tid; task < C * NCG; task += NTHREADS) {
-        const int r = task / NCG, cgp = task - (task / NCG) * NCG;
-        Raw16<T> x;
-        if (r < Lc) {
-          x.v = *reinterpret_cast<const frag*>(qb + r * qk_tok + cgp * EPB);
-        } else {
-#pragma unroll
-          for (int c = 0; c < EPB; ++c) x.v[c] = from_float<T>(0.f);
-        }
-#pragma unroll
-        for (int u = 0; u < EPB / 4; ++u) {
-          V4 w4;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) w4[c] = x.v[4 * u + c];
-          *reinterpret_cast<V4*>(sQ + r * LDK + MM::phys_k(cgp * EPB + 4 * u)) = w4;
-        }
-      }
-      // V: this workgroup's dv-slice, transposed.
-      constexpr int NVG = BV / EPB;
-      const T* vb = vg + static_cast<size_t>(cs) * v_tok + static_cast<size_t>(h) * DV + col0;
-      for (int task = tid; task < NPG * NVG; task += NTHREADS) {
-        const int pg = task / NVG, cgp = task - (task / NVG) * NVG;
-        Raw16<T> rows[EPB];
-#pragma unroll
-        for (int e = 0; e < EPB; ++e) {
-          const int r = logical_k<T>(pg * EPB + e);
-          if (r < Lc) {
-            rows[e].v = *reinterpret_cast<const frag*>(vb + r * v_tok + cgp * EPB);
-          } else {
-#pragma unroll
-            for (int c = 0; c < EPB; ++c) rows[e].v[c] = from_float<T>(0.f);
-          }
-        }
-#pragma unroll
-        for (int c = 0; c < EPB; ++c) {
-          Raw16<T> col;
-#pragma unroll
-          for (int e = 0; e < EPB; ++e) col.v[e] = rows[e].v[c];
-          *reinterpret_cast<frag*>(sVT + (cgp * EPB + c) * LDC + pg * EPB) = col.v;
-        }
-      }
-    }
-    __syncthreads();
+    if (cs + C < eos) issue_loads(cs + C);  // lands while this chunk computes
+    lds_barrier();
 
     // ---------------- phase 1: K K^T and Q K^T, masked with the decay ----------------
     {
-      // Wavefront w owns token rows i in [16w, 16w+16).  Tile c of both products
-      // is computed transposed so that a lane ends up holding four consecutive
-      // columns j = 16c + 4lg + s of row i = 16w + lr.
-      const int w = wave;
-      floatx4 kk[4], qk[4];
+      // The ten 16x16 tiles on or below the diagonal, spread over the four
+      // wavefronts.  Tile (ti, tj) is computed transposed so that a lane holds
+      // four consecutive columns j = 16tj + 4lg + s of row i = 16ti + lr.
+      int ti[3], tj[3], nt;
+      switch (wave) {
+        case 0: ti[0] = 0; tj[0] = 0; ti[1] = 1; tj[1] = 0; ti[2] = 3; tj[2] = 3; nt = 3; break;
+        case 1: ti[0] = 1; tj[0] = 1; ti[1] = 2; tj[1] = 0; ti[2] = 3; tj[2] = 2; nt = 3; break;
+        case 2: ti[0] = 2; tj[0] = 1; ti[1] = 3; tj[1] = 0; ti[2] = 0; tj[2] = 0; nt = 2; break;
+        default: ti[0] = 2; tj[0] = 2; ti[1] = 3; tj[1] = 1; ti[2] = 0; tj[2] = 0; nt = 2; break;
+      }
+      floatx4 kk[3], qk[3];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) kk[c] = qk[c] = zero4();
+      for (int t = 0; t < 3; ++t) kk[t] = qk[t] = zero4();
 #pragma unroll
       for (int kgi = 0; kgi < DK / MM::KG; ++kgi) {
-        const frag bk = lds_frag(sK + (16 * w + lr) * LDK, kgi, lane);
-        const frag bq = lds_frag(sQ + (16 * w + lr) * LDK, kgi, lane);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if (c <= w) {  // only tiles on or below the diagonal are needed
-            const frag a = lds_frag(sK + (16 * c + lr) * LDK, kgi, lane);
-            MM::mma(kk[c], a, bk);
-            MM::mma(qk[c], a, bq);
+        for (int t = 0; t < 3; ++t) {
+          if (t < nt) {
+            const frag a = lds_frag(sK + (16 * tj[t] + lr) * LDK, kgi, lane);
+            MM::mma(kk[t], a, lds_frag(sK + (16 * ti[t] + lr) * LDK, kgi, lane));
+            MM::mma(qk[t], a, lds_frag(sQ + (16 * ti[t] + lr) * LDK, kgi, lane));
           }
         }
       }
-      const int i = 16 * w + lr;
-      const float Gi = sG[i], bi = sb[i];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        floatx4 av = zero4(), pv = zero4();
+      for (int t = 0; t < 3; ++t) {
+        if (t < nt) {
+          const int i = 16 * ti[t] + lr;
+          const float Gi = sGl[i], bi = sb[i];
+          floatx4 av = zero4(), pv = zero4();
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int j = 16 * c + 4 * lg + s;
-          if (j <= i) {  // exp(G_i - G_j) is formed only on and below the diagonal
-            const float d = expf(Gi - sG[j]);
-            av[s] = (j < i) ? bi * d * kk[c][s] : 0.f;
-            pv[s] = d * qk[c][s];
+          for (int s = 0; s < 4; ++s) {
+            const int j = 16 * tj[t] + 4 * lg + s;
+            if (j <= i) {  // exp(G_i - G_j) is formed only on and below the diagonal
+              const float d = __builtin_amdgcn_exp2f(Gi - sGl[j]);
+              av[s] = (j < i) ? bi * d * kk[t][s] : 0.f;
+              pv[s] = d * qk[t][s];
+            }
           }
+          *reinterpret_cast<floatx4*>(sA + i * LDF + 16 * tj[t] + 4 * lg) = av;
+          *reinterpret_cast<V4*>(sP + i * LDC + MM::phys_k(16 * tj[t] + 4 * lg)) =
+              pack4<T>(pv[0], pv[1], pv[2], pv[3]);
         }
-        *reinterpret_cast<floatx4*>(sA + i * LDF + 16 * c + 4 * lg) = av;
-        *reinterpret_cast<V4*>(sP + i * LDC + MM::phys_k(16 * c + 4 * lg)) = pack4<T>(pv[0], pv[1], pv[2], pv[3]);
+      }
+      // zero the six tiles of P above the diagonal
+      if (wave >= 2) {
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+          const int zi = (wave == 2) ? 0 : (t == 2 ? 2 : 1);
+          const int zj = (wave == 2) ? t + 1 : (t == 2 ? 3 : t + 2);
+          *reinterpret_cast<V4*>(sP + (16 * zi + lr) * LDC + MM::phys_k(16 * zj + 4 * lg)) =
+              pack4<T>(0.f, 0.f, 0.f, 0.f);
+        }
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---------------- phase 2: diagonal 16x16 blocks of (I + A)^-1 ----------------
     if (wave == 0) {
-      // Lane (blk, cc) computes column cc of the inverse of block blk by forward
-      // substitution: x_i = [i == cc] - sum_{j < i} A_ij x_j.
+      // Lane (blk, cc) computes column cc of the inverse of diagonal block blk by
+      // forward substitution, x_i = [i == cc] - sum_{j < i} A_ij x_j, then stores
+      // it row-major into sT and as row cc of the block's transpose into sA
+      // (that block of A is not needed any more).
       const int blk = lg, cc = lr;
       const float* Ab = sA + (16 * blk) * LDF + 16 * blk;
       float x[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
+        float arow[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const floatx4 a4 = *reinterpret_cast<const floatx4*>(Ab + i * LDF + 4 * q4);
+          arow[4 * q4] = a4[0];
+          arow[4 * q4 + 1] = a4[1];
+          arow[4 * q4 + 2] = a4[2];
+          arow[4 * q4 + 3] = a4[3];
+        }
         float acc = (i == cc) ? 1.f : 0.f;
 #pragma unroll
-        for (int j = 0; j < i; ++j) acc -= Ab[i * LDF + j] * x[j];
+        for (int j = 0; j < i; ++j) acc -= arow[j] * x[j];
         x[i] = acc;
       }
       float* Tb = sT + (16 * blk) * LDF + 16 * blk;
 #pragma unroll
       for (int i = 0; i < 16; ++i) Tb[i * LDF + cc] = x[i];
+      float* TTb = sA + (16 * blk + cc) * LDF + 16 * blk;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<floatx4*>(TTb + 4 * q4) = floatx4{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---------------- phase 3: off-diagonal blocks, one block diagonal at a time ----------------
-    // T_ij = -T_ii * sum_{m=j}^{i-1} A_im T_mj   (16x16 blocks, i > j)
+    // T_ij = -T_ii * sum_{m=j}^{i-1} A_im T_mj   (16x16 blocks, i > j).  The
+    // T_mj operands are read from the transposed copy above the diagonal of sA.
 #pragma unroll
     for (int d = 1; d < 4; ++d) {
       if (wave < 4 - d) {
         const int bj = wave, bi = wave + d;
-        floatx4 y = zero4();
-        for (int m = bj; m < bi; ++m) {
-          const floatx4 af = *reinterpret_cast<const floatx4*>(sA + (16 * bi + lr) * LDF + 16 * m + 4 * lg);
-          floatx4 bf;
+        floatx4 y[3];
 #pragma unroll
-          for (int s = 0; s < 4; ++s) bf[s] = sT[(16 * m + 4 * lg + s) * LDF + 16 * bj + lr];
-          Mma<float>::mma(y, af, bf);
+        for (int u = 0; u < 3; ++u) {
+          y[u] = zero4();
+          if (u < d) {
+            const int m = bj + u;
+            const floatx4 af = *reinterpret_cast<const floatx4*>(sA + (16 * bi + lr) * LDF + 16 * m + 4 * lg);
+            const floatx4 bf = *reinterpret_cast<const floatx4*>(sA + (16 * bj + lr) * LDF + 16 * m + 4 * lg);
+            Mma<float>::mma(y[u], af, bf);
+          }
         }
+        const floatx4 ysum = y[0] + y[1] + y[2];
         const floatx4 tf = *reinterpret_cast<const floatx4*>(sT + (16 * bi + lr) * LDF + 16 * bi + 4 * lg);
         floatx4 t = zero4();
-        Mma<float>::mma(t, tf, y);
+        Mma<float>::mma(t, tf, ysum);
+        // lane holds T_ij[4lg + s][lr]
 #pragma unroll
         for (int s = 0; s < 4; ++s) sT[(16 * bi + 4 * lg + s) * LDF + 16 * bj + lr] = -t[s];
+        *reinterpret_cast<floatx4*>(sA + (16 * bj + lr) * LDF + 16 * bi + 4 * lg) = -t;
       }
-      __syncthreads();
+      lds_barrier();
     }
 
     // ---------------- phase 4: T diag(beta exp G) and T diag(beta) as operands ----------------
@@ -370,7 +453,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_kernel(Params p) {
       *reinterpret_cast<V4*>(sTu + i * LDC + MM::phys_k(j0)) =
           pack4<T>(t[0] * sb[j0], t[1] * sb[j0 + 1], t[2] * sb[j0 + 2], t[3] * sb[j0 + 3]);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---------------- phase 5: -W = -(T diag(beta exp G)) K, computed as W^T ----------------
     {
@@ -390,7 +473,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_kernel(Params p) {
         *reinterpret_cast<V4*>(sW + (16 * w + lr) * LDK + MM::phys_k(16 * a + 4 * lg)) =
             pack4<T>(-acc[a][0], -acc[a][1], -acc[a][2], -acc[a][3]);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---------------- phase 6: per-wavefront state work on its own dv columns ----------------
     {
@@ -476,7 +559,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void prefill_kernel(Params p) {
         }
       }
     }
-    __syncthreads();  // the next chunk overwrites every LDS tile
+    lds_barrier();  // the next chunk overwrites every LDS tile
   }
 
   if (p.hT) {
