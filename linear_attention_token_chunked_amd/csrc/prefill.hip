@@ -79,6 +79,33 @@ __device__ __forceinline__ typename Mma16<T>::frag lds_frag16(const T* row, int 
   return *reinterpret_cast<const typename Mma16<T>::frag*>(row + Mma<T>::phys_k(16 * m + 4 * (lane >> 4)));
 }
 
+// Four consecutive rows of one column of a row-major LDS tile, as lane data
+// for the accumulator layout: lane (lg, lr) gets X[r0 + 4lg + e][c0 + lr],
+// e = 0..3 (c0 a multiple of 16; PERM: the column axis is stored in phys_k
+// order, which keeps every aligned run of 4 columns contiguous).  bf16 uses
+// the gfx950 transposing LDS read: in each 16-lane group, lane i returns
+// element i%4 of the 8-byte loads of lanes 4e + i/4, so lane j loads row
+// r0 + 4lg + j/4 at the 4-column run c0 + 4(j%4).  fp32 reads the four values
+// one by one.
+template <class T, bool PERM>
+__device__ __forceinline__ typename Vec4<T>::type lds_col4(const T* base, int ld, int r0, int c0, int lane) {
+  const int lg = lane >> 4, lr = lane & 15;
+  if constexpr (sizeof(T) == 2) {
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    const int col = PERM ? Mma<T>::phys_k(c0 + 4 * (lr & 3)) : c0 + 4 * (lr & 3);
+    const T* ptr = base + (r0 + 4 * lg + (lr >> 2)) * ld + col;
+    const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<__attribute__((address_space(3))) s4*>(reinterpret_cast<size_t>(ptr)));
+    return __builtin_bit_cast(typename Vec4<T>::type, v);
+  } else {
+    const int col = PERM ? Mma<T>::phys_k(c0 + lr) : c0 + lr;
+    typename Vec4<T>::type v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = base[(r0 + 4 * lg + e) * ld + col];
+    return v;
+  }
+}
+
 // Operand fragment of k-group kg built from accumulator tiles tile(kg*TPG + t).
 template <class T, class F>
 __device__ __forceinline__ typename Mma<T>::frag chain_frag(F tile, int kg) {
@@ -95,15 +122,15 @@ struct Layout {
   static constexpr int EPB = 16 / sizeof(T);
   static constexpr int NTW = BV / (16 * NCW);   // 16-column state tiles per consumer wave
   static constexpr int LDK = DK + EPB;          // [C][DK] rows: K
-  static constexpr int LDC = C + EPB;           // [*][C] rows: K^T, V^T, P, -A
+  static constexpr int LDC = C + EPB;           // [*][C] rows: P, -A
+  static constexpr int LDV = BV + EPB;          // [C][BV] rows: V
   static constexpr int LDT = 20;                // [16][16] diagonal-block inverses
   static constexpr int LDA = 20;                // fp32 diagonal blocks of A
   // one stage, double-buffered: written by the producers in segment 1
   static constexpr size_t sK = 0;
   static constexpr size_t sQ = sK + sizeof(T) * C * LDK;
-  static constexpr size_t sKT = sQ + sizeof(T) * C * LDK;
-  static constexpr size_t sVT = sKT + sizeof(T) * DK * LDC;
-  static constexpr size_t sVec = sVT + sizeof(T) * BV * LDC;  // exp G, beta, exp(G_C - G), exp G_C
+  static constexpr size_t sV = sQ + sizeof(T) * C * LDK;
+  static constexpr size_t sVec = sV + sizeof(T) * C * LDV;  // exp G, beta, exp(G_C - G), exp G_C
   static constexpr size_t stage_bytes = (sVec + 4 * 4 * C + 15) / 16 * 16;
   // single-buffered: written by the producers in segment 3, after the
   // consumers have read the previous chunk's copy in segment 2
@@ -115,7 +142,7 @@ struct Layout {
   static constexpr size_t oGl = oAd + 4 * 4 * 16 * LDA;
   static constexpr size_t bytes = oGl + 4 * C;
   static_assert(BV % (16 * NCW) == 0, "every consumer wave owns whole 16-column tiles");
-  static_assert(sQ % 16 == 0 && sKT % 16 == 0 && sVT % 16 == 0 && sVec % 16 == 0 && oP % 16 == 0 &&
+  static_assert(sQ % 16 == 0 && sV % 16 == 0 && sVec % 16 == 0 && oP % 16 == 0 &&
                 oAn % 16 == 0 && oTbb % 16 == 0 && oAd % 16 == 0, "16-byte aligned LDS regions");
 };
 
@@ -135,40 +162,33 @@ template <class T, int DK, int BV>
 struct ChunkRegs {
   typedef typename Mma<T>::frag frag;
   static constexpr int EPB = 16 / sizeof(T);
-  static constexpr int NKT = (C / 4) * (DK / EPB);  // K tasks: 4 token rows x EPB key columns
-  static constexpr int KIT = (NKT + PTHREADS - 1) / PTHREADS;
-  static constexpr int NVT = (C / 4) * (BV / EPB);  // V tasks: 4 token rows x EPB value columns
-  static constexpr int VIT = (NVT + PTHREADS - 1) / PTHREADS;
-  frag k[KIT][4];
-  frag q[KIT][4];
-  frag v[VIT][4];
+  static constexpr int KPR = DK / EPB;                  // 16-byte pieces per K / Q row
+  static constexpr int KIT = C * KPR / PTHREADS;        // K (and Q) pieces per producer thread
+  static constexpr int VPR = BV / EPB;                  // 16-byte pieces per V row (this slice)
+  static constexpr int VIT = (C * VPR + PTHREADS - 1) / PTHREADS;
+  static_assert(C * KPR % PTHREADS == 0, "K rows split evenly");
+  frag k[KIT], q[KIT], v[VIT];
   float g, b;
 
   // Every load is unconditional and reads a valid row (rows past the end of
   // the sequence read its last token): a select on a loaded value would make
   // the compiler wait for the load on the spot.  The padded rows are finite
-  // and harmless because their gates are masked to g = 0, beta = 0 (see
-  // gates()), which zeroes their rows of A, Z and U exactly.
+  // and harmless because their gates are masked to g = 0, beta = 0, which
+  // zeroes their rows of A, Z and U exactly.  Consecutive lanes read
+  // consecutive 16-byte pieces of a row.
   __device__ __forceinline__ void load(const T* kb, const T* qb, const T* vb, size_t qk_tok, size_t v_tok,
                                        const float* gb, const float* bb, size_t g_tok, int Lc, int tid) {
 #pragma unroll
     for (int it = 0; it < KIT; ++it) {
-      const int t = min(tid + it * PTHREADS, NKT - 1);
-      const int rg = t % (C / 4), cgp = t / (C / 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const size_t off = min(4 * rg + e, Lc - 1) * qk_tok + cgp * EPB;
-        k[it][e] = *reinterpret_cast<const frag*>(kb + off);
-        q[it][e] = *reinterpret_cast<const frag*>(qb + off);
-      }
+      const int t = tid + it * PTHREADS;
+      const size_t off = min(t / KPR, Lc - 1) * qk_tok + (t % KPR) * EPB;
+      k[it] = *reinterpret_cast<const frag*>(kb + off);
+      q[it] = *reinterpret_cast<const frag*>(qb + off);
     }
 #pragma unroll
     for (int it = 0; it < VIT; ++it) {
-      const int t = min(tid + it * PTHREADS, NVT - 1);
-      const int rg = t % (C / 4), cgp = t / (C / 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        v[it][e] = *reinterpret_cast<const frag*>(vb + min(4 * rg + e, Lc - 1) * v_tok + cgp * EPB);
+      const int t = min(tid + it * PTHREADS, C * VPR - 1);
+      v[it] = *reinterpret_cast<const frag*>(vb + min(t / VPR, Lc - 1) * v_tok + (t % VPR) * EPB);
     }
     if (tid < 64) {  // wave 0 owns the gates, one token per lane
       g = gb[min(tid, Lc - 1) * g_tok];
@@ -176,48 +196,29 @@ struct ChunkRegs {
     }
   }
 
-  // K -> rows and K^T, Q -> rows, V -> V^T, contraction axes in phys_k order.
-  __device__ __forceinline__ void store(T* sK, T* sQ, T* sKT, T* sVT, int LDK, int LDC, int tid) const {
+  // K, Q -> rows with the key axis in phys_k order; V -> rows in natural order.
+  __device__ __forceinline__ void store(T* sK, T* sQ, T* sV, int LDK, int LDV, int tid) const {
     typedef typename Vec4<T>::type V4;
 #pragma unroll
     for (int it = 0; it < KIT; ++it) {
       const int t = tid + it * PTHREADS;
-      if (t < NKT) {
-        const int rg = t % (C / 4), cgp = t / (C / 4);
+      const int r = t / KPR, c = (t % KPR) * EPB;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+      for (int u = 0; u < EPB / 4; ++u) {
+        V4 wk, wq;
 #pragma unroll
-          for (int u = 0; u < EPB / 4; ++u) {
-            V4 w4;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) w4[c] = k[it][e][4 * u + c];
-            *reinterpret_cast<V4*>(sK + (4 * rg + e) * LDK + Mma<T>::phys_k(cgp * EPB + 4 * u)) = w4;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) w4[c] = q[it][e][4 * u + c];
-            *reinterpret_cast<V4*>(sQ + (4 * rg + e) * LDK + Mma<T>::phys_k(cgp * EPB + 4 * u)) = w4;
-          }
-#pragma unroll
-        for (int c = 0; c < EPB; ++c) {
-          V4 col;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) col[e] = k[it][e][c];
-          *reinterpret_cast<V4*>(sKT + (cgp * EPB + c) * LDC + Mma<T>::phys_k(4 * rg)) = col;
+        for (int e = 0; e < 4; ++e) {
+          wk[e] = k[it][4 * u + e];
+          wq[e] = q[it][4 * u + e];
         }
+        *reinterpret_cast<V4*>(sK + r * LDK + Mma<T>::phys_k(c + 4 * u)) = wk;
+        *reinterpret_cast<V4*>(sQ + r * LDK + Mma<T>::phys_k(c + 4 * u)) = wq;
       }
     }
 #pragma unroll
     for (int it = 0; it < VIT; ++it) {
       const int t = tid + it * PTHREADS;
-      if (t < NVT) {
-        const int rg = t % (C / 4), cgp = t / (C / 4);
-#pragma unroll
-        for (int c = 0; c < EPB; ++c) {
-          V4 col;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) col[e] = v[it][e][c];
-          *reinterpret_cast<V4*>(sVT + (cgp * EPB + c) * LDC + Mma<T>::phys_k(4 * rg)) = col;
-        }
-      }
+      if (t < C * VPR) *reinterpret_cast<frag*>(sV + (t / VPR) * LDV + (t % VPR) * EPB) = v[it];
     }
   }
 };
@@ -240,7 +241,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
   using M16 = Mma16<T>;
   using frag = typename MM::frag;
   using V4 = typename Vec4<T>::type;
-  constexpr int NTW = L::NTW, LDK = L::LDK, LDC = L::LDC, LDT = L::LDT, LDA = L::LDA;
+  constexpr int NTW = L::NTW, LDK = L::LDK, LDC = L::LDC, LDV = L::LDV, LDT = L::LDT, LDA = L::LDA;
   constexpr int KT = DK / 16;       // key-dim tiles of the state
   constexpr int KGK = DK / MM::KG;  // k-groups over the key dim
   constexpr int KGC = C / MM::KG;   // k-groups over the chunk
@@ -300,12 +301,12 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
     pre.load(kgp + tq, qg + tq, vg + tv, qk_tok, v_tok, p.g + tg, p.beta + tg, p.Hv, min(C, eos - cs), tid);
   };
 
-  // seg 1: stage the chunk's K, Q, K^T, V^T and gates; issue the next chunk's loads.
+  // seg 1: stage the chunk's K, Q, V and gates; issue the next chunk's loads.
   auto prod_seg1 = [&](int c, int s) {
     unsigned char* S = stage(s);
     const int cs = bos + c * C, Lc = min(C, eos - cs);
-    pre.store(reinterpret_cast<T*>(S + L::sK), reinterpret_cast<T*>(S + L::sQ), reinterpret_cast<T*>(S + L::sKT),
-              reinterpret_cast<T*>(S + L::sVT), LDK, LDC, tid);
+    pre.store(reinterpret_cast<T*>(S + L::sK), reinterpret_cast<T*>(S + L::sQ), reinterpret_cast<T*>(S + L::sV), LDK,
+              LDV, tid);
     if (wave == 0) {
       const bool live = lane < Lc;  // tokens past the end act as g = 0, beta = 0 (exact no-ops)
       const float bt = live ? pre.b : 0.f;
@@ -443,7 +444,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
   auto cons_seg1 = [&](int s) {
     const unsigned char* S = stage(s);
     const T* sK = reinterpret_cast<const T*>(S + L::sK);
-    const T* sVT = reinterpret_cast<const T*>(S + L::sVT);
+    const T* sV = reinterpret_cast<const T*>(S + L::sV);
     const float* vec = reinterpret_cast<const float*>(S + L::sVec);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -471,8 +472,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
       }
 #pragma unroll
       for (int j = 0; j < NTW; ++j) {
-        const V4 v4 =
-            *reinterpret_cast<const V4*>(sVT + ((cw * NTW + j) * 16 + lr) * LDC + MM::phys_k(16 * r + 4 * lg));
+        const V4 v4 = lds_col4<T, false>(sV, LDV, 16 * r, (cw * NTW + j) * 16, lane);
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) Z[r][j][s4] = bt[s4] * (to_float(v4[s4]) - eg[s4] * Z[r][j][s4]);
       }
@@ -540,7 +540,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
   // seg 3: M <- exp(G_C) M + K^T (diag(exp(G_C - G)) U).
   auto cons_seg3 = [&](int s) {
     const unsigned char* S = stage(s);
-    const T* sKT = reinterpret_cast<const T*>(S + L::sKT);
+    const T* sK = reinterpret_cast<const T*>(S + L::sK);
     const float* vec = reinterpret_cast<const float*>(S + L::sVec);
     const float eGC = vec[3 * C];
 #pragma unroll
@@ -562,7 +562,14 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
       for (int j = 0; j < NTW; ++j) bu[j] = chain_frag<T>([&](int t) { return Z[t][j]; }, kgi);
 #pragma unroll
       for (int a = 0; a < KT; ++a) {
-        const frag af = lds_frag(sKT + (16 * a + lr) * LDC, kgi, lane);
+        frag af;  // K^T rows 16a.., tokens of k-group kgi, from the row-major K tile
+        if constexpr (MM::KG == 32) {
+          af = __builtin_shufflevector(lds_col4<T, true>(sK, LDK, 32 * kgi, 16 * a, lane),
+                                       lds_col4<T, true>(sK, LDK, 32 * kgi + 16, 16 * a, lane), 0, 1, 2, 3, 4,
+                                       5, 6, 7);
+        } else {
+          af = lds_col4<T, true>(sK, LDK, 16 * kgi, 16 * a, lane);
+        }
 #pragma unroll
         for (int j = 0; j < NTW; ++j) MM::mma(Ms[a][j], af, bu[j]);
       }
@@ -672,13 +679,12 @@ hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// dv-slice width: 64 value columns per workgroup (two workgroups per value
-// head at dv = 128, each redoing the chunk-local work), the widest slice whose
-// double-buffered stage fits in LDS with padded rows.
+// dv-slice width: whole state rows per workgroup when there are enough
+// (sequence, head) units to fill the 256 compute units, half rows (twice the
+// workgroups, each redoing the chunk-local work) when there are not.
 int choose_bv(int units, int dv) {
-  (void)units;
-  (void)dv;
-  return 64;
+  if (dv == 64) return 64;
+  return units >= 256 ? 128 : 64;
 }
 
 }  // namespace
@@ -688,7 +694,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int units = a.num_seqs * a.Hv;
   if (a.bf16) {
     if (a.dk == 128 && a.dv == 128)
-      return choose_bv(units, 128) == 64 ? launch<bf16, 128, 128, 64, 2>(a, stream) : hipErrorInvalidValue;
+      return choose_bv(units, 128) == 128 ? launch<bf16, 128, 128, 128, 2>(a, stream)
+                                          : launch<bf16, 128, 128, 64, 2>(a, stream);
     if (a.dk == 64 && a.dv == 64) return launch<bf16, 64, 64, 64, 2>(a, stream);
   } else {
     if (a.dk == 64 && a.dv == 64) return launch<float, 64, 64, 64, 1>(a, stream);
