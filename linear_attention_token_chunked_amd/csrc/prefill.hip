@@ -35,6 +35,8 @@
 // other (the fp32 stage does not fit twice in LDS).  Accumulators feed the next
 // product straight from registers (see device_common.hpp).  Decay factors are
 // exp2 of log2(e)-scaled prefix sums; exp(G_i - G_j) is formed only for i >= j.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -223,16 +225,15 @@ struct ChunkRegs {
   }
 };
 
-// Gram tiles (ti >= tj) of each producer wave: at most three tiles and two
-// distinct token-row tiles ti per wave.
-__device__ __forceinline__ void gram_tiles(int w, int (&ti)[3], int (&tj)[3], int& nt) {
-  switch (w) {
-    case 0: ti[0] = 3; tj[0] = 0; ti[1] = 3; tj[1] = 1; ti[2] = 3; tj[2] = 2; nt = 3; break;
-    case 1: ti[0] = 3; tj[0] = 3; ti[1] = 2; tj[1] = 0; ti[2] = 2; tj[2] = 1; nt = 3; break;
-    case 2: ti[0] = 2; tj[0] = 2; ti[1] = 1; tj[1] = 0; ti[2] = 1; tj[2] = 0; nt = 2; break;
-    default: ti[0] = 1; tj[0] = 1; ti[1] = 0; tj[1] = 0; ti[2] = 0; tj[2] = 0; nt = 2; break;
-  }
-}
+// Gram tiles (ti >= tj) of producer wave W, grouped by token-row tile so that
+// a wave loads each B fragment (K and Q rows of tile ti) once per k-group:
+//   wave 0: (3,0) (3,1) (3,2)    wave 1: (2,0) (2,1) (2,2)
+//   wave 2: (1,0) (1,1)          wave 3: (0,0) (3,3)
+template <int W> struct GramTiles;
+template <> struct GramTiles<0> { static constexpr int n = 3, ti[3] = {3, 3, 3}, tj[3] = {0, 1, 2}; };
+template <> struct GramTiles<1> { static constexpr int n = 3, ti[3] = {2, 2, 2}, tj[3] = {0, 1, 2}; };
+template <> struct GramTiles<2> { static constexpr int n = 2, ti[3] = {1, 1, 0}, tj[3] = {0, 1, 0}; };
+template <> struct GramTiles<3> { static constexpr int n = 2, ti[3] = {0, 3, 0}, tj[3] = {0, 3, 0}; };
 
 template <class T, int DK, int DV, int BV, int NSTAGE>
 __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
   constexpr int KGC = C / MM::KG;   // k-groups over the chunk
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  float* sAd = reinterpret_cast<float*>(smem + L::oAd);  // [4][16][LDA] fp32 diagonal blocks of A
+  float* sAd = reinterpret_cast<float*>(smem + L::oAd);  // [4][16][LDA] fp32 diagonal blocks of A, transposed
   float* sGl = reinterpret_cast<float*>(smem + L::oGl);  // [C] G * log2(e)
 
   const int tid = threadIdx.x;
@@ -291,8 +292,6 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
 
   // ------------------------------------------------------------ producer state
   ChunkRegs<T, DK, BV> pre;
-  int gti[3], gtj[3], gnt = 0;
-  gram_tiles(producer ? wave : 0, gti, gtj, gnt);
   auto issue_loads = [&](int c) {
     const int cs = bos + c * C;
     const size_t tq = static_cast<size_t>(cs) * qk_tok + static_cast<size_t>(hq) * DK;
@@ -329,10 +328,11 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
   };
 
   // seg 2: K K^T and Q K^T tiles, masked with the decay.  The diagonal blocks
-  // of A go to LDS (fp32, for the inverses); -A below the diagonal and P stay
-  // in registers until segment 3.
+  // of A go to LDS transposed (fp32, for the inverses); -A below the diagonal
+  // and P stay in registers until segment 3.
   floatx4 pkeep[3], akeep[3];
-  auto prod_seg2 = [&](int s) {
+  auto gram = [&](auto wtag, int s) {
+    using GT = GramTiles<decltype(wtag)::value>;
     const unsigned char* S = stage(s);
     const T* sK = reinterpret_cast<const T*>(S + L::sK);
     const T* sQ = reinterpret_cast<const T*>(S + L::sQ);
@@ -342,54 +342,77 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
     for (int t = 0; t < 3; ++t) kk[t] = qk[t] = zero4();
 #pragma unroll
     for (int kgi = 0; kgi < KGK; ++kgi) {
+      frag rowk[4], rowq[4];  // fragments of token-row tiles; only the ones used are loaded
 #pragma unroll
-      for (int t = 0; t < 3; ++t) {
-        if (t < gnt) {
-          const frag a = lds_frag(sK + (16 * gtj[t] + lr) * LDK, kgi, lane);
-          MM::mma(kk[t], a, lds_frag(sK + (16 * gti[t] + lr) * LDK, kgi, lane));
-          MM::mma(qk[t], a, lds_frag(sQ + (16 * gti[t] + lr) * LDK, kgi, lane));
-        }
+      for (int t = 0; t < GT::n; ++t) {
+        rowk[GT::ti[t]] = lds_frag(sK + (16 * GT::ti[t] + lr) * LDK, kgi, lane);
+        rowq[GT::ti[t]] = lds_frag(sQ + (16 * GT::ti[t] + lr) * LDK, kgi, lane);
+        rowk[GT::tj[t]] = lds_frag(sK + (16 * GT::tj[t] + lr) * LDK, kgi, lane);
+      }
+#pragma unroll
+      for (int t = 0; t < GT::n; ++t) {
+        MM::mma(kk[t], rowk[GT::tj[t]], rowk[GT::ti[t]]);
+        MM::mma(qk[t], rowk[GT::tj[t]], rowq[GT::ti[t]]);
       }
     }
     // lane holds X[i = 16ti + lr][j = 16tj + 4lg + s] of both products
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
       pkeep[t] = akeep[t] = zero4();
-      if (t < gnt) {
-        const int i = 16 * gti[t] + lr;
+      if (t < GT::n) {
+        const int i = 16 * GT::ti[t] + lr;
         const float Gi = sGl[i], bi = beta[i];
+        const floatx4 Gj = *reinterpret_cast<const floatx4*>(sGl + 16 * GT::tj[t] + 4 * lg);
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
-          const int j = 16 * gtj[t] + 4 * lg + s4;
-          if (j <= i) {
-            const float d = __builtin_amdgcn_exp2f(Gi - sGl[j]);
-            akeep[t][s4] = (j < i) ? bi * d * kk[t][s4] : 0.f;
-            pkeep[t][s4] = d * qk[t][s4];
-          }
+          const int j = 16 * GT::tj[t] + 4 * lg + s4;
+          // exp(G_i - G_j) is formed only on and below the diagonal: exp2(-inf) = 0 above it
+          const float d = __builtin_amdgcn_exp2f(j <= i ? Gi - Gj[s4] : -__builtin_inff());
+          akeep[t][s4] = j < i ? bi * d * kk[t][s4] : 0.f;
+          pkeep[t][s4] = d * qk[t][s4];
         }
-        if (gti[t] == gtj[t]) *reinterpret_cast<floatx4*>(sAd + (gti[t] * 16 + lr) * LDA + 4 * lg) = akeep[t];
+        if (GT::ti[t] == GT::tj[t]) {
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4) sAd[(GT::ti[t] * 16 + 4 * lg + s4) * LDA + lr] = akeep[t][s4];
+        }
       }
     }
   };
+  auto prod_seg2 = [&](int s) {
+    switch (wave) {
+      case 0: gram(std::integral_constant<int, 0>(), s); break;
+      case 1: gram(std::integral_constant<int, 1>(), s); break;
+      case 2: gram(std::integral_constant<int, 2>(), s); break;
+      default: gram(std::integral_constant<int, 3>(), s); break;
+    }
+  };
 
-  // seg 3: P and -A into their (single) buffers; producer wave b inverts
-  // diagonal block b of I + A by forward substitution, one column per lane:
-  // x_i = [i == cc] - sum_{j<i} A_ij x_j.
-  auto prod_seg3 = [&]() {
+  // seg 3: P and -A into their (single) buffers; wave 0 inverts the four
+  // diagonal blocks of I + A, lane (blk, cc) computing column cc of block blk
+  // right-looking: once x_j is final, x_i -= A_ij x_j for every i > j.
+  auto put = [&](auto wtag) {
+    using GT = GramTiles<decltype(wtag)::value>;
     T* sP = reinterpret_cast<T*>(smem + L::oP);
     T* sAn = reinterpret_cast<T*>(smem + L::oAn);
 #pragma unroll
-    for (int t = 0; t < 3; ++t) {
-      if (t < gnt) {
-        const int i = 16 * gti[t] + lr;
-        *reinterpret_cast<V4*>(sP + i * LDC + MM::phys_k(16 * gtj[t] + 4 * lg)) =
-            pack4<T>(pkeep[t][0], pkeep[t][1], pkeep[t][2], pkeep[t][3]);
-        if (gti[t] != gtj[t])
-          *reinterpret_cast<V4*>(sAn + i * LDC + MM::phys_k(16 * gtj[t] + 4 * lg)) =
-              pack4<T>(-akeep[t][0], -akeep[t][1], -akeep[t][2], -akeep[t][3]);
-      }
+    for (int t = 0; t < GT::n; ++t) {
+      const int i = 16 * GT::ti[t] + lr;
+      *reinterpret_cast<V4*>(sP + i * LDC + MM::phys_k(16 * GT::tj[t] + 4 * lg)) =
+          pack4<T>(pkeep[t][0], pkeep[t][1], pkeep[t][2], pkeep[t][3]);
+      if (GT::ti[t] != GT::tj[t])
+        *reinterpret_cast<V4*>(sAn + i * LDC + MM::phys_k(16 * GT::tj[t] + 4 * lg)) =
+            pack4<T>(-akeep[t][0], -akeep[t][1], -akeep[t][2], -akeep[t][3]);
+    }
+  };
+  auto prod_seg3 = [&]() {
+    switch (wave) {
+      case 0: put(std::integral_constant<int, 0>()); break;
+      case 1: put(std::integral_constant<int, 1>()); break;
+      case 2: put(std::integral_constant<int, 2>()); break;
+      default: put(std::integral_constant<int, 3>()); break;
     }
     if (wave >= 2) {  // the six tiles of P above the diagonal are zero
+      T* sP = reinterpret_cast<T*>(smem + L::oP);
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
         const int zi = (wave == 2) ? 0 : (t == 2 ? 2 : 1);
@@ -398,27 +421,27 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
             pack4<T>(0.f, 0.f, 0.f, 0.f);
       }
     }
-    if (lane < 16) {
-      T* Tb = reinterpret_cast<T*>(smem + L::oTbb) + wave * 16 * LDT;
-      const float* Ab = sAd + wave * 16 * LDA;
-      const int cc = lane;
+    if (wave == 0) {
+      const int blk = lg, cc = lr;
+      const float* At = sAd + blk * 16 * LDA;  // At[j][i] = A_ij of the block
       float x[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float arow[16];
+      for (int i = 0; i < 16; ++i) x[i] = (i == cc) ? 1.f : 0.f;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const floatx4 a4 = *reinterpret_cast<const floatx4*>(Ab + i * LDA + 4 * q4);
-          arow[4 * q4] = a4[0];
-          arow[4 * q4 + 1] = a4[1];
-          arow[4 * q4 + 2] = a4[2];
-          arow[4 * q4 + 3] = a4[3];
+      for (int j = 0; j < 15; ++j) {
+        float col[16];
+#pragma unroll
+        for (int q4 = (j + 1) / 4; q4 < 4; ++q4) {
+          const floatx4 a4 = *reinterpret_cast<const floatx4*>(At + j * LDA + 4 * q4);
+          col[4 * q4] = a4[0];
+          col[4 * q4 + 1] = a4[1];
+          col[4 * q4 + 2] = a4[2];
+          col[4 * q4 + 3] = a4[3];
         }
-        float acc = (i == cc) ? 1.f : 0.f;
 #pragma unroll
-        for (int j = 0; j < i; ++j) acc -= arow[j] * x[j];
-        x[i] = acc;
+        for (int i = j + 1; i < 16; ++i) x[i] -= col[i] * x[j];
       }
+      T* Tb = reinterpret_cast<T*>(smem + L::oTbb) + blk * 16 * LDT;
 #pragma unroll
       for (int i = 0; i < 16; ++i) Tb[i * LDT + cc] = from_float<T>(x[i]);
     }
