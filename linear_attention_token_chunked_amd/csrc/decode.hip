@@ -108,10 +108,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   u[2] = b * (v2 - alpha * r[2]);
   u[3] = b * (v3 - alpha * r[3]);
 
+  // The updated state is not read again until the next step, after the rest of
+  // the state (and, in a model, every other layer) has streamed through the
+  // caches, so it is written with non-temporal stores.  Measured on MI355X at
+  // 256 sequences x 32 heads: 6.4 TB/s against 5.1 TB/s with ordinary stores
+  // (non-temporal loads, by contrast, are slower).
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const float ki = sk[rg + RG * i];
-    *reinterpret_cast<floatx4*>(M + static_cast<size_t>(rg + RG * i) * DV + 4 * cg) = alpha * m[i] + ki * u;
+    __builtin_nontemporal_store(alpha * m[i] + ki * u,
+                                reinterpret_cast<floatx4*>(M + static_cast<size_t>(rg + RG * i) * DV + 4 * cg));
   }
   if (rg == 0) {
     const floatx4 ov = scale * (alpha * p + kq * u);

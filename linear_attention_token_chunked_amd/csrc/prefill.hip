@@ -26,7 +26,9 @@
 //     U_b = T_bb (Z_b - sum_{m<b} A_bm U_m), the output tile O^T, and the
 //     state update.
 // Each chunk takes three segments separated by workgroup barriers that order
-// LDS only, so the producers' global loads for chunk n+2 stay in flight.
+// LDS only, so the producers' global loads, issued a chunk ahead, stay in
+// flight.  P, -A and the block inverses are single-buffered: producers write
+// chunk n+1's copies only after the consumers have used chunk n's.
 //
 // Matrix cores: bf16 inputs use v_mfma_f32_16x16x32_bf16 (K = 16 blocks:
 // v_mfma_f32_16x16x16_bf16) with fp32 accumulation; the state, Z and U are
@@ -288,11 +290,11 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
   const size_t qk_tok = static_cast<size_t>(p.Hqk) * DK;
   const size_t v_tok = static_cast<size_t>(p.Hv) * DV;
 
-  auto stage = [&](int s) { return smem + s * L::stage_bytes; };
+  auto stage = [&](int s) __attribute__((always_inline)) { return smem + s * L::stage_bytes; };
 
   // ------------------------------------------------------------ producer state
   ChunkRegs<T, DK, BV> pre;
-  auto issue_loads = [&](int c) {
+  auto issue_loads = [&](int c) __attribute__((always_inline)) {
     const int cs = bos + c * C;
     const size_t tq = static_cast<size_t>(cs) * qk_tok + static_cast<size_t>(hq) * DK;
     const size_t tv = static_cast<size_t>(cs) * v_tok + static_cast<size_t>(h) * DV + col0;
@@ -300,8 +302,8 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
     pre.load(kgp + tq, qg + tq, vg + tv, qk_tok, v_tok, p.g + tg, p.beta + tg, p.Hv, min(C, eos - cs), tid);
   };
 
-  // seg 1: stage the chunk's K, Q, V and gates; issue the next chunk's loads.
-  auto prod_seg1 = [&](int c, int s) {
+  // Stage the chunk's K, Q, V and gates; issue the next chunk's loads.
+  auto prod_stores = [&](int c, int s) __attribute__((always_inline)) {
     unsigned char* S = stage(s);
     const int cs = bos + c * C, Lc = min(C, eos - cs);
     pre.store(reinterpret_cast<T*>(S + L::sK), reinterpret_cast<T*>(S + L::sQ), reinterpret_cast<T*>(S + L::sV), LDK,
@@ -327,11 +329,11 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
     if (c + 1 < nch) issue_loads(c + 1);
   };
 
-  // seg 2: K K^T and Q K^T tiles, masked with the decay.  The diagonal blocks
-  // of A go to LDS transposed (fp32, for the inverses); -A below the diagonal
-  // and P stay in registers until segment 3.
+  // K K^T and Q K^T tiles, masked with the decay.  The diagonal blocks of A go
+  // to LDS transposed (fp32, for the inverses); -A below the diagonal and P stay
+  // in registers until prod_finish.
   floatx4 pkeep[3], akeep[3];
-  auto gram = [&](auto wtag, int s) {
+  auto gram = [&](auto wtag, int s) __attribute__((always_inline)) {
     using GT = GramTiles<decltype(wtag)::value>;
     const unsigned char* S = stage(s);
     const T* sK = reinterpret_cast<const T*>(S + L::sK);
@@ -378,7 +380,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
       }
     }
   };
-  auto prod_seg2 = [&](int s) {
+  auto prod_gram = [&](int s) __attribute__((always_inline)) {
     switch (wave) {
       case 0: gram(std::integral_constant<int, 0>(), s); break;
       case 1: gram(std::integral_constant<int, 1>(), s); break;
@@ -387,10 +389,10 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
     }
   };
 
-  // seg 3: P and -A into their (single) buffers; wave 0 inverts the four
-  // diagonal blocks of I + A, lane (blk, cc) computing column cc of block blk
+  // P and -A into their (single) buffers; wave 0 inverts the four diagonal
+  // blocks of I + A, lane (blk, cc) computing column cc of block blk
   // right-looking: once x_j is final, x_i -= A_ij x_j for every i > j.
-  auto put = [&](auto wtag) {
+  auto put = [&](auto wtag) __attribute__((always_inline)) {
     using GT = GramTiles<decltype(wtag)::value>;
     T* sP = reinterpret_cast<T*>(smem + L::oP);
     T* sAn = reinterpret_cast<T*>(smem + L::oAn);
@@ -404,7 +406,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
             pack4<T>(-akeep[t][0], -akeep[t][1], -akeep[t][2], -akeep[t][3]);
     }
   };
-  auto prod_seg3 = [&]() {
+  auto prod_finish = [&]() __attribute__((always_inline)) {
     switch (wave) {
       case 0: put(std::integral_constant<int, 0>()); break;
       case 1: put(std::integral_constant<int, 1>()); break;
@@ -451,6 +453,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
   // Ms[a][j] holds M[16a + 4lg + s][wcol + 16j + lr], s = 0..3.
   floatx4 Ms[KT][NTW];
   floatx4 Z[4][NTW];  // Z, then U, by 16-row token block
+  frag mfr[KGK][NTW];  // the state as matrix-core operands (bf16-rounded for bf16 inputs), per chunk
   const size_t sbase = static_cast<size_t>(unit) * DK * DV;
   if (!producer) {
 #pragma unroll
@@ -464,7 +467,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
   }
 
   // seg 1: Y = K M; Z = beta (V - exp(G) Y).
-  auto cons_seg1 = [&](int s) {
+  auto cons_seg1 = [&](int s) __attribute__((always_inline)) {
     const unsigned char* S = stage(s);
     const T* sK = reinterpret_cast<const T*>(S + L::sK);
     const T* sV = reinterpret_cast<const T*>(S + L::sV);
@@ -474,15 +477,16 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
 #pragma unroll
       for (int j = 0; j < NTW; ++j) Z[r][j] = zero4();
 #pragma unroll
-    for (int kgi = 0; kgi < KGK; ++kgi) {
-      frag bm[NTW];
+    for (int kgi = 0; kgi < KGK; ++kgi)
 #pragma unroll
-      for (int j = 0; j < NTW; ++j) bm[j] = chain_frag<T>([&](int t) { return Ms[t][j]; }, kgi);
+      for (int j = 0; j < NTW; ++j) mfr[kgi][j] = chain_frag<T>([&](int t) { return Ms[t][j]; }, kgi);
+#pragma unroll
+    for (int kgi = 0; kgi < KGK; ++kgi) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const frag af = lds_frag(sK + (16 * r + lr) * LDK, kgi, lane);
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) MM::mma(Z[r][j], af, bm[j]);
+        for (int j = 0; j < NTW; ++j) MM::mma(Z[r][j], af, mfr[kgi][j]);
       }
     }
 #pragma unroll
@@ -503,7 +507,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
   };
 
   // seg 2: U by block forward substitution, then the output tile O^T.
-  auto cons_seg2 = [&](int c, int s) {
+  auto cons_seg2 = [&](int c, int s) __attribute__((always_inline)) {
     const unsigned char* S = stage(s);
     const T* sQ = reinterpret_cast<const T*>(S + L::sQ);
     const T* sAn = reinterpret_cast<const T*>(smem + L::oAn);
@@ -534,34 +538,49 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
         Z[b][j] = u;  // Z_b is not needed any more
       }
     }
-    // O^T = M^T Q^T diag(exp G) + U^T P^T, one 16x16 tile per (own n-tile j, token tile ct)
+    // O^T = M^T Q^T diag(exp G) + U^T P^T, one 16x16 tile per (token tile ct, own n-tile j);
+    // every Q and P fragment read from LDS feeds all of the wave's n-tiles
+    frag ufr[KGC][NTW];
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) {
+    for (int kgi = 0; kgi < KGC; ++kgi)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        floatx4 acc = zero4();
+      for (int j = 0; j < NTW; ++j) ufr[kgi][j] = chain_frag<T>([&](int t) { return Z[t][j]; }, kgi);
 #pragma unroll
-        for (int kgi = 0; kgi < KGK; ++kgi)
-          MM::mma(acc, chain_frag<T>([&](int t) { return Ms[t][j]; }, kgi),
-                  lds_frag(sQ + (16 * ct + lr) * LDK, kgi, lane));
-        acc *= vec[16 * ct + lr];
+    for (int ct = 0; ct < 4; ++ct) {
+      floatx4 acc[NTW];
 #pragma unroll
-        for (int kgi = 0; kgi < KGC; ++kgi) {
-          if (kgi * MM::KG <= 16 * ct + 15)  // P is zero above the diagonal
-            MM::mma(acc, chain_frag<T>([&](int t) { return Z[t][j]; }, kgi),
-                    lds_frag(sP + (16 * ct + lr) * LDC, kgi, lane));
+      for (int j = 0; j < NTW; ++j) acc[j] = zero4();
+#pragma unroll
+      for (int kgi = 0; kgi < KGK; ++kgi) {
+        const frag qf = lds_frag(sQ + (16 * ct + lr) * LDK, kgi, lane);
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) MM::mma(acc[j], mfr[kgi][j], qf);
+      }
+      const float eg = vec[16 * ct + lr];
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) acc[j] *= eg;
+#pragma unroll
+      for (int kgi = 0; kgi < KGC; ++kgi) {
+        if (kgi * MM::KG <= 16 * ct + 15) {  // P is zero above the diagonal
+          const frag pf = lds_frag(sP + (16 * ct + lr) * LDC, kgi, lane);
+#pragma unroll
+          for (int j = 0; j < NTW; ++j) MM::mma(acc[j], ufr[kgi][j], pf);
         }
-        acc *= p.scale;
-        const int tok = 16 * ct + lr;  // lane holds O[tok][wcol + 16j + 4lg + s]
-        if (tok < Lc)
+      }
+      const int tok = 16 * ct + lr;  // lane holds O[tok][wcol + 16j + 4lg + s]
+      if (tok < Lc) {
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+          const floatx4 ov = acc[j] * p.scale;
           *reinterpret_cast<V4*>(og + static_cast<size_t>(cs + tok) * v_tok + static_cast<size_t>(h) * DV + wcol +
-                                 16 * j + 4 * lg) = pack4<T>(acc[0], acc[1], acc[2], acc[3]);
+                                 16 * j + 4 * lg) = pack4<T>(ov[0], ov[1], ov[2], ov[3]);
+        }
       }
     }
   };
 
   // seg 3: M <- exp(G_C) M + K^T (diag(exp(G_C - G)) U).
-  auto cons_seg3 = [&](int s) {
+  auto cons_seg3 = [&](int s) __attribute__((always_inline)) {
     const unsigned char* S = stage(s);
     const T* sK = reinterpret_cast<const T*>(S + L::sK);
     const float* vec = reinterpret_cast<const float*>(S + L::sVec);
@@ -601,30 +620,37 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
 
   // ------------------------------------------------------------ schedule
   // Producers and consumers run separate loops (so their registers are never
-  // live at the same time) that execute the same sequence of barriers.
+  // live at the same time) that execute the same sequence of barriers.  With
+  // a double-buffered stage, iteration c runs three segments:
+  //            producers                              consumers (chunk c)
+  //   seg 1    inverses, P and -A of chunk c          Y = K M, Z
+  //   seg 2    K, Q, V, gates of chunk c + 1          U, O
+  //   seg 3    Gram products of chunk c + 1           state update
   if (producer) {
     if (nch > 0) issue_loads(0);
     if constexpr (NSTAGE == 2) {
-      for (int c = 0; c < nch; ++c) {  // chunk c into stage c & 1, one chunk ahead of the consumers
-        prod_seg1(c, c & 1);
+      if (nch > 0) {
+        prod_stores(0, 0);
         lds_barrier();
-        prod_seg2(c & 1);
-        lds_barrier();
-        prod_seg3();
+        prod_gram(0);
         lds_barrier();
       }
-      if (nch > 0) {  // the consumers' last chunk
-        lds_barrier();
-        lds_barrier();
-        lds_barrier();
-      }
-    } else {
       for (int c = 0; c < nch; ++c) {
-        prod_seg1(c, 0);
+        const bool more = c + 1 < nch;
+        prod_finish();
         lds_barrier();
-        prod_seg2(0);
+        if (more) prod_stores(c + 1, (c + 1) & 1);
         lds_barrier();
-        prod_seg3();
+        if (more) prod_gram((c + 1) & 1);
+        lds_barrier();
+      }
+    } else {  // one stage: the two roles take turns
+      for (int c = 0; c < nch; ++c) {
+        prod_stores(c, 0);
+        lds_barrier();
+        prod_gram(0);
+        lds_barrier();
+        prod_finish();
         lds_barrier();
         lds_barrier();
         lds_barrier();
@@ -633,8 +659,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
     }
   } else {
     if constexpr (NSTAGE == 2) {
-      if (nch > 0) {  // the producers' first chunk
-        lds_barrier();
+      if (nch > 0) {
         lds_barrier();
         lds_barrier();
       }
