@@ -38,6 +38,7 @@
 // product straight from registers (see device_common.hpp).  Decay factors are
 // exp2 of log2(e)-scaled prefix sums; exp(G_i - G_j) is formed only for i >= j.
 #include <type_traits>
+#include <utility>
 
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -51,6 +52,38 @@ constexpr int NCW = 4;                   // consumer wavefronts
 constexpr int NTHREADS = 64 * (NP + NCW);
 constexpr int PTHREADS = 64 * NP;
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP row shifts
+// and row broadcasts (no LDS round trips).
+__device__ __forceinline__ float wave_inclusive_sum(float x) {
+#define GDN_DPP_ADD(ctrl, rows)                                                                               \
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, rows, 0xf, false))
+  GDN_DPP_ADD(0x111, 0xf);  // row_shr:1
+  GDN_DPP_ADD(0x112, 0xf);  // row_shr:2
+  GDN_DPP_ADD(0x114, 0xf);  // row_shr:4
+  GDN_DPP_ADD(0x118, 0xf);  // row_shr:8
+  GDN_DPP_ADD(0x142, 0xa);  // row_bcast:15 into rows 1 and 3
+  GDN_DPP_ADD(0x143, 0xc);  // row_bcast:31 into rows 2 and 3
+#undef GDN_DPP_ADD
+  return x;
+}
+
+// Every lane gets x from lane S of its group of four (DPP quad permutation).
+template <int S>
+__device__ __forceinline__ float quad_bcast(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x55 * S, 0xf, 0xf, false));
+}
+
+// Column cc of (I + A)^-1 for a 16x16 strictly lower A by right-looking
+// forward substitution, four lanes per column: the lane with q = lane % 4
+// holds rows 4q..4q+3 in x.  Once x_j is final (step j) it is broadcast
+// within the quad and every row i > j takes x_i -= A_ij x_j; At[j][i] = A_ij
+// (zero for i <= j, so the other rows are unchanged).
+template <int... J>
+__device__ __forceinline__ void unit_lower_inverse_column(floatx4& x, const float* At, int ld, int q,
+                                                          std::integer_sequence<int, J...>) {
+  ((x -= *reinterpret_cast<const floatx4*>(At + J * ld + 4 * q) * quad_bcast<J / 4>(x[J % 4])), ...);
+}
 
 // 16x16 tile products whose contraction is one 16-wide block: lane group g
 // supplies k = 4g..4g+3, which is the row set it owns in an accumulator tile.
@@ -110,6 +143,33 @@ __device__ __forceinline__ typename Vec4<T>::type lds_col4(const T* base, int ld
   }
 }
 
+// bf16 tiles that are read only down their columns (the natural-order copy of
+// K and the V tile) store the 16-column blocks of a row at swizzled places:
+// block b of row r sits at block b ^ swz(r).  A transposing read covers four
+// rows of one block per 16-lane group and eight rows per 32 lanes; the
+// swizzle puts those eight rows' 32-byte runs on eight different bank windows
+// (unswizzled, 256-byte rows would put them all on the same one).
+template <int W>
+__device__ __forceinline__ int swz(int r) {
+  constexpr int NB = W / 16;                    // 16-column blocks per row
+  constexpr int RPW = W >= 128 ? 1 : 128 / W;   // rows per 256 bytes
+  return (r / RPW) & (NB - 1);
+}
+template <int W>
+__device__ __forceinline__ int swz_off(int r, int c) {  // element offset of column c of row r
+  return r * W + ((((c >> 4) ^ swz<W>(r)) << 4) | (c & 15));
+}
+// lds_col4<bf16, false> for a swizzled tile of width W.
+template <int W>
+__device__ __forceinline__ bf16x4 swz_col4(const bf16* base, int r0, int c0, int lane) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  const int lg = lane >> 4, lr = lane & 15;
+  const bf16* ptr = base + swz_off<W>(r0 + 4 * lg + (lr >> 2), c0 + 4 * (lr & 3));
+  const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) s4*>(reinterpret_cast<size_t>(ptr)));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
 // Operand fragment of k-group kg built from accumulator tiles tile(kg*TPG + t).
 template <class T, class F>
 __device__ __forceinline__ typename Mma<T>::frag chain_frag(F tile, int kg) {
@@ -125,16 +185,21 @@ template <class T, int DK, int BV, int NSTAGE>
 struct Layout {
   static constexpr int EPB = 16 / sizeof(T);
   static constexpr int NTW = BV / (16 * NCW);   // 16-column state tiles per consumer wave
-  static constexpr int LDK = DK + EPB;          // [C][DK] rows: K
+  static constexpr int LDK = DK + EPB;          // [C][DK] rows: K, Q (key axis in phys_k order)
   static constexpr int LDC = C + EPB;           // [*][C] rows: P, -A
-  static constexpr int LDV = BV + EPB;          // [C][BV] rows: V
+  static constexpr int LDV = BV;                // [C][BV] rows: V (only read down its columns; bf16 swizzled)
+  // bf16 keeps a second copy of K with the key axis in natural order
+  // (swizzled): the transposing reads of K^T then load whole 32-byte runs, at
+  // half the cost of reading them out of the phys_k copy.
+  static constexpr bool KNAT = sizeof(T) == 2;
   static constexpr int LDT = 20;                // [16][16] diagonal-block inverses
   static constexpr int LDA = 20;                // fp32 diagonal blocks of A
   // one stage, double-buffered: written by the producers in segment 1
   static constexpr size_t sK = 0;
   static constexpr size_t sQ = sK + sizeof(T) * C * LDK;
   static constexpr size_t sV = sQ + sizeof(T) * C * LDK;
-  static constexpr size_t sVec = sV + sizeof(T) * C * LDV;  // exp G, beta, exp(G_C - G), exp G_C
+  static constexpr size_t sKn = sV + sizeof(T) * C * LDV;   // [C][DK] K, natural key order (bf16)
+  static constexpr size_t sVec = sKn + (KNAT ? sizeof(T) * C * DK : 0);  // exp G, beta, exp(G_C - G), exp G_C
   static constexpr size_t stage_bytes = (sVec + 4 * 4 * C + 15) / 16 * 16;
   // single-buffered: written by the producers in segment 3, after the
   // consumers have read the previous chunk's copy in segment 2
@@ -146,7 +211,7 @@ struct Layout {
   static constexpr size_t oGl = oAd + 4 * 4 * 16 * LDA;
   static constexpr size_t bytes = oGl + 4 * C;
   static_assert(BV % (16 * NCW) == 0, "every consumer wave owns whole 16-column tiles");
-  static_assert(sQ % 16 == 0 && sV % 16 == 0 && sVec % 16 == 0 && oP % 16 == 0 &&
+  static_assert(sQ % 16 == 0 && sV % 16 == 0 && sKn % 16 == 0 && sVec % 16 == 0 && oP % 16 == 0 &&
                 oAn % 16 == 0 && oTbb % 16 == 0 && oAd % 16 == 0, "16-byte aligned LDS regions");
 };
 
@@ -200,13 +265,16 @@ struct ChunkRegs {
     }
   }
 
-  // K, Q -> rows with the key axis in phys_k order; V -> rows in natural order.
-  __device__ __forceinline__ void store(T* sK, T* sQ, T* sV, int LDK, int LDV, int tid) const {
+  // K, Q -> rows with the key axis in phys_k order; V and (if sKn) a second
+  // copy of K -> rows in natural order.
+  __device__ __forceinline__ void store(T* sK, T* sQ, T* sV, T* sKn, int LDK, int LDV, int tid) const {
     typedef typename Vec4<T>::type V4;
 #pragma unroll
     for (int it = 0; it < KIT; ++it) {
       const int t = tid + it * PTHREADS;
       const int r = t / KPR, c = (t % KPR) * EPB;
+      if constexpr (sizeof(T) == 2)
+        if (sKn) *reinterpret_cast<frag*>(sKn + swz_off<DK>(r, c)) = k[it];
 #pragma unroll
       for (int u = 0; u < EPB / 4; ++u) {
         V4 wk, wq;
@@ -222,7 +290,10 @@ struct ChunkRegs {
 #pragma unroll
     for (int it = 0; it < VIT; ++it) {
       const int t = tid + it * PTHREADS;
-      if (t < C * VPR) *reinterpret_cast<frag*>(sV + (t / VPR) * LDV + (t % VPR) * EPB) = v[it];
+      if (t < C * VPR) {
+        const int r = t / VPR, c = (t % VPR) * EPB;
+        *reinterpret_cast<frag*>(sV + (sizeof(T) == 2 ? swz_off<BV>(r, c) : r * LDV + c)) = v[it];
+      }
     }
   }
 };
@@ -306,19 +377,14 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
   auto prod_stores = [&](int c, int s) __attribute__((always_inline)) {
     unsigned char* S = stage(s);
     const int cs = bos + c * C, Lc = min(C, eos - cs);
-    pre.store(reinterpret_cast<T*>(S + L::sK), reinterpret_cast<T*>(S + L::sQ), reinterpret_cast<T*>(S + L::sV), LDK,
-              LDV, tid);
+    pre.store(reinterpret_cast<T*>(S + L::sK), reinterpret_cast<T*>(S + L::sQ), reinterpret_cast<T*>(S + L::sV),
+              L::KNAT ? reinterpret_cast<T*>(S + L::sKn) : nullptr, LDK, LDV, tid);
     if (wave == 0) {
       const bool live = lane < Lc;  // tokens past the end act as g = 0, beta = 0 (exact no-ops)
       const float bt = live ? pre.b : 0.f;
-      float G = live ? pre.g : 0.f;  // inclusive prefix sum of the log-gates over the chunk
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(G, off);
-        if (lane >= off) G += y;
-      }
-      const float Gl = G * kLog2e;
-      const float GlC = __shfl(Gl, 63);
+      // inclusive prefix sum of the log-gates over the chunk
+      const float Gl = wave_inclusive_sum(live ? pre.g : 0.f) * kLog2e;
+      const float GlC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, Gl), 63));
       float* vec = reinterpret_cast<float*>(S + L::sVec);
       vec[lane] = __builtin_amdgcn_exp2f(Gl);
       vec[C + lane] = bt;
@@ -389,9 +455,8 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
     }
   };
 
-  // P and -A into their (single) buffers; wave 0 inverts the four diagonal
-  // blocks of I + A, lane (blk, cc) computing column cc of block blk
-  // right-looking: once x_j is final, x_i -= A_ij x_j for every i > j.
+  // P and -A into their (single) buffers; each producer wave inverts one of
+  // the four diagonal blocks of I + A.
   auto put = [&](auto wtag) __attribute__((always_inline)) {
     using GT = GramTiles<decltype(wtag)::value>;
     T* sP = reinterpret_cast<T*>(smem + L::oP);
@@ -423,53 +488,65 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
             pack4<T>(0.f, 0.f, 0.f, 0.f);
       }
     }
-    if (wave == 0) {
-      const int blk = lg, cc = lr;
-      const float* At = sAd + blk * 16 * LDA;  // At[j][i] = A_ij of the block
-      float x[16];
+    {  // producer wave w inverts diagonal block w of I + A
+      const int cc = lane >> 2, q = lane & 3;
+      const float* At = sAd + wave * 16 * LDA;  // At[j][i] = A_ij of the block
+      floatx4 x;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = (i == cc) ? 1.f : 0.f;
+      for (int t = 0; t < 4; ++t) x[t] = (4 * q + t == cc) ? 1.f : 0.f;
+      unit_lower_inverse_column(x, At, LDA, q, std::make_integer_sequence<int, 15>());
+      T* Tb = reinterpret_cast<T*>(smem + L::oTbb) + wave * 16 * LDT;
 #pragma unroll
-      for (int j = 0; j < 15; ++j) {
-        float col[16];
-#pragma unroll
-        for (int q4 = (j + 1) / 4; q4 < 4; ++q4) {
-          const floatx4 a4 = *reinterpret_cast<const floatx4*>(At + j * LDA + 4 * q4);
-          col[4 * q4] = a4[0];
-          col[4 * q4 + 1] = a4[1];
-          col[4 * q4 + 2] = a4[2];
-          col[4 * q4 + 3] = a4[3];
-        }
-#pragma unroll
-        for (int i = j + 1; i < 16; ++i) x[i] -= col[i] * x[j];
-      }
-      T* Tb = reinterpret_cast<T*>(smem + L::oTbb) + blk * 16 * LDT;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) Tb[i * LDT + cc] = from_float<T>(x[i]);
+      for (int t = 0; t < 4; ++t) Tb[(4 * q + t) * LDT + cc] = from_float<T>(x[t]);
     }
   };
+
 
   // ------------------------------------------------------------ consumer state
   // Ms[a][j] holds M[16a + 4lg + s][wcol + 16j + lr], s = 0..3.
   floatx4 Ms[KT][NTW];
   floatx4 Z[4][NTW];  // Z, then U, by 16-row token block
   frag mfr[KGK][NTW];  // the state as matrix-core operands (bf16-rounded for bf16 inputs), per chunk
+  // the unit's state: uniform base, small per-lane offsets (keeps 64-bit
+  // per-element addresses out of the registers)
   const size_t sbase = static_cast<size_t>(unit) * DK * DV;
+  const int slane = 4 * lg * DV + wcol + lr;
   if (!producer) {
+    const float* h0 = p.h0 + sbase;
 #pragma unroll
     for (int a = 0; a < KT; ++a)
 #pragma unroll
       for (int j = 0; j < NTW; ++j)
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          Ms[a][j][s] = p.h0 ? p.h0[sbase + static_cast<size_t>(16 * a + 4 * lg + s) * DV + wcol + 16 * j + lr]
-                             : 0.f;
+        for (int s = 0; s < 4; ++s) Ms[a][j][s] = p.h0 ? h0[slane + (16 * a + s) * DV + 16 * j] : 0.f;
   }
 
-  // seg 1: Y = K M; Z = beta (V - exp(G) Y).
+  // seg 1: Y = K M; Z = beta (V - exp(G) Y).  With one state tile per wave the
+  // state part of the output, O^T = diag-scaled (Q M)^T, is formed here too,
+  // next to K M which takes the same operands; with two, holding it until
+  // seg 2 would exceed the register budget, and seg 2 forms it instead.
+  constexpr bool QM_EARLY = NTW == 1;
+  floatx4 Ot[4][NTW];  // O^T by 16-token tile: lane holds O[16ct + lr][wcol + 16j + 4lg + s]
+  auto q_times_state = [&](const T* sQ, const float* vec) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) Ot[r][j] = zero4();
+#pragma unroll
+      for (int kgi = 0; kgi < KGK; ++kgi) {
+        const frag qf = lds_frag(sQ + (16 * r + lr) * LDK, kgi, lane);
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) MM::mma(Ot[r][j], mfr[kgi][j], qf);
+      }
+      const float egt = vec[16 * r + lr];  // exp(G) of the token this lane holds in O^T
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) Ot[r][j] *= egt;
+    }
+  };
   auto cons_seg1 = [&](int s) __attribute__((always_inline)) {
     const unsigned char* S = stage(s);
     const T* sK = reinterpret_cast<const T*>(S + L::sK);
+    const T* sQ = reinterpret_cast<const T*>(S + L::sQ);
     const T* sV = reinterpret_cast<const T*>(S + L::sV);
     const float* vec = reinterpret_cast<const float*>(S + L::sVec);
 #pragma unroll
@@ -489,6 +566,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
         for (int j = 0; j < NTW; ++j) MM::mma(Z[r][j], af, mfr[kgi][j]);
       }
     }
+    if constexpr (QM_EARLY) q_times_state(sQ, vec);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float eg[4], bt[4];
@@ -499,21 +577,29 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
       }
 #pragma unroll
       for (int j = 0; j < NTW; ++j) {
-        const V4 v4 = lds_col4<T, false>(sV, LDV, 16 * r, (cw * NTW + j) * 16, lane);
+        V4 v4;
+        if constexpr (sizeof(T) == 2)
+          v4 = swz_col4<BV>(sV, 16 * r, (cw * NTW + j) * 16, lane);
+        else
+          v4 = lds_col4<T, false>(sV, LDV, 16 * r, (cw * NTW + j) * 16, lane);
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) Z[r][j][s4] = bt[s4] * (to_float(v4[s4]) - eg[s4] * Z[r][j][s4]);
       }
     }
   };
 
-  // seg 2: U by block forward substitution, then the output tile O^T.
+  // seg 2: U by block forward substitution; O^T += U^T P^T; O -> HBM.
   auto cons_seg2 = [&](int c, int s) __attribute__((always_inline)) {
-    const unsigned char* S = stage(s);
-    const T* sQ = reinterpret_cast<const T*>(S + L::sQ);
+    if constexpr (!QM_EARLY) {  // the state operands are formed again rather than held over the barrier
+#pragma unroll
+      for (int kgi = 0; kgi < KGK; ++kgi)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) mfr[kgi][j] = chain_frag<T>([&](int t) { return Ms[t][j]; }, kgi);
+      q_times_state(reinterpret_cast<const T*>(stage(s) + L::sQ), reinterpret_cast<const float*>(stage(s) + L::sVec));
+    }
     const T* sAn = reinterpret_cast<const T*>(smem + L::oAn);
     const T* sTbb = reinterpret_cast<const T*>(smem + L::oTbb);
     const T* sP = reinterpret_cast<const T*>(smem + L::oP);
-    const float* vec = reinterpret_cast<const float*>(S + L::sVec);
     const int cs = bos + c * C, Lc = min(C, eos - cs);
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
@@ -538,51 +624,50 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
         Z[b][j] = u;  // Z_b is not needed any more
       }
     }
-    // O^T = M^T Q^T diag(exp G) + U^T P^T, one 16x16 tile per (token tile ct, own n-tile j);
-    // every Q and P fragment read from LDS feeds all of the wave's n-tiles
-    frag ufr[KGC][NTW];
+    // every P fragment read from LDS feeds all of the wave's n-tiles
 #pragma unroll
-    for (int kgi = 0; kgi < KGC; ++kgi)
+    for (int kgi = 0; kgi < KGC; ++kgi) {
+      frag uf[NTW];
 #pragma unroll
-      for (int j = 0; j < NTW; ++j) ufr[kgi][j] = chain_frag<T>([&](int t) { return Z[t][j]; }, kgi);
+      for (int j = 0; j < NTW; ++j) uf[j] = chain_frag<T>([&](int t) { return Z[t][j]; }, kgi);
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      floatx4 acc[NTW];
-#pragma unroll
-      for (int j = 0; j < NTW; ++j) acc[j] = zero4();
-#pragma unroll
-      for (int kgi = 0; kgi < KGK; ++kgi) {
-        const frag qf = lds_frag(sQ + (16 * ct + lr) * LDK, kgi, lane);
-#pragma unroll
-        for (int j = 0; j < NTW; ++j) MM::mma(acc[j], mfr[kgi][j], qf);
-      }
-      const float eg = vec[16 * ct + lr];
-#pragma unroll
-      for (int j = 0; j < NTW; ++j) acc[j] *= eg;
-#pragma unroll
-      for (int kgi = 0; kgi < KGC; ++kgi) {
+      for (int ct = 0; ct < 4; ++ct) {
         if (kgi * MM::KG <= 16 * ct + 15) {  // P is zero above the diagonal
           const frag pf = lds_frag(sP + (16 * ct + lr) * LDC, kgi, lane);
 #pragma unroll
-          for (int j = 0; j < NTW; ++j) MM::mma(acc[j], ufr[kgi][j], pf);
+          for (int j = 0; j < NTW; ++j) MM::mma(Ot[ct][j], uf[j], pf);
         }
       }
-      const int tok = 16 * ct + lr;  // lane holds O[tok][wcol + 16j + 4lg + s]
-      if (tok < Lc) {
+    }
+    T* orow = og + static_cast<size_t>(cs + lr) * v_tok + static_cast<size_t>(h) * DV + wcol + 4 * lg;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      if (16 * ct + lr < Lc) {
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
-          const floatx4 ov = acc[j] * p.scale;
-          *reinterpret_cast<V4*>(og + static_cast<size_t>(cs + tok) * v_tok + static_cast<size_t>(h) * DV + wcol +
-                                 16 * j + 4 * lg) = pack4<T>(ov[0], ov[1], ov[2], ov[3]);
+          const floatx4 ov = Ot[ct][j] * p.scale;
+          *reinterpret_cast<V4*>(orow + static_cast<size_t>(16 * ct) * v_tok + 16 * j) =
+              pack4<T>(ov[0], ov[1], ov[2], ov[3]);
         }
       }
     }
   };
 
   // seg 3: M <- exp(G_C) M + K^T (diag(exp(G_C - G)) U).
+  // The swizzled tiles' read addresses depend on the lane in a way the
+  // compiler would precompute for every column block and keep live across the
+  // loop; an opaque copy of the lane index, renewed each chunk, makes it form
+  // them where they are used instead.
+  auto opaque_lane = [&]() __attribute__((always_inline)) {
+    int v = lane;
+    asm volatile("" : "+v"(v));
+    return v;
+  };
   auto cons_seg3 = [&](int s) __attribute__((always_inline)) {
     const unsigned char* S = stage(s);
+    const int olane = opaque_lane();
     const T* sK = reinterpret_cast<const T*>(S + L::sK);
+    const T* sKn = reinterpret_cast<const T*>(S + L::sKn);
     const float* vec = reinterpret_cast<const float*>(S + L::sVec);
     const float eGC = vec[3 * C];
 #pragma unroll
@@ -606,9 +691,8 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
       for (int a = 0; a < KT; ++a) {
         frag af;  // K^T rows 16a.., tokens of k-group kgi, from the row-major K tile
         if constexpr (MM::KG == 32) {
-          af = __builtin_shufflevector(lds_col4<T, true>(sK, LDK, 32 * kgi, 16 * a, lane),
-                                       lds_col4<T, true>(sK, LDK, 32 * kgi + 16, 16 * a, lane), 0, 1, 2, 3, 4,
-                                       5, 6, 7);
+          af = __builtin_shufflevector(swz_col4<DK>(sKn, 32 * kgi, 16 * a, olane),
+                                       swz_col4<DK>(sKn, 32 * kgi + 16, 16 * a, olane), 0, 1, 2, 3, 4, 5, 6, 7);
         } else {
           af = lds_col4<T, true>(sK, LDK, 16 * kgi, 16 * a, lane);
         }
@@ -623,7 +707,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
   // live at the same time) that execute the same sequence of barriers.  With
   // a double-buffered stage, iteration c runs three segments:
   //            producers                              consumers (chunk c)
-  //   seg 1    inverses, P and -A of chunk c          Y = K M, Z
+  //   seg 1    inverses, P and -A of chunk c          Y = K M, Z, (Q M)^T
   //   seg 2    K, Q, V, gates of chunk c + 1          U, O
   //   seg 3    Gram products of chunk c + 1           state update
   if (producer) {
@@ -687,13 +771,13 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
   }
 
   if (!producer && p.hT) {
+    float* hT = p.hT + sbase;
 #pragma unroll
     for (int a = 0; a < KT; ++a)
 #pragma unroll
       for (int j = 0; j < NTW; ++j)
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          p.hT[sbase + static_cast<size_t>(16 * a + 4 * lg + s) * DV + wcol + 16 * j + lr] = Ms[a][j][s];
+        for (int s = 0; s < 4; ++s) hT[slane + (16 * a + s) * DV + 16 * j] = Ms[a][j][s];
   }
 }
 
