@@ -47,9 +47,7 @@ namespace gdn {
 namespace {
 
 constexpr int C = 64;                    // chunk length
-constexpr int NP = 4;                    // producer wavefronts
-constexpr int NCW = 4;                   // consumer wavefronts
-constexpr int NTHREADS = 64 * (NP + NCW);
+constexpr int NP = 4;                    // producer wavefronts (consumer wavefronts: a template parameter)
 constexpr int PTHREADS = 64 * NP;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -110,12 +108,6 @@ template <> struct Mma16<float> {
   __device__ __forceinline__ static frag chain(const floatx4& t) { return t; }
 };
 
-// LDS operand of 16-block m (k = 16m + 4lg .. +3) from a row stored in phys_k order.
-template <class T>
-__device__ __forceinline__ typename Mma16<T>::frag lds_frag16(const T* row, int m, int lane) {
-  return *reinterpret_cast<const typename Mma16<T>::frag*>(row + Mma<T>::phys_k(16 * m + 4 * (lane >> 4)));
-}
-
 // Four consecutive rows of one column of a row-major LDS tile, as lane data
 // for the accumulator layout: lane (lg, lr) gets X[r0 + 4lg + e][c0 + lr],
 // e = 0..3 (c0 a multiple of 16; PERM: the column axis is stored in phys_k
@@ -159,16 +151,33 @@ template <int W>
 __device__ __forceinline__ int swz_off(int r, int c) {  // element offset of column c of row r
   return r * W + ((((c >> 4) ^ swz<W>(r)) << 4) | (c & 15));
 }
-// lds_col4<bf16, false> for a swizzled tile of width W.
-template <int W>
-__device__ __forceinline__ bf16x4 swz_col4(const bf16* base, int r0, int c0, int lane) {
+// Transposing 8-byte LDS read (see lds_col4).
+__device__ __forceinline__ bf16x4 tr_read(const bf16* ptr) {
   typedef short s4 __attribute__((ext_vector_type(4)));
-  const int lg = lane >> 4, lr = lane & 15;
-  const bf16* ptr = base + swz_off<W>(r0 + 4 * lg + (lr >> 2), c0 + 4 * (lr & 3));
   const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       reinterpret_cast<__attribute__((address_space(3))) s4*>(reinterpret_cast<size_t>(ptr)));
   return __builtin_bit_cast(bf16x4, v);
 }
+// lds_col4<bf16, false> for a swizzled tile of width W.
+template <int W>
+__device__ __forceinline__ bf16x4 swz_col4(const bf16* base, int r0, int c0, int lane) {
+  const int lg = lane >> 4, lr = lane & 15;
+  return tr_read(base + swz_off<W>(r0 + 4 * lg + (lr >> 2), c0 + 4 * (lr & 3)));
+}
+// The same reads split into a per-lane part and a per-block part: for row
+// offsets r0 that are multiples of 16 the swizzle depends on the lane only, so
+// column block b of rows r0.. is read at lane_base + r0 * W + block_off(b).
+template <int W>
+struct SwzCols {
+  const bf16* lane_base;
+  int x;
+  __device__ __forceinline__ SwzCols(const bf16* base, int lane) {
+    const int rl = 4 * (lane >> 4) + ((lane & 15) >> 2);
+    x = swz<W>(rl);
+    lane_base = base + rl * W + 4 * (lane & 3);
+  }
+  __device__ __forceinline__ const bf16* block(int b) const { return lane_base + ((b ^ x) << 4); }
+};
 
 // Operand fragment of k-group kg built from accumulator tiles tile(kg*TPG + t).
 template <class T, class F>
@@ -180,19 +189,18 @@ __device__ __forceinline__ typename Mma<T>::frag chain_frag(F tile, int kg) {
   }
 }
 
-// LDS layout.  Rows are padded by 16 bytes against bank conflicts.
-template <class T, int DK, int BV, int NSTAGE>
+// LDS layout.  K and Q rows are padded by 16 bytes against bank conflicts.
+template <class T, int DK, int BV, int NSTAGE, int NCW>
 struct Layout {
   static constexpr int EPB = 16 / sizeof(T);
   static constexpr int NTW = BV / (16 * NCW);   // 16-column state tiles per consumer wave
   static constexpr int LDK = DK + EPB;          // [C][DK] rows: K, Q (key axis in phys_k order)
-  static constexpr int LDC = C + EPB;           // [*][C] rows: P, -A
   static constexpr int LDV = BV;                // [C][BV] rows: V (only read down its columns; bf16 swizzled)
   // bf16 keeps a second copy of K with the key axis in natural order
   // (swizzled): the transposing reads of K^T then load whole 32-byte runs, at
   // half the cost of reading them out of the phys_k copy.
   static constexpr bool KNAT = sizeof(T) == 2;
-  static constexpr int LDT = 20;                // [16][16] diagonal-block inverses
+  static constexpr int KGC = C / Mma<T>::KG;    // k-groups over the chunk
   static constexpr int LDA = 20;                // fp32 diagonal blocks of A
   // one stage, double-buffered: written by the producers in segment 1
   static constexpr size_t sK = 0;
@@ -201,18 +209,42 @@ struct Layout {
   static constexpr size_t sKn = sV + sizeof(T) * C * LDV;   // [C][DK] K, natural key order (bf16)
   static constexpr size_t sVec = sKn + (KNAT ? sizeof(T) * C * DK : 0);  // exp G, beta, exp(G_C - G), exp G_C
   static constexpr size_t stage_bytes = (sVec + 4 * 4 * C + 15) / 16 * 16;
-  // single-buffered: written by the producers in segment 3, after the
-  // consumers have read the previous chunk's copy in segment 2
-  static constexpr size_t oP = NSTAGE * stage_bytes;
-  static constexpr size_t oAn = oP + sizeof(T) * C * LDC;
-  static constexpr size_t oTbb = oAn + sizeof(T) * C * LDC;
+  // Single-buffered, written by the producers in segment 1 after the
+  // consumers have read the previous chunk's copy in segment 2.  All three
+  // are kept in "fragment order": the 16 (or 8) bytes one lane contributes to
+  // a matrix-core operand are stored contiguously, lane after lane, so both
+  // the producers' writes and the consumers' reads are conflict-free.
+  //   P:   per (token tile ct, k-group kg), the B operand P^T of O^T += U^T P^T
+  //   -A:  the A operands of the block substitution: (1,0); (2,0)+(2,1); (3,0)+(3,1); (3,2)
+  //   T_bb: the A operands (I + A_bb)^-1 of the four diagonal blocks
+  static constexpr size_t oPf = NSTAGE * stage_bytes;
+  static constexpr size_t oAnf = oPf + size_t(4) * KGC * 64 * 16;
+  static constexpr size_t oTbf = oAnf + size_t(6) * 64 * 4 * sizeof(T);
   // producer scratch
-  static constexpr size_t oAd = oTbb + sizeof(T) * 4 * 16 * LDT;
+  static constexpr size_t oAd = oTbf + size_t(4) * 64 * 4 * sizeof(T);
   static constexpr size_t oGl = oAd + 4 * 4 * 16 * LDA;
   static constexpr size_t bytes = oGl + 4 * C;
   static_assert(BV % (16 * NCW) == 0, "every consumer wave owns whole 16-column tiles");
-  static_assert(sQ % 16 == 0 && sV % 16 == 0 && sKn % 16 == 0 && sVec % 16 == 0 && oP % 16 == 0 &&
-                oAn % 16 == 0 && oTbb % 16 == 0 && oAd % 16 == 0, "16-byte aligned LDS regions");
+  static_assert(sQ % 16 == 0 && sV % 16 == 0 && sKn % 16 == 0 && sVec % 16 == 0 && oPf % 16 == 0 &&
+                oAnf % 16 == 0 && oTbf % 16 == 0 && oAd % 16 == 0, "16-byte aligned LDS regions");
+  // element offsets into the fragment-order buffers
+  // P: tile (ti, tj) of the lane's piece (4 elements) inside fragment (ti, tj / TPG)
+  __device__ __forceinline__ static int pf(int ti, int tj, int lane) {
+    constexpr int TPG = Mma<T>::TPG, FE = 16 / sizeof(T);
+    return ((ti * KGC + tj / TPG) * 64 + lane) * FE + (tj % TPG) * 4;
+  }
+  // -A: bf16 pairs the tiles (b,0) and (b,1) of b = 2, 3 into one 32-wide fragment
+  __device__ __forceinline__ static int anf(int ti, int tj, int lane) {
+    if constexpr (Mma<T>::TPG == 2) {
+      if (ti == 1) return lane * 4;                              // (1,0)
+      if (tj < 2) return 256 + (ti - 2) * 512 + lane * 8 + tj * 4;  // (2,0) (2,1) (3,0) (3,1)
+      return 1280 + lane * 4;                                    // (3,2)
+    } else {
+      const int k = ti == 1 ? 0 : (ti == 2 ? 1 + tj : 3 + tj);   // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+      return (k * 64 + lane) * 4;
+    }
+  }
+  __device__ __forceinline__ static int tbf(int b, int lane) { return (b * 64 + lane) * 4; }
 };
 
 struct Params {
@@ -308,14 +340,14 @@ template <> struct GramTiles<1> { static constexpr int n = 3, ti[3] = {2, 2, 2},
 template <> struct GramTiles<2> { static constexpr int n = 2, ti[3] = {1, 1, 0}, tj[3] = {0, 1, 0}; };
 template <> struct GramTiles<3> { static constexpr int n = 2, ti[3] = {0, 3, 0}, tj[3] = {0, 3, 0}; };
 
-template <class T, int DK, int DV, int BV, int NSTAGE>
-__global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
-  using L = Layout<T, DK, BV, NSTAGE>;
+template <class T, int DK, int DV, int BV, int NSTAGE, int NCW>
+__global__ __launch_bounds__(64 * (NP + NCW)) void prefill_kernel(Params p) {
+  using L = Layout<T, DK, BV, NSTAGE, NCW>;
   using MM = Mma<T>;
   using M16 = Mma16<T>;
   using frag = typename MM::frag;
   using V4 = typename Vec4<T>::type;
-  constexpr int NTW = L::NTW, LDK = L::LDK, LDC = L::LDC, LDV = L::LDV, LDT = L::LDT, LDA = L::LDA;
+  constexpr int NTW = L::NTW, LDK = L::LDK, LDV = L::LDV, LDA = L::LDA;
   constexpr int KT = DK / 16;       // key-dim tiles of the state
   constexpr int KGK = DK / MM::KG;  // k-groups over the key dim
   constexpr int KGC = C / MM::KG;   // k-groups over the chunk
@@ -459,15 +491,14 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
   // the four diagonal blocks of I + A.
   auto put = [&](auto wtag) __attribute__((always_inline)) {
     using GT = GramTiles<decltype(wtag)::value>;
-    T* sP = reinterpret_cast<T*>(smem + L::oP);
-    T* sAn = reinterpret_cast<T*>(smem + L::oAn);
+    T* sPf = reinterpret_cast<T*>(smem + L::oPf);
+    T* sAnf = reinterpret_cast<T*>(smem + L::oAnf);
 #pragma unroll
     for (int t = 0; t < GT::n; ++t) {
-      const int i = 16 * GT::ti[t] + lr;
-      *reinterpret_cast<V4*>(sP + i * LDC + MM::phys_k(16 * GT::tj[t] + 4 * lg)) =
+      *reinterpret_cast<V4*>(sPf + L::pf(GT::ti[t], GT::tj[t], lane)) =
           pack4<T>(pkeep[t][0], pkeep[t][1], pkeep[t][2], pkeep[t][3]);
       if (GT::ti[t] != GT::tj[t])
-        *reinterpret_cast<V4*>(sAn + i * LDC + MM::phys_k(16 * GT::tj[t] + 4 * lg)) =
+        *reinterpret_cast<V4*>(sAnf + L::anf(GT::ti[t], GT::tj[t], lane)) =
             pack4<T>(-akeep[t][0], -akeep[t][1], -akeep[t][2], -akeep[t][3]);
     }
   };
@@ -478,16 +509,6 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
       case 2: put(std::integral_constant<int, 2>()); break;
       default: put(std::integral_constant<int, 3>()); break;
     }
-    if (wave >= 2) {  // the six tiles of P above the diagonal are zero
-      T* sP = reinterpret_cast<T*>(smem + L::oP);
-#pragma unroll
-      for (int t = 0; t < 3; ++t) {
-        const int zi = (wave == 2) ? 0 : (t == 2 ? 2 : 1);
-        const int zj = (wave == 2) ? t + 1 : (t == 2 ? 3 : t + 2);
-        *reinterpret_cast<V4*>(sP + (16 * zi + lr) * LDC + MM::phys_k(16 * zj + 4 * lg)) =
-            pack4<T>(0.f, 0.f, 0.f, 0.f);
-      }
-    }
     {  // producer wave w inverts diagonal block w of I + A
       const int cc = lane >> 2, q = lane & 3;
       const float* At = sAd + wave * 16 * LDA;  // At[j][i] = A_ij of the block
@@ -495,9 +516,10 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) x[t] = (4 * q + t == cc) ? 1.f : 0.f;
       unit_lower_inverse_column(x, At, LDA, q, std::make_integer_sequence<int, 15>());
-      T* Tb = reinterpret_cast<T*>(smem + L::oTbb) + wave * 16 * LDT;
+      // T[4q + t][cc] belongs to operand lane 16 (cc / 4) + 4q + t, element cc % 4
+      T* Tb = reinterpret_cast<T*>(smem + L::oTbf);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) Tb[(4 * q + t) * LDT + cc] = from_float<T>(x[t]);
+      for (int t = 0; t < 4; ++t) Tb[L::tbf(wave, 16 * (cc >> 2) + 4 * q + t) + (cc & 3)] = from_float<T>(x[t]);
     }
   };
 
@@ -597,30 +619,29 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
         for (int j = 0; j < NTW; ++j) mfr[kgi][j] = chain_frag<T>([&](int t) { return Ms[t][j]; }, kgi);
       q_times_state(reinterpret_cast<const T*>(stage(s) + L::sQ), reinterpret_cast<const float*>(stage(s) + L::sVec));
     }
-    const T* sAn = reinterpret_cast<const T*>(smem + L::oAn);
-    const T* sTbb = reinterpret_cast<const T*>(smem + L::oTbb);
-    const T* sP = reinterpret_cast<const T*>(smem + L::oP);
+    const T* sAnf = reinterpret_cast<const T*>(smem + L::oAnf);
+    const T* sTbf = reinterpret_cast<const T*>(smem + L::oTbf);
+    const T* sPf = reinterpret_cast<const T*>(smem + L::oPf);
     const int cs = bos + c * C, Lc = min(C, eos - cs);
+    using F16 = typename M16::frag;
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
       // U_b = T_bb (Z_b + sum_{m<b} (-A_bm) U_m), b = 0..3
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         floatx4 w = Z[b][j];
-        const T* arow = sAn + (16 * b + lr) * LDC;
         if (b >= 2) {  // blocks 0 and 1 together: one 32-wide contraction
           if constexpr (MM::KG == 32) {
-            MM::mma(w, lds_frag(arow, 0, lane), MM::chain(Z[0][j], Z[1][j]));
+            MM::mma(w, *reinterpret_cast<const frag*>(sAnf + L::anf(b, 0, lane)), MM::chain(Z[0][j], Z[1][j]));
           } else {
-            MM::mma(w, lds_frag(arow, 0, lane), Mma<float>::chain(Z[0][j]));
-            MM::mma(w, lds_frag(arow, 1, lane), Mma<float>::chain(Z[1][j]));
+            MM::mma(w, *reinterpret_cast<const frag*>(sAnf + L::anf(b, 0, lane)), Mma<float>::chain(Z[0][j]));
+            MM::mma(w, *reinterpret_cast<const frag*>(sAnf + L::anf(b, 1, lane)), Mma<float>::chain(Z[1][j]));
           }
         }
-        if (b == 1) M16::mma(w, lds_frag16(arow, 0, lane), M16::chain(Z[0][j]));
-        if (b == 3) M16::mma(w, lds_frag16(arow, 2, lane), M16::chain(Z[2][j]));
+        if (b == 1) M16::mma(w, *reinterpret_cast<const F16*>(sAnf + L::anf(1, 0, lane)), M16::chain(Z[0][j]));
+        if (b == 3) M16::mma(w, *reinterpret_cast<const F16*>(sAnf + L::anf(3, 2, lane)), M16::chain(Z[2][j]));
         floatx4 u = zero4();
-        M16::mma(u, *reinterpret_cast<const typename M16::frag*>(sTbb + (b * 16 + lr) * LDT + 4 * lg),
-                 M16::chain(w));
+        M16::mma(u, *reinterpret_cast<const F16*>(sTbf + L::tbf(b, lane)), M16::chain(w));
         Z[b][j] = u;  // Z_b is not needed any more
       }
     }
@@ -633,7 +654,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         if (kgi * MM::KG <= 16 * ct + 15) {  // P is zero above the diagonal
-          const frag pf = lds_frag(sP + (16 * ct + lr) * LDC, kgi, lane);
+          const frag pf = *reinterpret_cast<const frag*>(sPf + L::pf(ct, kgi * MM::TPG, lane));
 #pragma unroll
           for (int j = 0; j < NTW; ++j) MM::mma(Ot[ct][j], uf[j], pf);
         }
@@ -656,11 +677,12 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
   // seg 3: M <- exp(G_C) M + K^T (diag(exp(G_C - G)) U).
   // The swizzled tiles' read addresses depend on the lane in a way the
   // compiler would precompute for every column block and keep live across the
-  // loop; an opaque copy of the lane index, renewed each chunk, makes it form
-  // them where they are used instead.
+  // loop; the lane index formed afresh each chunk by an opaque (volatile) pair
+  // of mbcnt instructions makes it form them where they are used instead, and
+  // leaves nothing lane-derived to hold across the loop.
   auto opaque_lane = [&]() __attribute__((always_inline)) {
-    int v = lane;
-    asm volatile("" : "+v"(v));
+    int v;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
     return v;
   };
   auto cons_seg3 = [&](int s) __attribute__((always_inline)) {
@@ -682,6 +704,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
     for (int a = 0; a < KT; ++a)
 #pragma unroll
       for (int j = 0; j < NTW; ++j) Ms[a][j] *= eGC;
+    const SwzCols<DK> kcols(reinterpret_cast<const bf16*>(sKn), olane);  // bf16 only (unused for fp32)
 #pragma unroll
     for (int kgi = 0; kgi < KGC; ++kgi) {
       frag bu[NTW];
@@ -691,8 +714,8 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
       for (int a = 0; a < KT; ++a) {
         frag af;  // K^T rows 16a.., tokens of k-group kgi, from the row-major K tile
         if constexpr (MM::KG == 32) {
-          af = __builtin_shufflevector(swz_col4<DK>(sKn, 32 * kgi, 16 * a, olane),
-                                       swz_col4<DK>(sKn, 32 * kgi + 16, 16 * a, olane), 0, 1, 2, 3, 4, 5, 6, 7);
+          const bf16* pa = kcols.block(a) + 32 * kgi * DK;
+          af = __builtin_shufflevector(tr_read(pa), tr_read(pa + 16 * DK), 0, 1, 2, 3, 4, 5, 6, 7);
         } else {
           af = lds_col4<T, true>(sK, LDK, 16 * kgi, 16 * a, lane);
         }
@@ -711,6 +734,10 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
   //   seg 2    K, Q, V, gates of chunk c + 1          U, O
   //   seg 3    Gram products of chunk c + 1           state update
   if (producer) {
+    if constexpr (MM::TPG == 2) {  // P tiles (0,1) and (2,3) share fragments with written tiles and are zero
+      T* sPf = reinterpret_cast<T*>(smem + L::oPf);
+      if (wave < 2) *reinterpret_cast<V4*>(sPf + L::pf(2 * wave, 2 * wave + 1, lane)) = pack4<T>(0.f, 0.f, 0.f, 0.f);
+    }
     if (nch > 0) issue_loads(0);
     if constexpr (NSTAGE == 2) {
       if (nch > 0) {
@@ -781,9 +808,9 @@ __global__ __launch_bounds__(NTHREADS) void prefill_kernel(Params p) {
   }
 }
 
-template <class T, int DK, int DV, int BV, int NSTAGE>
+template <class T, int DK, int DV, int BV, int NSTAGE, int NCW>
 hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
-  using L = Layout<T, DK, BV, NSTAGE>;
+  using L = Layout<T, DK, BV, NSTAGE, NCW>;
   static_assert(L::bytes <= 160 * 1024, "LDS budget of one gfx950 compute unit");
   Params p;
   p.q = a.q;
@@ -804,33 +831,43 @@ hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   if (p.nunits == 0) return hipSuccess;
   const int units_pad = (p.nunits + 7) / 8 * 8;
   const dim3 grid(units_pad * p.nslices);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<T, DK, DV, BV, NSTAGE>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<T, DK, DV, BV, NSTAGE, NCW>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(L::bytes));
   if (e != hipSuccess) return e;
-  prefill_kernel<T, DK, DV, BV, NSTAGE><<<grid, dim3(NTHREADS), L::bytes, stream>>>(p);
+  prefill_kernel<T, DK, DV, BV, NSTAGE, NCW><<<grid, dim3(64 * (NP + NCW)), L::bytes, stream>>>(p);
   return hipGetLastError();
 }
 
-// dv-slice width: whole state rows per workgroup when there are enough
-// (sequence, head) units to fill the 256 compute units, half rows (twice the
-// workgroups, each redoing the chunk-local work) when there are not.
-int choose_bv(int units, int dv) {
-  if (dv == 64) return 64;
-  return units >= 256 ? 128 : 64;
+// dv-slice width and consumer wavefronts.  Every (sequence, head) unit walks
+// its chunks in order, so the time is the chunk count times the time per
+// chunk of one workgroup.  With enough units to fill the 256 compute units,
+// whole 128-column state rows per workgroup (four consumer wavefronts of two
+// 16-column tiles each); with fewer, narrower slices: more workgroups, each
+// redoing the chunk-local work but with fewer consumer wavefronts sharing its
+// compute unit, which shortens the time per chunk.
+int slice_config(int units, int dv) {
+  if (dv == 64) return units >= 128 ? 64 : 32;
+  if (units >= 256) return 128;
+  return units >= 128 ? 64 : 32;
 }
-
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (a.chunk != C) return hipErrorInvalidValue;
   const int units = a.num_seqs * a.Hv;
   if (a.bf16) {
-    if (a.dk == 128 && a.dv == 128)
-      return choose_bv(units, 128) == 128 ? launch<bf16, 128, 128, 128, 2>(a, stream)
-                                          : launch<bf16, 128, 128, 64, 2>(a, stream);
-    if (a.dk == 64 && a.dv == 64) return launch<bf16, 64, 64, 64, 2>(a, stream);
+    if (a.dk == 128 && a.dv == 128) {
+      switch (slice_config(units, 128)) {
+        case 128: return launch<bf16, 128, 128, 128, 2, 4>(a, stream);
+        case 64: return launch<bf16, 128, 128, 64, 2, 4>(a, stream);
+        default: return launch<bf16, 128, 128, 32, 2, 2>(a, stream);
+      }
+    }
+    if (a.dk == 64 && a.dv == 64)
+      return slice_config(units, 64) == 64 ? launch<bf16, 64, 64, 64, 2, 4>(a, stream)
+                                           : launch<bf16, 64, 64, 32, 2, 2>(a, stream);
   } else {
-    if (a.dk == 64 && a.dv == 64) return launch<float, 64, 64, 64, 1>(a, stream);
+    if (a.dk == 64 && a.dv == 64) return launch<float, 64, 64, 64, 1, 4>(a, stream);
   }
   return hipErrorInvalidValue;
 }
