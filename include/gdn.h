@@ -59,7 +59,7 @@ typedef struct {
   int32_t seqlen;       /* T: tokens per row (total packed tokens with cu_seqlens); >= 0  */
   int32_t num_seqs;     /* N: number of sequences = B, or len(cu_seqlens) - 1             */
   int32_t num_qk_heads; /* Hqk >= 1                                                       */
-  int32_t num_v_heads;  /* Hv >= 1, a multiple of Hqk                                     */
+  int32_t num_v_heads;  /* Hv >= 1, a multiple of Hqk; NOT_SUPPORTED above 4096          */
   int32_t head_dim_k;   /* dk: 64 or 128                                                  */
   int32_t head_dim_v;   /* dv: 64 or 128 (prefill: dv == dk)                              */
   int32_t chunk_size;   /* prefill chunk length C; 64 is the one built                    */

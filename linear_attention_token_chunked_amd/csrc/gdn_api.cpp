@@ -21,6 +21,8 @@ gdn_status_t check_common(const gdn_dims_t* d) {
   if (d->num_v_heads % d->num_qk_heads != 0) return GDN_STATUS_INVALID_VALUE;
   if (d->dtype != GDN_DTYPE_FLOAT32 && d->dtype != GDN_DTYPE_BFLOAT16) return GDN_STATUS_INVALID_VALUE;
   if (!head_dim_ok(d->head_dim_k) || !head_dim_ok(d->head_dim_v)) return GDN_STATUS_NOT_SUPPORTED;
+  // The kernels address one token row of q, k, v with 32-bit byte offsets.
+  if (d->num_v_heads > 4096) return GDN_STATUS_NOT_SUPPORTED;
   return GDN_STATUS_SUCCESS;
 }
 

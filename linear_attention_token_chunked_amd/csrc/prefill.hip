@@ -277,25 +277,35 @@ struct ChunkRegs {
   // and harmless because their gates are masked to g = 0, beta = 0, which
   // zeroes their rows of A, Z and U exactly.  Consecutive lanes read
   // consecutive 16-byte pieces of a row.
-  __device__ __forceinline__ void load(const T* kb, const T* qb, const T* vb, size_t qk_tok, size_t v_tok,
-                                       const float* gb, const float* bb, size_t g_tok, int Lc, int tid) {
+  // Offsets inside a chunk are 32-bit byte counts (a token row of q, k or v
+  // is at most 4096 heads x 128 x 4 bytes, checked on the host), so the
+  // loads take a uniform 64-bit base plus one 24-bit multiply per row.
+  __device__ __forceinline__ void load(const T* kb, const T* qb, const T* vb, uint32_t qk_row, uint32_t v_row,
+                                       const float* gb, const float* bb, uint32_t g_row, int Lc, int tid) {
+    const char* kc = reinterpret_cast<const char*>(kb);
+    const char* qc = reinterpret_cast<const char*>(qb);
+    const char* vc = reinterpret_cast<const char*>(vb);
 #pragma unroll
     for (int it = 0; it < KIT; ++it) {
       const int t = tid + it * PTHREADS;
-      const size_t off = min(t / KPR, Lc - 1) * qk_tok + (t % KPR) * EPB;
-      k[it] = *reinterpret_cast<const frag*>(kb + off);
-      q[it] = *reinterpret_cast<const frag*>(qb + off);
+      const uint32_t off = __umul24(min(t / KPR, Lc - 1), qk_row) + (t % KPR) * 16;
+      k[it] = *reinterpret_cast<const frag*>(kc + off);
+      q[it] = *reinterpret_cast<const frag*>(qc + off);
     }
 #pragma unroll
     for (int it = 0; it < VIT; ++it) {
       const int t = min(tid + it * PTHREADS, C * VPR - 1);
-      v[it] = *reinterpret_cast<const frag*>(vb + min(t / VPR, Lc - 1) * v_tok + (t % VPR) * EPB);
+      v[it] = *reinterpret_cast<const frag*>(vc + __umul24(min(t / VPR, Lc - 1), v_row) + (t % VPR) * 16);
     }
     if (tid < 64) {  // wave 0 owns the gates, one token per lane
-      g = gb[min(tid, Lc - 1) * g_tok];
-      b = bb[min(tid, Lc - 1) * g_tok];
+      const uint32_t off = __umul24(min(tid, Lc - 1), g_row);
+      g = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(gb) + off);
+      b = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(bb) + off);
     }
   }
+
+
+
 
   // K, Q -> rows with the key axis in phys_k order; V and (if sKn) a second
   // copy of K -> rows in natural order.
@@ -402,10 +412,14 @@ __global__ __launch_bounds__(64 * (NP + NCW)) void prefill_kernel(Params p) {
     const size_t tq = static_cast<size_t>(cs) * qk_tok + static_cast<size_t>(hq) * DK;
     const size_t tv = static_cast<size_t>(cs) * v_tok + static_cast<size_t>(h) * DV + col0;
     const size_t tg = static_cast<size_t>(cs) * p.Hv + h;
-    pre.load(kgp + tq, qg + tq, vg + tv, qk_tok, v_tok, p.g + tg, p.beta + tg, p.Hv, min(C, eos - cs), tid);
+    pre.load(kgp + tq, qg + tq, vg + tv, static_cast<uint32_t>(qk_tok * sizeof(T)),
+             static_cast<uint32_t>(v_tok * sizeof(T)), p.g + tg, p.beta + tg, static_cast<uint32_t>(p.Hv * 4),
+             min(C, eos - cs), tid);
   };
 
-  // Stage the chunk's K, Q, V and gates; issue the next chunk's loads.
+  // Stage the chunk's K, Q, V and gates; issue the next chunk's loads.  (The
+  // loads sit in this segment because here the producers have slack: the
+  // consumers' segment 2 is the longer one.)
   auto prod_stores = [&](int c, int s) __attribute__((always_inline)) {
     unsigned char* S = stage(s);
     const int cs = bos + c * C, Lc = min(C, eos - cs);
@@ -731,7 +745,8 @@ __global__ __launch_bounds__(64 * (NP + NCW)) void prefill_kernel(Params p) {
   // a double-buffered stage, iteration c runs three segments:
   //            producers                              consumers (chunk c)
   //   seg 1    inverses, P and -A of chunk c          Y = K M, Z, (Q M)^T
-  //   seg 2    K, Q, V, gates of chunk c + 1          U, O
+  //   seg 2    K, Q, V, gates of chunk c + 1;         U, O
+  //            loads of chunk c + 2
   //   seg 3    Gram products of chunk c + 1           state update
   if (producer) {
     if constexpr (MM::TPG == 2) {  // P tiles (0,1) and (2,3) share fragments with written tiles and are zero

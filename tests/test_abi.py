@@ -91,6 +91,7 @@ def test_null_dims_rejected(gdn):
     (dict(dk=96, dv=96), NOT_SUPPORTED),   # head dims not built
     (dict(dk=128, dv=64), NOT_SUPPORTED),  # prefill needs dk == dv
     (dict(chunk_size=32), NOT_SUPPORTED),
+    (dict(Hqk=1, Hv=8192), NOT_SUPPORTED),  # token rows beyond the kernels' 32-bit offsets
     (dict(dtype=7), INVALID),
 ])
 def test_fwd_invalid_dims(gdn, kw, code):
