@@ -190,7 +190,7 @@ __device__ __forceinline__ typename Mma<T>::frag chain_frag(F tile, int kg) {
 }
 
 // LDS layout.  K and Q rows are padded by 16 bytes against bank conflicts.
-template <class T, int DK, int BV, int NSTAGE, int NCW>
+template <class T, int DK, int BV, int NSTAGE, int NCW, bool OUTW>
 struct Layout {
   static constexpr int EPB = 16 / sizeof(T);
   static constexpr int NTW = BV / (16 * NCW);   // 16-column state tiles per consumer wave
@@ -223,10 +223,17 @@ struct Layout {
   // producer scratch
   static constexpr size_t oAd = oTbf + size_t(4) * 64 * 4 * sizeof(T);
   static constexpr size_t oGl = oAd + 4 * 4 * 16 * LDA;
-  static constexpr size_t bytes = oGl + 4 * C;
+  // With output wavefronts: the state and U of each consumer wave as bf16
+  // matrix-core operands, fragment order (written in segments 1 and 2, read
+  // by the paired output wave in segments 2 and 3).
+  static constexpr size_t oMx = oGl + 4 * C;
+  static constexpr size_t oUx = oMx + (OUTW ? size_t(NCW) * (DK / Mma<T>::KG) * 64 * 16 : 0);
+  static constexpr size_t bytes = oUx + (OUTW ? size_t(NCW) * KGC * 64 * 16 : 0);
+  static_assert(!OUTW || NTW == 1, "output wavefronts pair with one-tile consumer waves");
   static_assert(BV % (16 * NCW) == 0, "every consumer wave owns whole 16-column tiles");
   static_assert(sQ % 16 == 0 && sV % 16 == 0 && sKn % 16 == 0 && sVec % 16 == 0 && oPf % 16 == 0 &&
-                oAnf % 16 == 0 && oTbf % 16 == 0 && oAd % 16 == 0, "16-byte aligned LDS regions");
+                oAnf % 16 == 0 && oTbf % 16 == 0 && oAd % 16 == 0 && oMx % 16 == 0 && oUx % 16 == 0,
+                "16-byte aligned LDS regions");
   // element offsets into the fragment-order buffers
   // P: tile (ti, tj) of the lane's piece (4 elements) inside fragment (ti, tj / TPG)
   __device__ __forceinline__ static int pf(int ti, int tj, int lane) {
@@ -350,9 +357,9 @@ template <> struct GramTiles<1> { static constexpr int n = 3, ti[3] = {2, 2, 2},
 template <> struct GramTiles<2> { static constexpr int n = 2, ti[3] = {1, 1, 0}, tj[3] = {0, 1, 0}; };
 template <> struct GramTiles<3> { static constexpr int n = 2, ti[3] = {0, 3, 0}, tj[3] = {0, 3, 0}; };
 
-template <class T, int DK, int DV, int BV, int NSTAGE, int NCW>
-__global__ __launch_bounds__(64 * (NP + NCW)) void prefill_kernel(Params p) {
-  using L = Layout<T, DK, BV, NSTAGE, NCW>;
+template <class T, int DK, int DV, int BV, int NSTAGE, int NCW, bool OUTW>
+__global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kernel(Params p) {
+  using L = Layout<T, DK, BV, NSTAGE, NCW, OUTW>;
   using MM = Mma<T>;
   using M16 = Mma16<T>;
   using frag = typename MM::frag;
@@ -370,6 +377,7 @@ __global__ __launch_bounds__(64 * (NP + NCW)) void prefill_kernel(Params p) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const bool producer = wave < NP;
+  const bool consumer = !producer && wave < NP + NCW;  // else (OUTW) an output wave
   const int lg = lane >> 4;
   const int lr = lane & 15;
 
@@ -393,8 +401,8 @@ __global__ __launch_bounds__(64 * (NP + NCW)) void prefill_kernel(Params p) {
   }
   const int nch = (eos - bos + C - 1) / C;
   const int col0 = slice * BV;
-  const int cw = wave - NP;                    // consumer index
-  const int wcol = col0 + cw * 16 * NTW;       // first state column of a consumer wave
+  const int cw = producer ? 0 : (wave - NP) % NCW;  // consumer index (an output wave: its consumer's)
+  const int wcol = col0 + cw * 16 * NTW;             // first state column of a consumer (or output) wave
 
   const T* qg = static_cast<const T*>(p.q);
   const T* kgp = static_cast<const T*>(p.k);
@@ -547,7 +555,7 @@ __global__ __launch_bounds__(64 * (NP + NCW)) void prefill_kernel(Params p) {
   // per-element addresses out of the registers)
   const size_t sbase = static_cast<size_t>(unit) * DK * DV;
   const int slane = 4 * lg * DV + wcol + lr;
-  if (!producer) {
+  if (consumer) {
     const float* h0 = p.h0 + sbase;
 #pragma unroll
     for (int a = 0; a < KT; ++a)
@@ -561,7 +569,21 @@ __global__ __launch_bounds__(64 * (NP + NCW)) void prefill_kernel(Params p) {
   // state part of the output, O^T = diag-scaled (Q M)^T, is formed here too,
   // next to K M which takes the same operands; with two, holding it until
   // seg 2 would exceed the register budget, and seg 2 forms it instead.
-  constexpr bool QM_EARLY = NTW == 1;
+  constexpr bool QM_EARLY = NTW == 1 && !OUTW;
+  frag* sMx = reinterpret_cast<frag*>(smem + L::oMx) + cw * KGK * 64;  // this column tile's exchange slots
+  frag* sUx = reinterpret_cast<frag*>(smem + L::oUx) + cw * KGC * 64;
+  // The state as matrix-core operands (bf16-rounded for bf16 inputs); with
+  // output waves also handed to the paired output wave.
+  auto state_operands = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int kgi = 0; kgi < KGK; ++kgi)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) mfr[kgi][j] = chain_frag<T>([&](int t) { return Ms[t][j]; }, kgi);
+    if constexpr (OUTW) {
+#pragma unroll
+      for (int kgi = 0; kgi < KGK; ++kgi) sMx[kgi * 64 + lane] = mfr[kgi][0];
+    }
+  };
   floatx4 Ot[4][NTW];  // O^T by 16-token tile: lane holds O[16ct + lr][wcol + 16j + 4lg + s]
   auto q_times_state = [&](const T* sQ, const float* vec) __attribute__((always_inline)) {
 #pragma unroll
@@ -589,10 +611,7 @@ __global__ __launch_bounds__(64 * (NP + NCW)) void prefill_kernel(Params p) {
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int j = 0; j < NTW; ++j) Z[r][j] = zero4();
-#pragma unroll
-    for (int kgi = 0; kgi < KGK; ++kgi)
-#pragma unroll
-      for (int j = 0; j < NTW; ++j) mfr[kgi][j] = chain_frag<T>([&](int t) { return Ms[t][j]; }, kgi);
+    if constexpr (!OUTW) state_operands();  // (with output waves they were formed after the last update)
 #pragma unroll
     for (int kgi = 0; kgi < KGK; ++kgi) {
 #pragma unroll
@@ -624,9 +643,44 @@ __global__ __launch_bounds__(64 * (NP + NCW)) void prefill_kernel(Params p) {
     }
   };
 
+  // O^T += U^T P^T over the chunk's token tiles, then O -> HBM (U from Z, or,
+  // in an output wave, from the exchange slots).
+  auto out_pu = [&](int c, const frag* uex = nullptr) __attribute__((always_inline)) {
+    const T* sPf = reinterpret_cast<const T*>(smem + L::oPf);
+    const int cs = bos + c * C, Lc = min(C, eos - cs);
+    // every P fragment read from LDS feeds all of the wave's n-tiles
+#pragma unroll
+    for (int kgi = 0; kgi < KGC; ++kgi) {
+      frag uf[NTW];
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+        uf[j] = uex ? uex[kgi * 64 + lane] : chain_frag<T>([&](int t) { return Z[t][j]; }, kgi);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        if (kgi * MM::KG <= 16 * ct + 15) {  // P is zero above the diagonal
+          const frag pf = *reinterpret_cast<const frag*>(sPf + L::pf(ct, kgi * MM::TPG, lane));
+#pragma unroll
+          for (int j = 0; j < NTW; ++j) MM::mma(Ot[ct][j], uf[j], pf);
+        }
+      }
+    }
+    T* orow = og + static_cast<size_t>(cs + lr) * v_tok + static_cast<size_t>(h) * DV + wcol + 4 * lg;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      if (16 * ct + lr < Lc) {
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+          const floatx4 ov = Ot[ct][j] * p.scale;
+          *reinterpret_cast<V4*>(orow + static_cast<size_t>(16 * ct) * v_tok + 16 * j) =
+              pack4<T>(ov[0], ov[1], ov[2], ov[3]);
+        }
+      }
+    }
+  };
+
   // seg 2: U by block forward substitution; O^T += U^T P^T; O -> HBM.
   auto cons_seg2 = [&](int c, int s) __attribute__((always_inline)) {
-    if constexpr (!QM_EARLY) {  // the state operands are formed again rather than held over the barrier
+    if constexpr (!QM_EARLY && !OUTW) {  // the state operands are formed again rather than held over the barrier
 #pragma unroll
       for (int kgi = 0; kgi < KGK; ++kgi)
 #pragma unroll
@@ -635,8 +689,6 @@ __global__ __launch_bounds__(64 * (NP + NCW)) void prefill_kernel(Params p) {
     }
     const T* sAnf = reinterpret_cast<const T*>(smem + L::oAnf);
     const T* sTbf = reinterpret_cast<const T*>(smem + L::oTbf);
-    const T* sPf = reinterpret_cast<const T*>(smem + L::oPf);
-    const int cs = bos + c * C, Lc = min(C, eos - cs);
     using F16 = typename M16::frag;
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
@@ -659,32 +711,11 @@ __global__ __launch_bounds__(64 * (NP + NCW)) void prefill_kernel(Params p) {
         Z[b][j] = u;  // Z_b is not needed any more
       }
     }
-    // every P fragment read from LDS feeds all of the wave's n-tiles
+    if constexpr (OUTW) {  // U as operands for the output wave
 #pragma unroll
-    for (int kgi = 0; kgi < KGC; ++kgi) {
-      frag uf[NTW];
-#pragma unroll
-      for (int j = 0; j < NTW; ++j) uf[j] = chain_frag<T>([&](int t) { return Z[t][j]; }, kgi);
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        if (kgi * MM::KG <= 16 * ct + 15) {  // P is zero above the diagonal
-          const frag pf = *reinterpret_cast<const frag*>(sPf + L::pf(ct, kgi * MM::TPG, lane));
-#pragma unroll
-          for (int j = 0; j < NTW; ++j) MM::mma(Ot[ct][j], uf[j], pf);
-        }
-      }
-    }
-    T* orow = og + static_cast<size_t>(cs + lr) * v_tok + static_cast<size_t>(h) * DV + wcol + 4 * lg;
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      if (16 * ct + lr < Lc) {
-#pragma unroll
-        for (int j = 0; j < NTW; ++j) {
-          const floatx4 ov = Ot[ct][j] * p.scale;
-          *reinterpret_cast<V4*>(orow + static_cast<size_t>(16 * ct) * v_tok + 16 * j) =
-              pack4<T>(ov[0], ov[1], ov[2], ov[3]);
-        }
-      }
+      for (int kgi = 0; kgi < KGC; ++kgi) sUx[kgi * 64 + lane] = chain_frag<T>([&](int t) { return Z[t][0]; }, kgi);
+    } else {
+      out_pu(c);
     }
   };
 
@@ -737,6 +768,15 @@ __global__ __launch_bounds__(64 * (NP + NCW)) void prefill_kernel(Params p) {
         for (int j = 0; j < NTW; ++j) MM::mma(Ms[a][j], af, bu[j]);
       }
     }
+    if constexpr (OUTW) state_operands();  // the next chunk's state operands, for both waves
+  };
+
+  // Output wavefronts: the state part of O^T in segment 1 and U^T P^T with the
+  // store in segment 3, from the operands their consumer wave leaves in LDS.
+  auto outw_qm = [&](int s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kgi = 0; kgi < KGK; ++kgi) mfr[kgi][0] = sMx[kgi * 64 + lane];
+    q_times_state(reinterpret_cast<const T*>(stage(s) + L::sQ), reinterpret_cast<const float*>(stage(s) + L::sVec));
   };
 
   // ------------------------------------------------------------ schedule
@@ -748,6 +788,10 @@ __global__ __launch_bounds__(64 * (NP + NCW)) void prefill_kernel(Params p) {
   //   seg 2    K, Q, V, gates of chunk c + 1;         U, O
   //            loads of chunk c + 2
   //   seg 3    Gram products of chunk c + 1           state update
+  // With output wavefronts the consumers hand the state (after the update in
+  // segment 3, for the next chunk) and U (segment 2) to them as bf16 operands,
+  // and they form O^T: the state part in segment 1, U^T P^T and the store in
+  // segment 3.
   if (producer) {
     if constexpr (MM::TPG == 2) {  // P tiles (0,1) and (2,3) share fragments with written tiles and are zero
       T* sPf = reinterpret_cast<T*>(smem + L::oPf);
@@ -783,9 +827,24 @@ __global__ __launch_bounds__(64 * (NP + NCW)) void prefill_kernel(Params p) {
         lds_barrier();
       }
     }
+  } else if (!consumer) {
+    if constexpr (OUTW) {
+      if (nch > 0) {
+        lds_barrier();
+        lds_barrier();
+      }
+      for (int c = 0; c < nch; ++c) {
+        outw_qm(c & 1);
+        lds_barrier();
+        lds_barrier();
+        out_pu(c, sUx);
+        lds_barrier();
+      }
+    }
   } else {
     if constexpr (NSTAGE == 2) {
       if (nch > 0) {
+        if constexpr (OUTW) state_operands();
         lds_barrier();
         lds_barrier();
       }
@@ -812,7 +871,7 @@ __global__ __launch_bounds__(64 * (NP + NCW)) void prefill_kernel(Params p) {
     }
   }
 
-  if (!producer && p.hT) {
+  if (consumer && p.hT) {
     float* hT = p.hT + sbase;
 #pragma unroll
     for (int a = 0; a < KT; ++a)
@@ -823,9 +882,9 @@ __global__ __launch_bounds__(64 * (NP + NCW)) void prefill_kernel(Params p) {
   }
 }
 
-template <class T, int DK, int DV, int BV, int NSTAGE, int NCW>
+template <class T, int DK, int DV, int BV, int NSTAGE, int NCW, bool OUTW>
 hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
-  using L = Layout<T, DK, BV, NSTAGE, NCW>;
+  using L = Layout<T, DK, BV, NSTAGE, NCW, OUTW>;
   static_assert(L::bytes <= 160 * 1024, "LDS budget of one gfx950 compute unit");
   Params p;
   p.q = a.q;
@@ -846,10 +905,10 @@ hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   if (p.nunits == 0) return hipSuccess;
   const int units_pad = (p.nunits + 7) / 8 * 8;
   const dim3 grid(units_pad * p.nslices);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<T, DK, DV, BV, NSTAGE, NCW>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<T, DK, DV, BV, NSTAGE, NCW, OUTW>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(L::bytes));
   if (e != hipSuccess) return e;
-  prefill_kernel<T, DK, DV, BV, NSTAGE, NCW><<<grid, dim3(64 * (NP + NCW)), L::bytes, stream>>>(p);
+  prefill_kernel<T, DK, DV, BV, NSTAGE, NCW, OUTW><<<grid, dim3(64 * (NP + NCW * (OUTW ? 2 : 1))), L::bytes, stream>>>(p);
   return hipGetLastError();
 }
 
@@ -873,16 +932,16 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (a.bf16) {
     if (a.dk == 128 && a.dv == 128) {
       switch (slice_config(units, 128)) {
-        case 128: return launch<bf16, 128, 128, 128, 2, 4>(a, stream);
-        case 64: return launch<bf16, 128, 128, 64, 2, 4>(a, stream);
-        default: return launch<bf16, 128, 128, 32, 2, 2>(a, stream);
+        case 128: return launch<bf16, 128, 128, 128, 2, 4, false>(a, stream);
+        case 64: return launch<bf16, 128, 128, 64, 2, 4, false>(a, stream);
+        default: return launch<bf16, 128, 128, 32, 2, 2, true>(a, stream);
       }
     }
     if (a.dk == 64 && a.dv == 64)
-      return slice_config(units, 64) == 64 ? launch<bf16, 64, 64, 64, 2, 4>(a, stream)
-                                           : launch<bf16, 64, 64, 32, 2, 2>(a, stream);
+      return slice_config(units, 64) == 64 ? launch<bf16, 64, 64, 64, 2, 4, false>(a, stream)
+                                           : launch<bf16, 64, 64, 32, 2, 2, true>(a, stream);
   } else {
-    if (a.dk == 64 && a.dv == 64) return launch<float, 64, 64, 64, 1, 4>(a, stream);
+    if (a.dk == 64 && a.dv == 64) return launch<float, 64, 64, 64, 1, 4, false>(a, stream);
   }
   return hipErrorInvalidValue;
 }
