@@ -792,7 +792,9 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
   // segment 3, for the next chunk) and U (segment 2) to them as bf16 operands,
   // and they form O^T: the state part in segment 1, U^T P^T and the store in
   // segment 3.
+  // Issue priority: consumers (the recurrence) over producers over output waves.
   if (producer) {
+    __builtin_amdgcn_s_setprio(1);
     if constexpr (MM::TPG == 2) {  // P tiles (0,1) and (2,3) share fragments with written tiles and are zero
       T* sPf = reinterpret_cast<T*>(smem + L::oPf);
       if (wave < 2) *reinterpret_cast<V4*>(sPf + L::pf(2 * wave, 2 * wave + 1, lane)) = pack4<T>(0.f, 0.f, 0.f, 0.f);
@@ -842,6 +844,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
       }
     }
   } else {
+    __builtin_amdgcn_s_setprio(2);
     if constexpr (NSTAGE == 2) {
       if (nch > 0) {
         if constexpr (OUTW) state_operands();
