@@ -77,10 +77,14 @@ __device__ __forceinline__ float quad_bcast(float x) {
 // holds rows 4q..4q+3 in x.  Once x_j is final (step j) it is broadcast
 // within the quad and every row i > j takes x_i -= A_ij x_j; At[j][i] = A_ij
 // (zero for i <= j, so the other rows are unchanged).
+// The 15 columns of A the lane needs are loaded first, so the substitution
+// waits for LDS once rather than once per step.
 template <int... J>
 __device__ __forceinline__ void unit_lower_inverse_column(floatx4& x, const float* At, int ld, int q,
                                                           std::integer_sequence<int, J...>) {
-  ((x -= *reinterpret_cast<const floatx4*>(At + J * ld + 4 * q) * quad_bcast<J / 4>(x[J % 4])), ...);
+  floatx4 a[sizeof...(J)];
+  ((a[J] = *reinterpret_cast<const floatx4*>(At + J * ld + 4 * q)), ...);
+  ((x -= a[J] * quad_bcast<J / 4>(x[J % 4])), ...);
 }
 
 // 16x16 tile products whose contraction is one 16-wide block: lane group g
@@ -304,8 +308,9 @@ struct ChunkRegs {
       const int t = min(tid + it * PTHREADS, C * VPR - 1);
       v[it] = *reinterpret_cast<const frag*>(vc + __umul24(min(t / VPR, Lc - 1), v_row) + (t % VPR) * 16);
     }
-    if (tid < 64) {  // wave 0 owns the gates, one token per lane
-      const uint32_t off = __umul24(min(tid, Lc - 1), g_row);
+    const int gl = tid - (PTHREADS - 64);  // the last producer wave owns the gates, one token per lane
+    if (gl >= 0) {
+      const uint32_t off = __umul24(min(gl, Lc - 1), g_row);
       g = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(gb) + off);
       b = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(bb) + off);
     }
@@ -348,13 +353,15 @@ struct ChunkRegs {
 };
 
 // Gram tiles (ti >= tj) of producer wave W, grouped by token-row tile so that
-// a wave loads each B fragment (K and Q rows of tile ti) once per k-group:
-//   wave 0: (3,0) (3,1) (3,2)    wave 1: (2,0) (2,1) (2,2)
-//   wave 2: (1,0) (1,1)          wave 3: (0,0) (3,3)
+// a wave loads each B fragment (K and Q rows of tile ti) once per k-group.
+// Waves 0 and 1 share their SIMDs with the (higher-priority) consumer waves
+// and get the lighter shares:
+//   wave 0: (3,0) (3,1) (3,2)    wave 1: (2,0) (2,1)
+//   wave 2: (1,0) (1,1) (2,2)    wave 3: (0,0) (3,3)
 template <int W> struct GramTiles;
 template <> struct GramTiles<0> { static constexpr int n = 3, ti[3] = {3, 3, 3}, tj[3] = {0, 1, 2}; };
-template <> struct GramTiles<1> { static constexpr int n = 3, ti[3] = {2, 2, 2}, tj[3] = {0, 1, 2}; };
-template <> struct GramTiles<2> { static constexpr int n = 2, ti[3] = {1, 1, 0}, tj[3] = {0, 1, 0}; };
+template <> struct GramTiles<1> { static constexpr int n = 2, ti[3] = {2, 2, 0}, tj[3] = {0, 1, 0}; };
+template <> struct GramTiles<2> { static constexpr int n = 3, ti[3] = {1, 1, 2}, tj[3] = {0, 1, 2}; };
 template <> struct GramTiles<3> { static constexpr int n = 2, ti[3] = {0, 3, 0}, tj[3] = {0, 3, 0}; };
 
 template <class T, int DK, int DV, int BV, int NSTAGE, int NCW, bool OUTW>
@@ -433,7 +440,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
     const int cs = bos + c * C, Lc = min(C, eos - cs);
     pre.store(reinterpret_cast<T*>(S + L::sK), reinterpret_cast<T*>(S + L::sQ), reinterpret_cast<T*>(S + L::sV),
               L::KNAT ? reinterpret_cast<T*>(S + L::sKn) : nullptr, LDK, LDV, tid);
-    if (wave == 0) {
+    if (wave == NP - 1) {  // the lightest producer wave in this segment and the next
       const bool live = lane < Lc;  // tokens past the end act as g = 0, beta = 0 (exact no-ops)
       const float bt = live ? pre.b : 0.f;
       // inclusive prefix sum of the log-gates over the chunk
