@@ -652,7 +652,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
 
   // O^T += U^T P^T over the chunk's token tiles, then O -> HBM (U from Z, or,
   // in an output wave, from the exchange slots).
-  auto out_pu = [&](int c, const frag* uex = nullptr) __attribute__((always_inline)) {
+  auto out_pu = [&](int c, int s, const frag* uex = nullptr) __attribute__((always_inline)) {
     const T* sPf = reinterpret_cast<const T*>(smem + L::oPf);
     const int cs = bos + c * C, Lc = min(C, eos - cs);
     // every P fragment read from LDS feeds all of the wave's n-tiles
@@ -671,17 +671,54 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
         }
       }
     }
-    T* orow = og + static_cast<size_t>(cs + lr) * v_tok + static_cast<size_t>(h) * DV + wcol + 4 * lg;
+    if constexpr (OUTW) {
+      T* orow = og + static_cast<size_t>(cs + lr) * v_tok + static_cast<size_t>(h) * DV + wcol + 4 * lg;
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      if (16 * ct + lr < Lc) {
+      for (int ct = 0; ct < 4; ++ct) {
+        if (16 * ct + lr < Lc) {
+#pragma unroll
+          for (int j = 0; j < NTW; ++j) {
+            const floatx4 ov = Ot[ct][j] * p.scale;
+            *reinterpret_cast<V4*>(orow + static_cast<size_t>(16 * ct) * v_tok + 16 * j) =
+                pack4<T>(ov[0], ov[1], ov[2], ov[3]);
+          }
+        }
+      }
+    } else {
+      // The output tile goes to LDS first, into the chunk's V tile (V is used
+      // up by now and the stage is not refilled before the next chunk's
+      // segment 2); o_rows_out then writes it as whole rows.  Written straight
+      // from the accumulator layout, every store would cover 16 rows with 32
+      // bytes each, and the memory path would stall the consumer for a large
+      // part of the chunk.
+      T* sO = reinterpret_cast<T*>(stage(s) + L::sV);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
           const floatx4 ov = Ot[ct][j] * p.scale;
-          *reinterpret_cast<V4*>(orow + static_cast<size_t>(16 * ct) * v_tok + 16 * j) =
+          const int r = 16 * ct + lr, col = (cw * NTW + j) * 16 + 4 * lg;
+          *reinterpret_cast<V4*>(sO + (sizeof(T) == 2 ? swz_off<BV>(r, col) : r * LDV + col)) =
               pack4<T>(ov[0], ov[1], ov[2], ov[3]);
         }
-      }
+    }
+  };
+  // The chunk's output rows, BV columns each, from LDS to HBM in 16-byte
+  // pieces (consecutive lanes cover consecutive pieces of a row).
+  auto o_rows_out = [&](int c, int s) __attribute__((always_inline)) {
+    constexpr int PPR = BV * sizeof(T) / 16;      // 16-byte pieces per row
+    constexpr int NT = 64 * NCW;                  // consumer threads
+    constexpr int EP = 16 / sizeof(T);
+    const T* sO = reinterpret_cast<const T*>(stage(s) + L::sV);
+    const int cs = bos + c * C, Lc = min(C, eos - cs);
+    const int ct0 = tid - 64 * NP;
+#pragma unroll
+    for (int it = 0; it < (C * PPR + NT - 1) / NT; ++it) {
+      const int t = ct0 + it * NT;
+      const int r = t / PPR, col = (t % PPR) * EP;
+      if (t < C * PPR && r < Lc)
+        *reinterpret_cast<frag*>(og + static_cast<size_t>(cs + r) * v_tok + static_cast<size_t>(h) * DV + col0 + col) =
+            *reinterpret_cast<const frag*>(sO + (sizeof(T) == 2 ? swz_off<BV>(r, col) : r * LDV + col));
     }
   };
 
@@ -722,7 +759,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
 #pragma unroll
       for (int kgi = 0; kgi < KGC; ++kgi) sUx[kgi * 64 + lane] = chain_frag<T>([&](int t) { return Z[t][0]; }, kgi);
     } else {
-      out_pu(c);
+      out_pu(c, s);
     }
   };
 
@@ -737,7 +774,8 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
     return v;
   };
-  auto cons_seg3 = [&](int s) __attribute__((always_inline)) {
+  auto cons_seg3 = [&](int c, int s) __attribute__((always_inline)) {
+    if constexpr (!OUTW) o_rows_out(c, s);
     const unsigned char* S = stage(s);
     const int olane = opaque_lane();
     const T* sK = reinterpret_cast<const T*>(S + L::sK);
@@ -846,7 +884,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
         outw_qm(c & 1);
         lds_barrier();
         lds_barrier();
-        out_pu(c, sUx);
+        out_pu(c, c & 1, sUx);
         lds_barrier();
       }
     }
@@ -863,7 +901,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
         lds_barrier();
         cons_seg2(c, c & 1);
         lds_barrier();
-        cons_seg3(c & 1);
+        cons_seg3(c, c & 1);
         lds_barrier();
       }
     } else {
@@ -875,7 +913,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
         lds_barrier();
         cons_seg2(c, 0);
         lds_barrier();
-        cons_seg3(0);
+        cons_seg3(c, 0);
         lds_barrier();
       }
     }
