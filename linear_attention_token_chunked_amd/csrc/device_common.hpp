@@ -55,9 +55,10 @@ __device__ __forceinline__ typename Vec4<T>::type pack4(float a, float b, float 
 // product straight from registers ("chaining"): lane group g owns accumulator
 // rows 4g..4g+3, so K(g) is taken to be {4g..4g+3} for fp32 and
 // {4g..4g+3} u {16+4g..16+4g+3} for bf16 (two stacked accumulator tiles).
-// Operands that come from LDS are stored with the k axis permuted the same way
-// (see phys_k), so a lane reads its 16 bytes contiguously.
-// ---------------------------------------------------------------------------
+// Operands read from LDS rows instead come in natural k order: lane group g
+// reads k = 8g..8g+7 of a bf16 k-group as one 16-byte run.  Where both meet (the
+// state, a chained B operand, against K or Q rows from LDS), the state's
+// accumulator rows are assigned to key indices to match (see state_row).
 template <class T> struct Mma;
 
 template <> struct Mma<bf16> {
@@ -76,9 +77,12 @@ template <> struct Mma<bf16> {
     f[6] = static_cast<bf16>(hi[2]); f[7] = static_cast<bf16>(hi[3]);
     return f;
   }
-  // Position inside LDS of logical contraction index k (any k >= 0).
-  __device__ __forceinline__ static int phys_k(int k) {
-    return (k & ~31) | (((k >> 2) & 3) << 3) | (((k >> 4) & 1) << 2) | (k & 3);
+  // Key index held by row 4g + s of state accumulator tile a.  Element e of
+  // the chained operand of k-group kg is row 4g + (e & 3) of tile 2kg + (e >> 2);
+  // it must pair with key 32kg + 8g + e, the one a natural-order LDS row
+  // gives lane group g there.
+  __device__ __forceinline__ static constexpr int state_row(int a, int g, int s) {
+    return 32 * (a >> 1) + 8 * g + 4 * (a & 1) + s;
   }
 };
 
@@ -93,11 +97,11 @@ template <> struct Mma<float> {
     c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
   }
   __device__ __forceinline__ static frag chain(const floatx4& t) { return t; }
-  __device__ __forceinline__ static int phys_k(int k) { return k; }
+  __device__ __forceinline__ static constexpr int state_row(int a, int g, int s) { return 16 * a + 4 * g + s; }
 };
 
-// 16-byte operand fragment of k-group kg from an LDS row (row-major, k axis
-// stored in phys_k order).  Lane group g reads bytes [16g, 16g+16) of the group.
+// 16-byte operand fragment of k-group kg from an LDS row (row-major, natural
+// k order).  Lane group g reads bytes [16g, 16g+16) of the group.
 template <class T>
 __device__ __forceinline__ typename Mma<T>::frag lds_frag(const T* row, int kg, int lane) {
   constexpr int EPB = 16 / sizeof(T);

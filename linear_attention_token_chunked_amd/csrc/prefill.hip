@@ -114,37 +114,33 @@ template <> struct Mma16<float> {
 
 // Four consecutive rows of one column of a row-major LDS tile, as lane data
 // for the accumulator layout: lane (lg, lr) gets X[r0 + 4lg + e][c0 + lr],
-// e = 0..3 (c0 a multiple of 16; PERM: the column axis is stored in phys_k
-// order, which keeps every aligned run of 4 columns contiguous).  bf16 uses
-// the gfx950 transposing LDS read: in each 16-lane group, lane i returns
-// element i%4 of the 8-byte loads of lanes 4e + i/4, so lane j loads row
-// r0 + 4lg + j/4 at the 4-column run c0 + 4(j%4).  fp32 reads the four values
-// one by one.
-template <class T, bool PERM>
+// e = 0..3 (c0 a multiple of 16).  bf16 uses the gfx950 transposing LDS read:
+// in each 16-lane group, lane i returns element i%4 of the 8-byte loads of
+// lanes 4e + i/4, so lane j loads row r0 + 4lg + j/4 at the 4-column run
+// c0 + 4(j%4).  fp32 reads the four values one by one.
+template <class T>
 __device__ __forceinline__ typename Vec4<T>::type lds_col4(const T* base, int ld, int r0, int c0, int lane) {
   const int lg = lane >> 4, lr = lane & 15;
   if constexpr (sizeof(T) == 2) {
     typedef short s4 __attribute__((ext_vector_type(4)));
-    const int col = PERM ? Mma<T>::phys_k(c0 + 4 * (lr & 3)) : c0 + 4 * (lr & 3);
-    const T* ptr = base + (r0 + 4 * lg + (lr >> 2)) * ld + col;
+    const T* ptr = base + (r0 + 4 * lg + (lr >> 2)) * ld + c0 + 4 * (lr & 3);
     const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         reinterpret_cast<__attribute__((address_space(3))) s4*>(reinterpret_cast<size_t>(ptr)));
     return __builtin_bit_cast(typename Vec4<T>::type, v);
   } else {
-    const int col = PERM ? Mma<T>::phys_k(c0 + lr) : c0 + lr;
     typename Vec4<T>::type v;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = base[(r0 + 4 * lg + e) * ld + col];
+    for (int e = 0; e < 4; ++e) v[e] = base[(r0 + 4 * lg + e) * ld + c0 + lr];
     return v;
   }
 }
 
-// bf16 tiles that are read only down their columns (the natural-order copy of
-// K and the V tile) store the 16-column blocks of a row at swizzled places:
-// block b of row r sits at block b ^ swz(r).  A transposing read covers four
-// rows of one block per 16-lane group and eight rows per 32 lanes; the
-// swizzle puts those eight rows' 32-byte runs on eight different bank windows
-// (unswizzled, 256-byte rows would put them all on the same one).
+// The bf16 V tile is read only down its columns; it stores the 16-column
+// blocks of a row at swizzled places: block b of row r sits at block
+// b ^ swz(r).  A transposing read covers four rows of one block per 16-lane
+// group and eight rows per 32 lanes; the swizzle puts those eight rows'
+// 32-byte runs on eight different bank windows (unswizzled, 256-byte rows
+// would put them all on the same one).
 template <int W>
 __device__ __forceinline__ int swz(int r) {
   constexpr int NB = W / 16;                    // 16-column blocks per row
@@ -162,25 +158,42 @@ __device__ __forceinline__ bf16x4 tr_read(const bf16* ptr) {
       reinterpret_cast<__attribute__((address_space(3))) s4*>(reinterpret_cast<size_t>(ptr)));
   return __builtin_bit_cast(bf16x4, v);
 }
-// lds_col4<bf16, false> for a swizzled tile of width W.
+// lds_col4<bf16> for a swizzled tile of width W.
 template <int W>
 __device__ __forceinline__ bf16x4 swz_col4(const bf16* base, int r0, int c0, int lane) {
   const int lg = lane >> 4, lr = lane & 15;
   return tr_read(base + swz_off<W>(r0 + 4 * lg + (lr >> 2), c0 + 4 * (lr & 3)));
 }
-// The same reads split into a per-lane part and a per-block part: for row
-// offsets r0 that are multiples of 16 the swizzle depends on the lane only, so
-// column block b of rows r0.. is read at lane_base + r0 * W + block_off(b).
-template <int W>
-struct SwzCols {
+
+// The second, column-read copy of K (bf16, rows of DK keys).  The K^T operand
+// for state tile a (keys per state_row) takes from each token row the four
+// 8-byte runs of keys 32(a>>1) + 4(a&1) + 8m, m = 0..3, 16 bytes apart.  The
+// 8-byte units u of row r are stored at u ^ (8 kn_x(r) + kn_e(r)): kn_x
+// permutes pairs of 32-byte blocks and kn_e swaps the halves of each 16-byte
+// piece, so the eight rows one 32-lane half of a transposing read covers use
+// 32 distinct bank pairs.  kn_e is bit 2 of the row.
+template <int DK>
+__device__ __forceinline__ int kn_x(int r) { return (r / (128 / DK)) & (DK / 32 - 1); }
+__device__ __forceinline__ int kn_e(int r) { return (r >> 2) & 1; }
+// Element offset of the (unswapped) 16-byte piece pc of row r.
+template <int DK>
+__device__ __forceinline__ int kn_piece(int r, int pc) { return r * DK + 8 * (pc ^ (kn_x<DK>(r) << 2)); }
+// Read addresses, split into a per-lane part and a per-tile part: the rows a
+// transposing read covers start at multiples of 8, where the swizzle depends
+// on the lane only.
+template <int DK>
+struct KnCols {
   const bf16* lane_base;
-  int x;
-  __device__ __forceinline__ SwzCols(const bf16* base, int lane) {
+  int x, e;
+  __device__ __forceinline__ KnCols(const bf16* base, int lane) {
     const int rl = 4 * (lane >> 4) + ((lane & 15) >> 2);
-    x = swz<W>(rl);
-    lane_base = base + rl * W + 4 * (lane & 3);
+    x = kn_x<DK>(rl);
+    e = kn_e(rl);
+    lane_base = base + rl * DK + 8 * (lane & 3);
   }
-  __device__ __forceinline__ const bf16* block(int b) const { return lane_base + ((b ^ x) << 4); }
+  __device__ __forceinline__ const bf16* tile(int a) const {
+    return lane_base + 32 * ((a >> 1) ^ x) + 4 * ((a & 1) ^ e);
+  }
 };
 
 // Operand fragment of k-group kg built from accumulator tiles tile(kg*TPG + t).
@@ -198,11 +211,10 @@ template <class T, int DK, int BV, int NSTAGE, int NCW, bool OUTW>
 struct Layout {
   static constexpr int EPB = 16 / sizeof(T);
   static constexpr int NTW = BV / (16 * NCW);   // 16-column state tiles per consumer wave
-  static constexpr int LDK = DK + EPB;          // [C][DK] rows: K, Q (key axis in phys_k order)
+  static constexpr int LDK = DK + EPB;          // [C][DK] rows: K, Q (natural key order)
   static constexpr int LDV = BV;                // [C][BV] rows: V (only read down its columns; bf16 swizzled)
-  // bf16 keeps a second copy of K with the key axis in natural order
-  // (swizzled): the transposing reads of K^T then load whole 32-byte runs, at
-  // half the cost of reading them out of the phys_k copy.
+  // bf16 keeps a second copy of K for the transposing reads of K^T, swizzled
+  // for them (kn_piece); out of the padded rows they would conflict on banks.
   static constexpr bool KNAT = sizeof(T) == 2;
   static constexpr int KGC = C / Mma<T>::KG;    // k-groups over the chunk
   static constexpr int LDA = 20;                // fp32 diagonal blocks of A
@@ -210,7 +222,7 @@ struct Layout {
   static constexpr size_t sK = 0;
   static constexpr size_t sQ = sK + sizeof(T) * C * LDK;
   static constexpr size_t sV = sQ + sizeof(T) * C * LDK;
-  static constexpr size_t sKn = sV + sizeof(T) * C * LDV;   // [C][DK] K, natural key order (bf16)
+  static constexpr size_t sKn = sV + sizeof(T) * C * LDV;   // [C][DK] K, column-read copy (bf16)
   static constexpr size_t sVec = sKn + (KNAT ? sizeof(T) * C * DK : 0);  // exp G, beta, exp(G_C - G), exp G_C
   static constexpr size_t stage_bytes = (sVec + 4 * 4 * C + 15) / 16 * 16;
   // Single-buffered, written by the producers in segment 1 after the
@@ -276,11 +288,20 @@ struct ChunkRegs {
   static constexpr int EPB = 16 / sizeof(T);
   static constexpr int KPR = DK / EPB;                  // 16-byte pieces per K / Q row
   static constexpr int KIT = C * KPR / PTHREADS;        // K (and Q) pieces per producer thread
+  static constexpr int RPI = 64 / KPR;                  // K rows per wave-wide load
   static constexpr int VPR = BV / EPB;                  // 16-byte pieces per V row (this slice)
   static constexpr int VIT = (C * VPR + PTHREADS - 1) / PTHREADS;
-  static_assert(C * KPR % PTHREADS == 0, "K rows split evenly");
+  static_assert(C * KPR % PTHREADS == 0 && KIT % 2 == 0 && RPI % 4 == 0, "K rows split evenly");
   frag k[KIT], q[KIT], v[VIT];
   float g, b;
+
+  // Row of the K / Q piece a producer thread holds in slot it (its column is
+  // piece lane % KPR).  Bit 2 of the row is bit 0 of it, so the half swap of
+  // the column-read K copy (kn_e) is known at compile time.
+  __device__ __forceinline__ static int kq_row(int it, int tid) {
+    const int rr = (tid & 63) / KPR, w = tid >> 6;
+    return (rr & 3) | ((it & 1) << 2) | (((rr >> 2) + (RPI / 4) * (w + NP * (it >> 1))) << 3);
+  }
 
   // Every load is unconditional and reads a valid row (rows past the end of
   // the sequence read its last token): a select on a loaded value would make
@@ -298,8 +319,7 @@ struct ChunkRegs {
     const char* vc = reinterpret_cast<const char*>(vb);
 #pragma unroll
     for (int it = 0; it < KIT; ++it) {
-      const int t = tid + it * PTHREADS;
-      const uint32_t off = __umul24(min(t / KPR, Lc - 1), qk_row) + (t % KPR) * 16;
+      const uint32_t off = __umul24(min(kq_row(it, tid), Lc - 1), qk_row) + (tid % KPR) * 16;
       k[it] = *reinterpret_cast<const frag*>(kc + off);
       q[it] = *reinterpret_cast<const frag*>(qc + off);
     }
@@ -316,29 +336,19 @@ struct ChunkRegs {
     }
   }
 
-
-
-
-  // K, Q -> rows with the key axis in phys_k order; V and (if sKn) a second
-  // copy of K -> rows in natural order.
+  // K, Q -> padded rows in natural key order; V and (if sKn) the column-read
+  // copy of K -> swizzled rows.  Every store is one 16-byte piece.
   __device__ __forceinline__ void store(T* sK, T* sQ, T* sV, T* sKn, int LDK, int LDV, int tid) const {
-    typedef typename Vec4<T>::type V4;
 #pragma unroll
     for (int it = 0; it < KIT; ++it) {
-      const int t = tid + it * PTHREADS;
-      const int r = t / KPR, c = (t % KPR) * EPB;
-      if constexpr (sizeof(T) == 2)
-        if (sKn) *reinterpret_cast<frag*>(sKn + swz_off<DK>(r, c)) = k[it];
-#pragma unroll
-      for (int u = 0; u < EPB / 4; ++u) {
-        V4 wk, wq;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          wk[e] = k[it][4 * u + e];
-          wq[e] = q[it][4 * u + e];
+      const int r = kq_row(it, tid), pc = tid % KPR;
+      *reinterpret_cast<frag*>(sK + r * LDK + pc * EPB) = k[it];
+      *reinterpret_cast<frag*>(sQ + r * LDK + pc * EPB) = q[it];
+      if constexpr (sizeof(T) == 2) {
+        if (sKn) {
+          const frag x = (it & 1) ? __builtin_shufflevector(k[it], k[it], 4, 5, 6, 7, 0, 1, 2, 3) : k[it];
+          *reinterpret_cast<frag*>(sKn + kn_piece<DK>(r, pc)) = x;
         }
-        *reinterpret_cast<V4*>(sK + r * LDK + Mma<T>::phys_k(c + 4 * u)) = wk;
-        *reinterpret_cast<V4*>(sQ + r * LDK + Mma<T>::phys_k(c + 4 * u)) = wq;
       }
     }
 #pragma unroll
@@ -469,21 +479,25 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
     floatx4 kk[3], qk[3];
 #pragma unroll
     for (int t = 0; t < 3; ++t) kk[t] = qk[t] = zero4();
+    // All fragments are read before the first product: under the load the
+    // other roles put on the LDS, a read takes hundreds of cycles, and a
+    // read-then-multiply loop over the k-groups would pay that once per group.
+    frag rowk[KGK][4], rowq[KGK][4];  // fragments of token-row tiles; only the ones used are loaded
 #pragma unroll
-    for (int kgi = 0; kgi < KGK; ++kgi) {
-      frag rowk[4], rowq[4];  // fragments of token-row tiles; only the ones used are loaded
-#pragma unroll
-      for (int t = 0; t < GT::n; ++t) {
-        rowk[GT::ti[t]] = lds_frag(sK + (16 * GT::ti[t] + lr) * LDK, kgi, lane);
-        rowq[GT::ti[t]] = lds_frag(sQ + (16 * GT::ti[t] + lr) * LDK, kgi, lane);
-        rowk[GT::tj[t]] = lds_frag(sK + (16 * GT::tj[t] + lr) * LDK, kgi, lane);
-      }
+    for (int kgi = 0; kgi < KGK; ++kgi)
 #pragma unroll
       for (int t = 0; t < GT::n; ++t) {
-        MM::mma(kk[t], rowk[GT::tj[t]], rowk[GT::ti[t]]);
-        MM::mma(qk[t], rowk[GT::tj[t]], rowq[GT::ti[t]]);
+        rowk[kgi][GT::ti[t]] = lds_frag(sK + (16 * GT::ti[t] + lr) * LDK, kgi, lane);
+        rowq[kgi][GT::ti[t]] = lds_frag(sQ + (16 * GT::ti[t] + lr) * LDK, kgi, lane);
+        rowk[kgi][GT::tj[t]] = lds_frag(sK + (16 * GT::tj[t] + lr) * LDK, kgi, lane);
       }
-    }
+#pragma unroll
+    for (int kgi = 0; kgi < KGK; ++kgi)
+#pragma unroll
+      for (int t = 0; t < GT::n; ++t) {
+        MM::mma(kk[t], rowk[kgi][GT::tj[t]], rowk[kgi][GT::ti[t]]);
+        MM::mma(qk[t], rowk[kgi][GT::tj[t]], rowq[kgi][GT::ti[t]]);
+      }
     // lane holds X[i = 16ti + lr][j = 16tj + 4lg + s] of both products
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
@@ -532,6 +546,9 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
     }
   };
   auto prod_finish = [&]() __attribute__((always_inline)) {
+    // With output waves, the inverses are the longest chain of segment 1:
+    // they get the top issue priority while they run.
+    if constexpr (OUTW) __builtin_amdgcn_s_setprio(3);
     switch (wave) {
       case 0: put(std::integral_constant<int, 0>()); break;
       case 1: put(std::integral_constant<int, 1>()); break;
@@ -550,18 +567,19 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
 #pragma unroll
       for (int t = 0; t < 4; ++t) Tb[L::tbf(wave, 16 * (cc >> 2) + 4 * q + t) + (cc & 3)] = from_float<T>(x[t]);
     }
+    if constexpr (OUTW) __builtin_amdgcn_s_setprio(1);
   };
 
 
   // ------------------------------------------------------------ consumer state
-  // Ms[a][j] holds M[16a + 4lg + s][wcol + 16j + lr], s = 0..3.
+  // Ms[a][j] holds M[state_row(a, lg, s)][wcol + 16j + lr], s = 0..3.
   floatx4 Ms[KT][NTW];
   floatx4 Z[4][NTW];  // Z, then U, by 16-row token block
   frag mfr[KGK][NTW];  // the state as matrix-core operands (bf16-rounded for bf16 inputs), per chunk
   // the unit's state: uniform base, small per-lane offsets (keeps 64-bit
   // per-element addresses out of the registers)
   const size_t sbase = static_cast<size_t>(unit) * DK * DV;
-  const int slane = 4 * lg * DV + wcol + lr;
+  const int slane = MM::state_row(0, lg, 0) * DV + wcol + lr;
   if (consumer) {
     const float* h0 = p.h0 + sbase;
 #pragma unroll
@@ -569,7 +587,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
 #pragma unroll
       for (int j = 0; j < NTW; ++j)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) Ms[a][j][s] = p.h0 ? h0[slane + (16 * a + s) * DV + 16 * j] : 0.f;
+        for (int s = 0; s < 4; ++s) Ms[a][j][s] = p.h0 ? h0[slane + MM::state_row(a, 0, s) * DV + 16 * j] : 0.f;
   }
 
   // seg 1: Y = K M; Z = beta (V - exp(G) Y).  With one state tile per wave the
@@ -592,9 +610,9 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
     }
   };
   floatx4 Ot[4][NTW];  // O^T by 16-token tile: lane holds O[16ct + lr][wcol + 16j + 4lg + s]
-  auto q_times_state = [&](const T* sQ, const float* vec) __attribute__((always_inline)) {
+  auto q_times_state = [&](const T* sQ, const float* vec, int r0 = 0, int r1 = 4) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = r0; r < r1; ++r) {
 #pragma unroll
       for (int j = 0; j < NTW; ++j) Ot[r][j] = zero4();
 #pragma unroll
@@ -643,7 +661,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
         if constexpr (sizeof(T) == 2)
           v4 = swz_col4<BV>(sV, 16 * r, (cw * NTW + j) * 16, lane);
         else
-          v4 = lds_col4<T, false>(sV, LDV, 16 * r, (cw * NTW + j) * 16, lane);
+          v4 = lds_col4<T>(sV, LDV, 16 * r, (cw * NTW + j) * 16, lane);
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) Z[r][j][s4] = bt[s4] * (to_float(v4[s4]) - eg[s4] * Z[r][j][s4]);
       }
@@ -794,7 +812,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
     for (int a = 0; a < KT; ++a)
 #pragma unroll
       for (int j = 0; j < NTW; ++j) Ms[a][j] *= eGC;
-    const SwzCols<DK> kcols(reinterpret_cast<const bf16*>(sKn), olane);  // bf16 only (unused for fp32)
+    const KnCols<DK> kcols(reinterpret_cast<const bf16*>(sKn), olane);  // bf16 only (unused for fp32)
 #pragma unroll
     for (int kgi = 0; kgi < KGC; ++kgi) {
       frag bu[NTW];
@@ -804,10 +822,10 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
       for (int a = 0; a < KT; ++a) {
         frag af;  // K^T rows 16a.., tokens of k-group kgi, from the row-major K tile
         if constexpr (MM::KG == 32) {
-          const bf16* pa = kcols.block(a) + 32 * kgi * DK;
+          const bf16* pa = kcols.tile(a) + 32 * kgi * DK;
           af = __builtin_shufflevector(tr_read(pa), tr_read(pa + 16 * DK), 0, 1, 2, 3, 4, 5, 6, 7);
         } else {
-          af = lds_col4<T, true>(sK, LDK, 16 * kgi, 16 * a, lane);
+          af = lds_col4<T>(sK, LDK, 16 * kgi, 16 * a, lane);
         }
 #pragma unroll
         for (int j = 0; j < NTW; ++j) MM::mma(Ms[a][j], af, bu[j]);
@@ -816,12 +834,18 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
     if constexpr (OUTW) state_operands();  // the next chunk's state operands, for both waves
   };
 
-  // Output wavefronts: the state part of O^T in segment 1 and U^T P^T with the
-  // store in segment 3, from the operands their consumer wave leaves in LDS.
-  auto outw_qm = [&](int s) __attribute__((always_inline)) {
+  // Output wavefronts: the state part of O^T over segments 1 and 2 (token
+  // tiles 0-1, then 2-3) and U^T P^T with the store in segment 3, from the
+  // operands their consumer wave leaves in LDS.  Spreading the state part
+  // over two segments keeps their LDS reads from crowding the start of
+  // segment 1, where the producers' inverses are on the critical path.
+  auto outw_qm = [&](int s, int r0, int r1) __attribute__((always_inline)) {
+    if (r0 == 0) {
 #pragma unroll
-    for (int kgi = 0; kgi < KGK; ++kgi) mfr[kgi][0] = sMx[kgi * 64 + lane];
-    q_times_state(reinterpret_cast<const T*>(stage(s) + L::sQ), reinterpret_cast<const float*>(stage(s) + L::sVec));
+      for (int kgi = 0; kgi < KGK; ++kgi) mfr[kgi][0] = sMx[kgi * 64 + lane];
+    }
+    q_times_state(reinterpret_cast<const T*>(stage(s) + L::sQ), reinterpret_cast<const float*>(stage(s) + L::sVec),
+                  r0, r1);
   };
 
   // ------------------------------------------------------------ schedule
@@ -835,9 +859,10 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
   //   seg 3    Gram products of chunk c + 1           state update
   // With output wavefronts the consumers hand the state (after the update in
   // segment 3, for the next chunk) and U (segment 2) to them as bf16 operands,
-  // and they form O^T: the state part in segment 1, U^T P^T and the store in
-  // segment 3.
-  // Issue priority: consumers (the recurrence) over producers over output waves.
+  // and they form O^T: the state part in segments 1 and 2, U^T P^T and the
+  // store in segment 3.
+  // Issue priority: consumers (the recurrence) over producers over output
+  // waves; with output waves the producers' segment-1 work goes first.
   if (producer) {
     __builtin_amdgcn_s_setprio(1);
     if constexpr (MM::TPG == 2) {  // P tiles (0,1) and (2,3) share fragments with written tiles and are zero
@@ -881,8 +906,9 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
         lds_barrier();
       }
       for (int c = 0; c < nch; ++c) {
-        outw_qm(c & 1);
+        outw_qm(c & 1, 0, 2);
         lds_barrier();
+        outw_qm(c & 1, 2, 4);
         lds_barrier();
         out_pu(c, c & 1, sUx);
         lds_barrier();
@@ -926,7 +952,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
 #pragma unroll
       for (int j = 0; j < NTW; ++j)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) hT[slane + (16 * a + s) * DV + 16 * j] = Ms[a][j][s];
+        for (int s = 0; s < 4; ++s) hT[slane + MM::state_row(a, 0, s) * DV + 16 * j] = Ms[a][j][s];
   }
 }
 
