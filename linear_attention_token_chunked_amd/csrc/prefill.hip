@@ -206,12 +206,16 @@ __device__ __forceinline__ typename Mma<T>::frag chain_frag(F tile, int kg) {
   }
 }
 
-// LDS layout.  K and Q rows are padded by 16 bytes against bank conflicts.
+// LDS layout.  K and Q rows are padded against bank conflicts (see LDK).
 template <class T, int DK, int BV, int NSTAGE, int NCW, bool OUTW>
 struct Layout {
   static constexpr int EPB = 16 / sizeof(T);
   static constexpr int NTW = BV / (16 * NCW);   // 16-column state tiles per consumer wave
-  static constexpr int LDK = DK + EPB;          // [C][DK] rows: K, Q (natural key order)
+  // [C][DK] rows of K and Q (natural key order), padded so that the 16 rows
+  // one 16-byte row read covers fall on distinct banks: bf16 rows take 32
+  // bytes of padding (16 bytes leave a two-way conflict on gfx950).  fp32
+  // keeps 16, which also serves its column reads.
+  static constexpr int LDK = DK + (sizeof(T) == 2 ? 2 * EPB : EPB);
   static constexpr int LDV = BV;                // [C][BV] rows: V (only read down its columns; bf16 swizzled)
   // bf16 keeps a second copy of K for the transposing reads of K^T, swizzled
   // for them (kn_piece); out of the padded rows they would conflict on banks.
