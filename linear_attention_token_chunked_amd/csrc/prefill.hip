@@ -227,14 +227,16 @@ struct Layout {
   static constexpr size_t sQ = sK + sizeof(T) * C * LDK;
   static constexpr size_t sV = sQ + sizeof(T) * C * LDK;
   static constexpr size_t sKn = sV + sizeof(T) * C * LDV;   // [C][DK] K, column-read copy (bf16)
-  static constexpr size_t sVec = sKn + (KNAT ? sizeof(T) * C * DK : 0);  // exp G, beta, exp(G_C - G), exp G_C
-  static constexpr size_t stage_bytes = (sVec + 4 * 4 * C + 15) / 16 * 16;
+  // per-token vectors: exp G, beta, exp(G_C - G), exp G_C (uniform), G log2(e)
+  static constexpr size_t sVec = sKn + (KNAT ? sizeof(T) * C * DK : 0);
+  static constexpr size_t stage_bytes = (sVec + 5 * 4 * C + 15) / 16 * 16;
   // Single-buffered, written by the producers in segment 1 after the
   // consumers have read the previous chunk's copy in segment 2.  All three
   // are kept in "fragment order": the 16 (or 8) bytes one lane contributes to
   // a matrix-core operand are stored contiguously, lane after lane, so both
   // the producers' writes and the consumers' reads are conflict-free.
   //   P:   per (token tile ct, k-group kg), the B operand P^T of O^T += U^T P^T
+  //        (with output waves written by them, in segment 2)
   //   -A:  the A operands of the block substitution: (1,0); (2,0)+(2,1); (3,0)+(3,1); (3,2)
   //   T_bb: the A operands (I + A_bb)^-1 of the four diagonal blocks
   static constexpr size_t oPf = NSTAGE * stage_bytes;
@@ -242,11 +244,11 @@ struct Layout {
   static constexpr size_t oTbf = oAnf + size_t(6) * 64 * 4 * sizeof(T);
   // producer scratch
   static constexpr size_t oAd = oTbf + size_t(4) * 64 * 4 * sizeof(T);
-  static constexpr size_t oGl = oAd + 4 * 4 * 16 * LDA;
   // With output wavefronts: the state and U of each consumer wave as bf16
-  // matrix-core operands, fragment order (written in segments 1 and 2, read
-  // by the paired output wave in segments 2 and 3).
-  static constexpr size_t oMx = oGl + 4 * C;
+  // matrix-core operands, fragment order (the state written in segment 3 for
+  // the next chunk, U in segment 2; read by the paired output wave in
+  // segments 1 and 3).
+  static constexpr size_t oMx = oAd + 4 * 4 * 16 * LDA;
   static constexpr size_t oUx = oMx + (OUTW ? size_t(NCW) * (DK / Mma<T>::KG) * 64 * 16 : 0);
   static constexpr size_t bytes = oUx + (OUTW ? size_t(NCW) * KGC * 64 * 16 : 0);
   static_assert(!OUTW || NTW == 1, "output wavefronts pair with one-tile consumer waves");
@@ -378,6 +380,11 @@ template <> struct GramTiles<1> { static constexpr int n = 2, ti[3] = {2, 2, 0},
 template <> struct GramTiles<2> { static constexpr int n = 3, ti[3] = {1, 1, 2}, tj[3] = {0, 1, 2}; };
 template <> struct GramTiles<3> { static constexpr int n = 2, ti[3] = {0, 3, 0}, tj[3] = {0, 3, 0}; };
 
+// P tiles (ti >= tj) formed by output wave W (with output waves only).
+template <int W> struct OutPTiles;
+template <> struct OutPTiles<0> { static constexpr int ti[5] = {0, 1, 1, 2, 3}, tj[5] = {0, 0, 1, 0, 0}; };
+template <> struct OutPTiles<1> { static constexpr int ti[5] = {2, 2, 3, 3, 3}, tj[5] = {1, 2, 1, 2, 3}; };
+
 template <class T, int DK, int DV, int BV, int NSTAGE, int NCW, bool OUTW>
 __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kernel(Params p) {
   using L = Layout<T, DK, BV, NSTAGE, NCW, OUTW>;
@@ -392,7 +399,6 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   float* sAd = reinterpret_cast<float*>(smem + L::oAd);  // [4][16][LDA] fp32 diagonal blocks of A, transposed
-  float* sGl = reinterpret_cast<float*>(smem + L::oGl);  // [C] G * log2(e)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -465,14 +471,16 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
       vec[C + lane] = bt;
       vec[2 * C + lane] = __builtin_amdgcn_exp2f(GlC - Gl);
       vec[3 * C + lane] = __builtin_amdgcn_exp2f(GlC);
-      sGl[lane] = Gl;
+      vec[4 * C + lane] = Gl;
     }
     if (c + 1 < nch) issue_loads(c + 1);
   };
 
-  // K K^T and Q K^T tiles, masked with the decay.  The diagonal blocks of A go
-  // to LDS transposed (fp32, for the inverses); -A below the diagonal and P stay
-  // in registers until prod_finish.
+  // K K^T and (without output waves, which form P themselves) Q K^T tiles,
+  // masked with the decay.  The diagonal blocks of A go to LDS transposed
+  // (fp32, for the inverses); -A below the diagonal and P stay in registers
+  // until prod_finish.
+  constexpr bool PROD_P = !(OUTW && NCW == 2);  // two output waves form P themselves
   floatx4 pkeep[3], akeep[3];
   auto gram = [&](auto wtag, int s) __attribute__((always_inline)) {
     using GT = GramTiles<decltype(wtag)::value>;
@@ -480,6 +488,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
     const T* sK = reinterpret_cast<const T*>(S + L::sK);
     const T* sQ = reinterpret_cast<const T*>(S + L::sQ);
     const float* beta = reinterpret_cast<const float*>(S + L::sVec) + C;
+    const float* sGl = beta + 3 * C;  // G log2(e)
     floatx4 kk[3], qk[3];
 #pragma unroll
     for (int t = 0; t < 3; ++t) kk[t] = qk[t] = zero4();
@@ -492,7 +501,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
 #pragma unroll
       for (int t = 0; t < GT::n; ++t) {
         rowk[kgi][GT::ti[t]] = lds_frag(sK + (16 * GT::ti[t] + lr) * LDK, kgi, lane);
-        rowq[kgi][GT::ti[t]] = lds_frag(sQ + (16 * GT::ti[t] + lr) * LDK, kgi, lane);
+        if constexpr (PROD_P) rowq[kgi][GT::ti[t]] = lds_frag(sQ + (16 * GT::ti[t] + lr) * LDK, kgi, lane);
         rowk[kgi][GT::tj[t]] = lds_frag(sK + (16 * GT::tj[t] + lr) * LDK, kgi, lane);
       }
 #pragma unroll
@@ -500,7 +509,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
 #pragma unroll
       for (int t = 0; t < GT::n; ++t) {
         MM::mma(kk[t], rowk[kgi][GT::tj[t]], rowk[kgi][GT::ti[t]]);
-        MM::mma(qk[t], rowk[kgi][GT::tj[t]], rowq[kgi][GT::ti[t]]);
+        if constexpr (PROD_P) MM::mma(qk[t], rowk[kgi][GT::tj[t]], rowq[kgi][GT::ti[t]]);
       }
     // lane holds X[i = 16ti + lr][j = 16tj + 4lg + s] of both products
 #pragma unroll
@@ -516,7 +525,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
           // exp(G_i - G_j) is formed only on and below the diagonal: exp2(-inf) = 0 above it
           const float d = __builtin_amdgcn_exp2f(j <= i ? Gi - Gj[s4] : -__builtin_inff());
           akeep[t][s4] = j < i ? bi * d * kk[t][s4] : 0.f;
-          pkeep[t][s4] = d * qk[t][s4];
+          if constexpr (PROD_P) pkeep[t][s4] = d * qk[t][s4];
         }
         if (GT::ti[t] == GT::tj[t]) {
 #pragma unroll
@@ -534,16 +543,17 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
     }
   };
 
-  // P and -A into their (single) buffers; each producer wave inverts one of
-  // the four diagonal blocks of I + A.
+  // P (without output waves) and -A into their (single) buffers; each
+  // producer wave inverts one of the four diagonal blocks of I + A.
   auto put = [&](auto wtag) __attribute__((always_inline)) {
     using GT = GramTiles<decltype(wtag)::value>;
     T* sPf = reinterpret_cast<T*>(smem + L::oPf);
     T* sAnf = reinterpret_cast<T*>(smem + L::oAnf);
 #pragma unroll
     for (int t = 0; t < GT::n; ++t) {
-      *reinterpret_cast<V4*>(sPf + L::pf(GT::ti[t], GT::tj[t], lane)) =
-          pack4<T>(pkeep[t][0], pkeep[t][1], pkeep[t][2], pkeep[t][3]);
+      if constexpr (PROD_P)
+        *reinterpret_cast<V4*>(sPf + L::pf(GT::ti[t], GT::tj[t], lane)) =
+            pack4<T>(pkeep[t][0], pkeep[t][1], pkeep[t][2], pkeep[t][3]);
       if (GT::ti[t] != GT::tj[t])
         *reinterpret_cast<V4*>(sAnf + L::anf(GT::ti[t], GT::tj[t], lane)) =
             pack4<T>(-akeep[t][0], -akeep[t][1], -akeep[t][2], -akeep[t][3]);
@@ -614,9 +624,9 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
     }
   };
   floatx4 Ot[4][NTW];  // O^T by 16-token tile: lane holds O[16ct + lr][wcol + 16j + 4lg + s]
-  auto q_times_state = [&](const T* sQ, const float* vec, int r0 = 0, int r1 = 4) __attribute__((always_inline)) {
+  auto q_times_state = [&](const T* sQ, const float* vec) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = r0; r < r1; ++r) {
+    for (int r = 0; r < 4; ++r) {
 #pragma unroll
       for (int j = 0; j < NTW; ++j) Ot[r][j] = zero4();
 #pragma unroll
@@ -838,18 +848,49 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
     if constexpr (OUTW) state_operands();  // the next chunk's state operands, for both waves
   };
 
-  // Output wavefronts: the state part of O^T over segments 1 and 2 (token
-  // tiles 0-1, then 2-3) and U^T P^T with the store in segment 3, from the
-  // operands their consumer wave leaves in LDS.  Spreading the state part
-  // over two segments keeps their LDS reads from crowding the start of
-  // segment 1, where the producers' inverses are on the critical path.
-  auto outw_qm = [&](int s, int r0, int r1) __attribute__((always_inline)) {
-    if (r0 == 0) {
+  // Output wavefronts.  Segment 1: the state part of O^T, from the state
+  // operands their consumer wave leaves in LDS.  Segment 2: P, masked with
+  // the decay, five tiles per output wave, into the fragment-order buffer.
+  // Segment 3: U^T P^T and the store.
+  auto outw_qm = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kgi = 0; kgi < KGK; ++kgi) mfr[kgi][0] = sMx[kgi * 64 + lane];
+    for (int kgi = 0; kgi < KGK; ++kgi) mfr[kgi][0] = sMx[kgi * 64 + lane];
+    q_times_state(reinterpret_cast<const T*>(stage(s) + L::sQ), reinterpret_cast<const float*>(stage(s) + L::sVec));
+  };
+  auto outw_p = [&](auto wtag, int s) __attribute__((always_inline)) {
+    using PT = OutPTiles<decltype(wtag)::value>;
+    const unsigned char* S = stage(s);
+    const T* sK = reinterpret_cast<const T*>(S + L::sK);
+    const T* sQ = reinterpret_cast<const T*>(S + L::sQ);
+    const float* gl = reinterpret_cast<const float*>(S + L::sVec) + 4 * C;  // G log2(e)
+    T* sPf = reinterpret_cast<T*>(smem + L::oPf);
+    floatx4 pt[5];  // lane holds P[16ti + lr][16tj + 4lg + s]
+#pragma unroll
+    for (int t = 0; t < 5; ++t) pt[t] = zero4();
+#pragma unroll
+    for (int kgi = 0; kgi < KGK; ++kgi) {
+      frag kf[4], qf[4];  // only the rows used are read
+#pragma unroll
+      for (int t = 0; t < 5; ++t) {
+        kf[PT::tj[t]] = lds_frag(sK + (16 * PT::tj[t] + lr) * LDK, kgi, lane);
+        qf[PT::ti[t]] = lds_frag(sQ + (16 * PT::ti[t] + lr) * LDK, kgi, lane);
+      }
+#pragma unroll
+      for (int t = 0; t < 5; ++t) MM::mma(pt[t], kf[PT::tj[t]], qf[PT::ti[t]]);
     }
-    q_times_state(reinterpret_cast<const T*>(stage(s) + L::sQ), reinterpret_cast<const float*>(stage(s) + L::sVec),
-                  r0, r1);
+#pragma unroll
+    for (int t = 0; t < 5; ++t) {
+      const int i = 16 * PT::ti[t] + lr;
+      const float Gi = gl[i];
+      const floatx4 Gj = *reinterpret_cast<const floatx4*>(gl + 16 * PT::tj[t] + 4 * lg);
+      floatx4 pv;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int j = 16 * PT::tj[t] + 4 * lg + s4;
+        pv[s4] = pt[t][s4] * __builtin_amdgcn_exp2f(j <= i ? Gi - Gj[s4] : -__builtin_inff());
+      }
+      *reinterpret_cast<V4*>(sPf + L::pf(PT::ti[t], PT::tj[t], lane)) = pack4<T>(pv[0], pv[1], pv[2], pv[3]);
+    }
   };
 
   // ------------------------------------------------------------ schedule
@@ -863,8 +904,8 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
   //   seg 3    Gram products of chunk c + 1           state update
   // With output wavefronts the consumers hand the state (after the update in
   // segment 3, for the next chunk) and U (segment 2) to them as bf16 operands,
-  // and they form O^T: the state part in segments 1 and 2, U^T P^T and the
-  // store in segment 3.
+  // and they form O^T: the state part in segment 1, P in segment 2 (instead
+  // of the producers), U^T P^T and the store in segment 3.
   // Issue priority: consumers (the recurrence) over producers over output
   // waves; with output waves the producers' segment-1 work goes first.
   if (producer) {
@@ -910,9 +951,12 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
         lds_barrier();
       }
       for (int c = 0; c < nch; ++c) {
-        outw_qm(c & 1, 0, 2);
+        outw_qm(c & 1);
         lds_barrier();
-        outw_qm(c & 1, 2, 4);
+        if constexpr (NCW == 2) {
+          if (wave == NP + NCW) outw_p(std::integral_constant<int, 0>(), c & 1);
+          else outw_p(std::integral_constant<int, 1>(), c & 1);
+        }
         lds_barrier();
         out_pu(c, c & 1, sUx);
         lds_barrier();
@@ -996,7 +1040,9 @@ hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
 // whole 128-column state rows per workgroup (four consumer wavefronts of two
 // 16-column tiles each); with fewer, narrower slices: more workgroups, each
 // redoing the chunk-local work but with fewer consumer wavefronts sharing its
-// compute unit, which shortens the time per chunk.
+// compute unit, which shortens the time per chunk.  (Narrower slices than 32
+// columns do not shorten it further: with fewer units than compute units the
+// time is still the chunk count times the same time per chunk.)
 int slice_config(int units, int dv) {
   if (dv == 64) return units >= 128 ? 64 : 32;
   if (units >= 256) return 128;

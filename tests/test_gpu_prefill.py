@@ -78,13 +78,15 @@ def test_small_shapes(gdn, dtype, B, T, Hqk, Hv, d, init):
 
 
 @pytest.mark.parametrize("B,T,Hqk,Hv,d", [
-    (8, 130, 8, 16, 128),    # 128 (sequence, head) units
-    (16, 70, 8, 16, 128),    # 256 units
-    (8, 100, 4, 16, 64),     # 128 units, dk = dv = 64
+    (3, 150, 8, 16, 128),    # 48 (sequence, head) units: 32-wide slices
+    (8, 130, 8, 16, 128),    # 128 units: 64-wide
+    (16, 70, 8, 16, 128),    # 256 units: whole rows
+    (8, 100, 4, 16, 64),     # 128 units, dk = dv = 64: whole rows
 ])
 def test_unit_counts_of_every_slice_width(gdn, B, T, Hqk, Hv, d):
     """The kernel splits the state columns into 32, 64 or 128-wide slices depending on how many
-    (sequence, head) units there are; the small shapes above take the narrowest, these the others."""
+    (sequence, head) units there are; the small shapes above take the narrowest, these the
+    others (and a ragged last chunk in each)."""
     flush(f"prefill units={B * Hv} B={B} T={T} Hqk={Hqk} Hv={Hv} d={d}")
     inp = make_prefill(B, T, Hqk, Hv, d, d, "bf16", init_state=True, seed=B * 100 + T)
     check_against_oracle(gdn, inp, "bf16", scale=1.1)
