@@ -13,8 +13,10 @@ The same JSON line also carries
                 heads (512 MiB fp32 state): algorithmic GB/s against 8 TB/s;
   cpu_baseline  the fp64 oracle on the host cores over the same workload.
 Inputs are seeded synthetic tensors (linear_attention_token_chunked_amd.inputs).
+Every timed loop starts after W untimed steps and at least --warm-seconds of
+untimed load, so that it sees the GPU at its steady clocks.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--all]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--warm-seconds S] [--no-cpu-baseline] [--all]
 """
 
 from __future__ import annotations
@@ -116,11 +118,22 @@ def cpu_baseline(inp, workers):
 
 
 # ------------------------------------------------------------------ GPU timing
+WARM_SECONDS = 1.0  # set from --warm-seconds
+
+
 def time_launches(fn, steps, warmup, torch):
-    """Run fn() warmup times, then time exactly `steps` calls: wall clock around the whole
-    loop (synchronised on both sides) and HIP events around every launch on the current stream."""
-    for _ in range(warmup):
+    """Run fn() warmup times, and on for at least WARM_SECONDS of wall time in all, then time
+    exactly `steps` calls: wall clock around the whole loop (synchronised on both sides) and HIP
+    events around every launch on the current stream.  The GPU raises its clocks only after
+    some hundreds of milliseconds of sustained load; without the timed warm-up the first
+    launches of a fresh process run up to 15 % slower than the steady state."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < WARM_SECONDS:
         fn()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
@@ -204,6 +217,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warm-seconds", type=float, default=1.0,
+                    help="keep warming up (untimed) for at least this long per workload")
     ap.add_argument("--workload", default="prefill_b4_t4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -211,6 +226,8 @@ def main():
     ap.add_argument("--pmc-calib-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
+    global WARM_SECONDS
+    WARM_SECONDS = args.warm_seconds
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the mixer needs no cross-GPU exchange and this build has no "

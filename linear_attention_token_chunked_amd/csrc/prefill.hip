@@ -206,6 +206,35 @@ __device__ __forceinline__ typename Mma<T>::frag chain_frag(F tile, int kg) {
   }
 }
 
+// Per-token gate vectors of a chunk, C floats each, in this order.
+enum { VEC_EG, VEC_BETA, VEC_EGC_G, VEC_EGC, VEC_GL, VEC_E0, VEC_N = VEC_E0 + 3 };
+
+// Decay factors exp(G_i - G_j) (j <= i, else 0) of the 16x16 tile (ti, tj) of a
+// chunk, for the accumulator layout that gives the lane i = 16ti + lr and
+// j = 16tj + 4lg + s.  Below the diagonal blocks they are products of two
+// factors no larger than one that the gate scan stores, exp(G_i - G_r) and
+// exp(G_r - G_j) with r the last token of tile tj (G is non-increasing);
+// on a diagonal block they are formed directly.
+__device__ __forceinline__ floatx4 decay_tile(const float* vec, int ti, int tj, int lg, int lr) {
+  const int i = 16 * ti + lr;
+  floatx4 d;
+  if (ti > tj) {
+    const float* e = vec + (VEC_E0 + tj) * C;
+    const floatx4 ej = *reinterpret_cast<const floatx4*>(e + 16 * tj + 4 * lg);
+    d = ej * e[i];
+  } else {
+    const float* gl = vec + VEC_GL * C;
+    const float Gi = gl[i];
+    const floatx4 Gj = *reinterpret_cast<const floatx4*>(gl + 16 * tj + 4 * lg);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int j = 16 * tj + 4 * lg + s4;
+      d[s4] = __builtin_amdgcn_exp2f(j <= i ? Gi - Gj[s4] : -__builtin_inff());  // exp2(-inf) = 0
+    }
+  }
+  return d;
+}
+
 // LDS layout.  K and Q rows are padded against bank conflicts (see LDK).
 template <class T, int DK, int BV, int NSTAGE, int NCW, bool OUTW>
 struct Layout {
@@ -227,9 +256,10 @@ struct Layout {
   static constexpr size_t sQ = sK + sizeof(T) * C * LDK;
   static constexpr size_t sV = sQ + sizeof(T) * C * LDK;
   static constexpr size_t sKn = sV + sizeof(T) * C * LDV;   // [C][DK] K, column-read copy (bf16)
-  // per-token vectors: exp G, beta, exp(G_C - G), exp G_C (uniform), G log2(e)
+  // per-token vectors (VEC_*): exp G, beta, exp(G_C - G), exp G_C (uniform),
+  // G log2(e), and the decay to or from the last token of 16-token tiles 0-2
   static constexpr size_t sVec = sKn + (KNAT ? sizeof(T) * C * DK : 0);
-  static constexpr size_t stage_bytes = (sVec + 5 * 4 * C + 15) / 16 * 16;
+  static constexpr size_t stage_bytes = (sVec + VEC_N * 4 * C + 15) / 16 * 16;
   // Single-buffered, written by the producers in segment 1 after the
   // consumers have read the previous chunk's copy in segment 2.  All three
   // are kept in "fragment order": the 16 (or 8) bytes one lane contributes to
@@ -467,11 +497,16 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
       const float Gl = wave_inclusive_sum(live ? pre.g : 0.f) * kLog2e;
       const float GlC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, Gl), 63));
       float* vec = reinterpret_cast<float*>(S + L::sVec);
-      vec[lane] = __builtin_amdgcn_exp2f(Gl);
-      vec[C + lane] = bt;
-      vec[2 * C + lane] = __builtin_amdgcn_exp2f(GlC - Gl);
-      vec[3 * C + lane] = __builtin_amdgcn_exp2f(GlC);
-      vec[4 * C + lane] = Gl;
+      vec[VEC_EG * C + lane] = __builtin_amdgcn_exp2f(Gl);
+      vec[VEC_BETA * C + lane] = bt;
+      vec[VEC_EGC_G * C + lane] = __builtin_amdgcn_exp2f(GlC - Gl);
+      vec[VEC_EGC * C + lane] = __builtin_amdgcn_exp2f(GlC);
+      vec[VEC_GL * C + lane] = Gl;
+#pragma unroll
+      for (int b = 0; b < 3; ++b) {  // exp(-|G - G_r|), r = 16b + 15
+        const float Gr = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, Gl), 16 * b + 15));
+        vec[(VEC_E0 + b) * C + lane] = __builtin_amdgcn_exp2f(lane <= 16 * b + 15 ? Gr - Gl : Gl - Gr);
+      }
     }
     if (c + 1 < nch) issue_loads(c + 1);
   };
@@ -487,8 +522,8 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
     const unsigned char* S = stage(s);
     const T* sK = reinterpret_cast<const T*>(S + L::sK);
     const T* sQ = reinterpret_cast<const T*>(S + L::sQ);
-    const float* beta = reinterpret_cast<const float*>(S + L::sVec) + C;
-    const float* sGl = beta + 3 * C;  // G log2(e)
+    const float* vec = reinterpret_cast<const float*>(S + L::sVec);
+    const float* beta = vec + VEC_BETA * C;
     floatx4 kk[3], qk[3];
 #pragma unroll
     for (int t = 0; t < 3; ++t) kk[t] = qk[t] = zero4();
@@ -517,13 +552,12 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
       pkeep[t] = akeep[t] = zero4();
       if (t < GT::n) {
         const int i = 16 * GT::ti[t] + lr;
-        const float Gi = sGl[i], bi = beta[i];
-        const floatx4 Gj = *reinterpret_cast<const floatx4*>(sGl + 16 * GT::tj[t] + 4 * lg);
+        const float bi = beta[i];
+        const floatx4 dd = decay_tile(vec, GT::ti[t], GT::tj[t], lg, lr);
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
           const int j = 16 * GT::tj[t] + 4 * lg + s4;
-          // exp(G_i - G_j) is formed only on and below the diagonal: exp2(-inf) = 0 above it
-          const float d = __builtin_amdgcn_exp2f(j <= i ? Gi - Gj[s4] : -__builtin_inff());
+          const float d = dd[s4];
           akeep[t][s4] = j < i ? bi * d * kk[t][s4] : 0.f;
           if constexpr (PROD_P) pkeep[t][s4] = d * qk[t][s4];
         }
@@ -635,7 +669,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
 #pragma unroll
         for (int j = 0; j < NTW; ++j) MM::mma(Ot[r][j], mfr[kgi][j], qf);
       }
-      const float egt = vec[16 * r + lr];  // exp(G) of the token this lane holds in O^T
+      const float egt = vec[VEC_EG * C + 16 * r + lr];  // exp(G) of the token this lane holds in O^T
 #pragma unroll
       for (int j = 0; j < NTW; ++j) Ot[r][j] *= egt;
     }
@@ -666,8 +700,8 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
       float eg[4], bt[4];
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
-        eg[s4] = vec[16 * r + 4 * lg + s4];
-        bt[s4] = vec[C + 16 * r + 4 * lg + s4];
+        eg[s4] = vec[VEC_EG * C + 16 * r + 4 * lg + s4];
+        bt[s4] = vec[VEC_BETA * C + 16 * r + 4 * lg + s4];
       }
 #pragma unroll
       for (int j = 0; j < NTW; ++j) {
@@ -813,12 +847,12 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
     const T* sK = reinterpret_cast<const T*>(S + L::sK);
     const T* sKn = reinterpret_cast<const T*>(S + L::sKn);
     const float* vec = reinterpret_cast<const float*>(S + L::sVec);
-    const float eGC = vec[3 * C];
+    const float eGC = vec[VEC_EGC * C];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
-        const float f = vec[2 * C + 16 * r + 4 * lg + s4];
+        const float f = vec[VEC_EGC_G * C + 16 * r + 4 * lg + s4];
 #pragma unroll
         for (int j = 0; j < NTW; ++j) Z[r][j][s4] *= f;
       }
@@ -862,33 +896,26 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
     const unsigned char* S = stage(s);
     const T* sK = reinterpret_cast<const T*>(S + L::sK);
     const T* sQ = reinterpret_cast<const T*>(S + L::sQ);
-    const float* gl = reinterpret_cast<const float*>(S + L::sVec) + 4 * C;  // G log2(e)
+    const float* vec = reinterpret_cast<const float*>(S + L::sVec);
     T* sPf = reinterpret_cast<T*>(smem + L::oPf);
     floatx4 pt[5];  // lane holds P[16ti + lr][16tj + 4lg + s]
 #pragma unroll
     for (int t = 0; t < 5; ++t) pt[t] = zero4();
+    frag kf[KGK][4], qf[KGK][4];  // only the rows used are read, all before the first product
 #pragma unroll
-    for (int kgi = 0; kgi < KGK; ++kgi) {
-      frag kf[4], qf[4];  // only the rows used are read
+    for (int kgi = 0; kgi < KGK; ++kgi)
 #pragma unroll
       for (int t = 0; t < 5; ++t) {
-        kf[PT::tj[t]] = lds_frag(sK + (16 * PT::tj[t] + lr) * LDK, kgi, lane);
-        qf[PT::ti[t]] = lds_frag(sQ + (16 * PT::ti[t] + lr) * LDK, kgi, lane);
+        kf[kgi][PT::tj[t]] = lds_frag(sK + (16 * PT::tj[t] + lr) * LDK, kgi, lane);
+        qf[kgi][PT::ti[t]] = lds_frag(sQ + (16 * PT::ti[t] + lr) * LDK, kgi, lane);
       }
 #pragma unroll
-      for (int t = 0; t < 5; ++t) MM::mma(pt[t], kf[PT::tj[t]], qf[PT::ti[t]]);
-    }
+    for (int kgi = 0; kgi < KGK; ++kgi)
+#pragma unroll
+      for (int t = 0; t < 5; ++t) MM::mma(pt[t], kf[kgi][PT::tj[t]], qf[kgi][PT::ti[t]]);
 #pragma unroll
     for (int t = 0; t < 5; ++t) {
-      const int i = 16 * PT::ti[t] + lr;
-      const float Gi = gl[i];
-      const floatx4 Gj = *reinterpret_cast<const floatx4*>(gl + 16 * PT::tj[t] + 4 * lg);
-      floatx4 pv;
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const int j = 16 * PT::tj[t] + 4 * lg + s4;
-        pv[s4] = pt[t][s4] * __builtin_amdgcn_exp2f(j <= i ? Gi - Gj[s4] : -__builtin_inff());
-      }
+      const floatx4 pv = pt[t] * decay_tile(vec, PT::ti[t], PT::tj[t], lg, lr);
       *reinterpret_cast<V4*>(sPf + L::pf(PT::ti[t], PT::tj[t], lane)) = pack4<T>(pv[0], pv[1], pv[2], pv[3]);
     }
   };
