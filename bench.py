@@ -7,8 +7,8 @@ B=4, T=4096, 16 heads, dk=dv=128, bf16 in, fp32 state ("prefill_b4_t4096").
 ``value`` is that prefill's throughput in Mtok/s with inputs resident in HBM.
 The same JSON line also carries
   roofline      the prefill kernel's achieved algorithmic TFLOP/s against the
-                2.5 PFLOP/s dense bf16 matrix-core peak, timed per launch with
-                HIP events on the launch stream;
+                2.5 PFLOP/s dense bf16 matrix-core peak, timed with HIP events
+                on the launch stream around the K back-to-back launches;
   decode        64 consecutive gdn_decode_step calls on 256 sequences x 32 value
                 heads (512 MiB fp32 state): algorithmic GB/s against 8 TB/s;
   cpu_baseline  the fp64 oracle on the host cores over the same workload.
@@ -123,10 +123,14 @@ WARM_SECONDS = 1.0  # set from --warm-seconds
 
 def time_launches(fn, steps, warmup, torch):
     """Run fn() warmup times, and on for at least WARM_SECONDS of wall time in all, then time
-    exactly `steps` calls: wall clock around the whole loop (synchronised on both sides) and HIP
-    events around every launch on the current stream.  The GPU raises its clocks only after
-    some hundreds of milliseconds of sustained load; without the timed warm-up the first
-    launches of a fresh process run up to 15 % slower than the steady state."""
+    exactly `steps` calls back to back: wall clock around the whole loop (synchronised on both
+    sides) and one pair of HIP events on the launch stream around it.  Returns the wall time
+    (s), the event time per launch (ms) and, from a second loop of `steps` calls with events
+    around every launch, the sorted per-launch times (ms).  (Events between launches cost the
+    stream a few microseconds each, so the first loop has none.)
+    The GPU raises its clocks only after some hundreds of milliseconds of sustained load;
+    without the timed warm-up the first launches of a fresh process run up to 15 % slower
+    than the steady state."""
     t0 = time.perf_counter()
     n = 0
     while n < warmup or time.perf_counter() - t0 < WARM_SECONDS:
@@ -135,16 +139,23 @@ def time_launches(fn, steps, warmup, torch):
         if n % 16 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mean_ms = e0.elapsed_time(e1) / steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, b in evs:
         a.record()
         fn()
         b.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = sorted(a.elapsed_time(b) for a, b in evs)  # ms
-    return wall, per
+    per = sorted(a.elapsed_time(b) for a, b in evs)
+    return wall, mean_ms, per
 
 
 def bench_prefill(name, gdn, torch, steps, warmup):
@@ -168,9 +179,8 @@ def bench_prefill(name, gdn, torch, steps, warmup):
     step()
     torch.cuda.synchronize()
     cold_ms = (time.perf_counter() - c0) * 1e3
-    wall, per = time_launches(step, steps, warmup, torch)
+    wall, kern_ms, per = time_launches(step, steps, warmup, torch)
     tokens = B * T
-    kern_ms = sum(per) / len(per)
     flops = prefill_flops_per_token(Hqk, Hv, dk, dv, w.chunk) * tokens
     nbytes = prefill_bytes(tokens, N, Hqk, Hv, dk, dv, dev["q"].element_size(), dev["initial_state"] is not None,
                            True)
@@ -198,8 +208,8 @@ def bench_decode(gdn, torch, warmup_rounds=1):
         gdn.decode_step(dev["q"][t], dev["k"][t], dev["v"][t], dev["g"][t], dev["beta"][t], state, out=o)
         it["t"] += 1
 
-    wall, per = time_launches(step, w.steps, warmup_rounds * w.steps, torch)
-    us = sum(per) / len(per) * 1e3
+    wall, mean_ms, per = time_launches(step, w.steps, warmup_rounds * w.steps, torch)
+    us = mean_ms * 1e3
     nbytes = decode_bytes(w.N, w.Hqk, w.Hv, w.dk, w.dv, dev["q"].element_size())
     gbps = nbytes / (us * 1e-6) / 1e9
     traffic = measured_traffic("decode", w.name)
