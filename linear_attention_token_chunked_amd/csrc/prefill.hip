@@ -404,16 +404,20 @@ struct ChunkRegs {
 // and get the lighter shares:
 //   wave 0: (3,0) (3,1) (3,2)    wave 1: (2,0) (2,1)
 //   wave 2: (1,0) (1,1) (2,2)    wave 3: (0,0) (3,3)
+// Every tile gives A; P comes from Q K^T of the same tiles, except with two
+// output waves, which form P themselves but for the tiles in pmask (bit t:
+// tile t), which waves 1 and 3 have room for.
 template <int W> struct GramTiles;
-template <> struct GramTiles<0> { static constexpr int n = 3, ti[3] = {3, 3, 3}, tj[3] = {0, 1, 2}; };
-template <> struct GramTiles<1> { static constexpr int n = 2, ti[3] = {2, 2, 0}, tj[3] = {0, 1, 0}; };
-template <> struct GramTiles<2> { static constexpr int n = 3, ti[3] = {1, 1, 2}, tj[3] = {0, 1, 2}; };
-template <> struct GramTiles<3> { static constexpr int n = 2, ti[3] = {0, 3, 0}, tj[3] = {0, 3, 0}; };
+template <> struct GramTiles<0> { static constexpr int n = 3, ti[3] = {3, 3, 3}, tj[3] = {0, 1, 2}, pmask = 0; };
+template <> struct GramTiles<1> { static constexpr int n = 2, ti[3] = {2, 2, 0}, tj[3] = {0, 1, 0}, pmask = 1; };
+template <> struct GramTiles<2> { static constexpr int n = 3, ti[3] = {1, 1, 2}, tj[3] = {0, 1, 2}, pmask = 0; };
+template <> struct GramTiles<3> { static constexpr int n = 2, ti[3] = {0, 3, 0}, tj[3] = {0, 3, 0}, pmask = 2; };
 
-// P tiles (ti >= tj) formed by output wave W (with output waves only).
+// P tiles (ti >= tj) formed by output wave W (with two output waves only):
+// the eight the producers leave.
 template <int W> struct OutPTiles;
-template <> struct OutPTiles<0> { static constexpr int ti[5] = {0, 1, 1, 2, 3}, tj[5] = {0, 0, 1, 0, 0}; };
-template <> struct OutPTiles<1> { static constexpr int ti[5] = {2, 2, 3, 3, 3}, tj[5] = {1, 2, 1, 2, 3}; };
+template <> struct OutPTiles<0> { static constexpr int n = 4, ti[4] = {0, 1, 1, 3}, tj[4] = {0, 0, 1, 0}; };
+template <> struct OutPTiles<1> { static constexpr int n = 4, ti[4] = {2, 2, 3, 3}, tj[4] = {1, 2, 1, 2}; };
 
 template <class T, int DK, int DV, int BV, int NSTAGE, int NCW, bool OUTW>
 __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kernel(Params p) {
@@ -515,7 +519,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
   // masked with the decay.  The diagonal blocks of A go to LDS transposed
   // (fp32, for the inverses); -A below the diagonal and P stay in registers
   // until prod_finish.
-  constexpr bool PROD_P = !(OUTW && NCW == 2);  // two output waves form P themselves
+  constexpr bool PROD_P = !(OUTW && NCW == 2);  // two output waves form most of P themselves
   floatx4 pkeep[3], akeep[3];
   auto gram = [&](auto wtag, int s) __attribute__((always_inline)) {
     using GT = GramTiles<decltype(wtag)::value>;
@@ -536,7 +540,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
 #pragma unroll
       for (int t = 0; t < GT::n; ++t) {
         rowk[kgi][GT::ti[t]] = lds_frag(sK + (16 * GT::ti[t] + lr) * LDK, kgi, lane);
-        if constexpr (PROD_P) rowq[kgi][GT::ti[t]] = lds_frag(sQ + (16 * GT::ti[t] + lr) * LDK, kgi, lane);
+        if (PROD_P || (GT::pmask >> t & 1)) rowq[kgi][GT::ti[t]] = lds_frag(sQ + (16 * GT::ti[t] + lr) * LDK, kgi, lane);
         rowk[kgi][GT::tj[t]] = lds_frag(sK + (16 * GT::tj[t] + lr) * LDK, kgi, lane);
       }
 #pragma unroll
@@ -544,7 +548,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
 #pragma unroll
       for (int t = 0; t < GT::n; ++t) {
         MM::mma(kk[t], rowk[kgi][GT::tj[t]], rowk[kgi][GT::ti[t]]);
-        if constexpr (PROD_P) MM::mma(qk[t], rowk[kgi][GT::tj[t]], rowq[kgi][GT::ti[t]]);
+        if (PROD_P || (GT::pmask >> t & 1)) MM::mma(qk[t], rowk[kgi][GT::tj[t]], rowq[kgi][GT::ti[t]]);
       }
     // lane holds X[i = 16ti + lr][j = 16tj + 4lg + s] of both products
 #pragma unroll
@@ -559,7 +563,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
           const int j = 16 * GT::tj[t] + 4 * lg + s4;
           const float d = dd[s4];
           akeep[t][s4] = j < i ? bi * d * kk[t][s4] : 0.f;
-          if constexpr (PROD_P) pkeep[t][s4] = d * qk[t][s4];
+          if (PROD_P || (GT::pmask >> t & 1)) pkeep[t][s4] = d * qk[t][s4];
         }
         if (GT::ti[t] == GT::tj[t]) {
 #pragma unroll
@@ -585,7 +589,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
     T* sAnf = reinterpret_cast<T*>(smem + L::oAnf);
 #pragma unroll
     for (int t = 0; t < GT::n; ++t) {
-      if constexpr (PROD_P)
+      if (PROD_P || (GT::pmask >> t & 1))
         *reinterpret_cast<V4*>(sPf + L::pf(GT::ti[t], GT::tj[t], lane)) =
             pack4<T>(pkeep[t][0], pkeep[t][1], pkeep[t][2], pkeep[t][3]);
       if (GT::ti[t] != GT::tj[t])
@@ -884,7 +888,8 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
 
   // Output wavefronts.  Segment 1: the state part of O^T, from the state
   // operands their consumer wave leaves in LDS.  Segment 2: P, masked with
-  // the decay, five tiles per output wave, into the fragment-order buffer.
+  // the decay, four tiles per output wave (the producers form the other two),
+  // into the fragment-order buffer.
   // Segment 3: U^T P^T and the store.
   auto outw_qm = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
@@ -898,23 +903,23 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
     const T* sQ = reinterpret_cast<const T*>(S + L::sQ);
     const float* vec = reinterpret_cast<const float*>(S + L::sVec);
     T* sPf = reinterpret_cast<T*>(smem + L::oPf);
-    floatx4 pt[5];  // lane holds P[16ti + lr][16tj + 4lg + s]
+    floatx4 pt[PT::n];  // lane holds P[16ti + lr][16tj + 4lg + s]
 #pragma unroll
-    for (int t = 0; t < 5; ++t) pt[t] = zero4();
+    for (int t = 0; t < PT::n; ++t) pt[t] = zero4();
     frag kf[KGK][4], qf[KGK][4];  // only the rows used are read, all before the first product
 #pragma unroll
     for (int kgi = 0; kgi < KGK; ++kgi)
 #pragma unroll
-      for (int t = 0; t < 5; ++t) {
+      for (int t = 0; t < PT::n; ++t) {
         kf[kgi][PT::tj[t]] = lds_frag(sK + (16 * PT::tj[t] + lr) * LDK, kgi, lane);
         qf[kgi][PT::ti[t]] = lds_frag(sQ + (16 * PT::ti[t] + lr) * LDK, kgi, lane);
       }
 #pragma unroll
     for (int kgi = 0; kgi < KGK; ++kgi)
 #pragma unroll
-      for (int t = 0; t < 5; ++t) MM::mma(pt[t], kf[kgi][PT::tj[t]], qf[kgi][PT::ti[t]]);
+      for (int t = 0; t < PT::n; ++t) MM::mma(pt[t], kf[kgi][PT::tj[t]], qf[kgi][PT::ti[t]]);
 #pragma unroll
-    for (int t = 0; t < 5; ++t) {
+    for (int t = 0; t < PT::n; ++t) {
       const floatx4 pv = pt[t] * decay_tile(vec, PT::ti[t], PT::tj[t], lg, lr);
       *reinterpret_cast<V4*>(sPf + L::pf(PT::ti[t], PT::tj[t], lane)) = pack4<T>(pv[0], pv[1], pv[2], pv[3]);
     }
@@ -931,8 +936,8 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
   //   seg 3    Gram products of chunk c + 1           state update
   // With output wavefronts the consumers hand the state (after the update in
   // segment 3, for the next chunk) and U (segment 2) to them as bf16 operands,
-  // and they form O^T: the state part in segment 1, P in segment 2 (instead
-  // of the producers), U^T P^T and the store in segment 3.
+  // and they form O^T: the state part in segment 1, P in segment 2 (all but
+  // two tiles, which the producers form), U^T P^T and the store in segment 3.
   // Issue priority: consumers (the recurrence) over producers over output
   // waves; with output waves the producers' segment-1 work goes first.
   if (producer) {
