@@ -11,6 +11,8 @@ The same JSON line also carries
                 on the launch stream around the K back-to-back launches;
   decode        64 consecutive gdn_decode_step calls on 256 sequences x 32 value
                 heads (512 MiB fp32 state): algorithmic GB/s against 8 TB/s;
+  verify        gdn_decode_verify, 4 drafted tokens per sequence from the same
+                kind of live state: algorithmic GB/s against 8 TB/s;
   cpu_baseline  the fp64 oracle on the host cores over the same workload.
 Inputs are seeded synthetic tensors (linear_attention_token_chunked_amd.inputs).
 Every timed loop starts after W untimed steps and at least --warm-seconds of
@@ -58,6 +60,11 @@ def prefill_bytes(tokens, N, Hqk, Hv, dk, dv, s_in, has_initial, has_final):
 def decode_bytes(N, Hqk, Hv, dk, dv, s_in):
     """Per step: the fp32 state read and written, q, k, v read and o written, g and beta read."""
     return N * Hv * dk * dv * 4 * 2 + N * (2 * Hqk * dk + 2 * Hv * dv) * s_in + N * Hv * 8
+
+
+def verify_bytes(N, Tv, Hqk, Hv, dk, dv, s_in):
+    """Per call: the fp32 state read and written once, and Tv tokens' q, k, v, o, g, beta."""
+    return N * Hv * dk * dv * 4 * 2 + Tv * (N * (2 * Hqk * dk + 2 * Hv * dv) * s_in + N * Hv * 8)
 
 
 def source_hash(path):
@@ -222,6 +229,32 @@ def bench_decode(gdn, torch, warmup_rounds=1):
     }
 
 
+def bench_verify(gdn, torch, steps=20):
+    """Multi-token verify (Tv drafted tokens per sequence from a live state), state updated in place."""
+    from linear_attention_token_chunked_amd.inputs import WORKLOADS, make_workload
+
+    w = WORKLOADS["verify_n256_t4"]
+    inp = make_workload(w)
+    dev = {k: v.cuda() for k, v in inp.items()}
+    state = dev["state"].clone()
+    o = torch.empty((w.N, w.steps, w.Hv, w.dv), dtype=dev["q"].dtype, device="cuda")
+
+    def step():
+        gdn.decode_verify(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], state, out=o)
+
+    wall, mean_ms, per = time_launches(step, steps, 2, torch)
+    us = mean_ms * 1e3
+    nbytes = verify_bytes(w.N, w.steps, w.Hqk, w.Hv, w.dk, w.dv, dev["q"].element_size())
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {
+        "workload": w.name, "N": w.N, "tokens_per_seq": w.steps, "Hqk": w.Hqk, "Hv": w.Hv, "dk": w.dk, "dv": w.dv,
+        "us_per_call_mean": us, "us_per_call_median": per[len(per) // 2] * 1e3,
+        "Mtok_s": w.N * w.steps / (us * 1e-6) / 1e6, "bytes_per_call": nbytes, "GBps": gbps,
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -262,6 +295,7 @@ def main():
     res, _ = bench_prefill(args.workload, gdn, torch, args.steps, args.warmup)
     traffic = measured_traffic("prefill", args.workload)
     dec = None if args.no_decode else bench_decode(gdn, torch)
+    ver = None if args.no_decode else bench_verify(gdn, torch)
     extra = {}
     if args.all:
         for name in ("prefill_t65536_gqa", "varlen_64"):
@@ -294,6 +328,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(res["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "prefill": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in res.items()},
         "decode": dec,
+        "verify": ver,
         "cpu_baseline": cpu,
     }
     if extra:

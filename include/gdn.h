@@ -125,6 +125,33 @@ gdn_status_t gdn_decode_step(const gdn_dims_t* d, const void* q, const void* k, 
                              const float* g, const float* beta, float* state, void* o,
                              hipStream_t stream);
 
+/*
+ * Multi-token verify from a live state, for speculative decoding: the archdiff
+ * model page "Qwen3.8-2.4T-A95B" (components list) drafts tokens with
+ * multi-token-prediction modules and verifies them in the target model.  Runs
+ * Tv consecutive steps of the recurrence above per sequence, each exactly the
+ * step of gdn_decode_step, starting from state_in, in one pass over the state.
+ *
+ *   d->num_seqs = N, d->batch must equal N, d->seqlen = Tv (1..8; NOT_SUPPORTED
+ *   above 8); chunk_size is ignored.
+ *   q, k          [N, Tv, Hqk, dk]      dtype, 16-byte aligned
+ *   v             [N, Tv, Hv, dv]       dtype, 16-byte aligned
+ *   g, beta       [N, Tv, Hv]           fp32
+ *   state_in      [N, Hv, dk, dv]       fp32, 16-byte aligned, read
+ *   state_out     [N, Hv, dk, dv]       fp32, 16-byte aligned: the state after all Tv
+ *                                       tokens, or NULL (not written); may be state_in
+ *   token_states  [N, Tv, Hv, dk, dv]   fp32, 16-byte aligned: the state after each
+ *                                       token, or NULL.  A caller that accepts the first
+ *                                       a tokens continues from token_states[:, a - 1].
+ *   o             [N, Tv, Hv, dv]       dtype, 16-byte aligned; o[:, t] reads the state
+ *                                       after token t
+ * Any overlap of outputs with inputs other than state_out == state_in is undefined.
+ * Supported: dk, dv in {64, 128}, dtype fp32 or bf16.
+ */
+gdn_status_t gdn_decode_verify(const gdn_dims_t* d, const void* q, const void* k, const void* v,
+                               const float* g, const float* beta, const float* state_in,
+                               float* state_out, float* token_states, void* o, hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* gdn_status_string(gdn_status_t s);
 

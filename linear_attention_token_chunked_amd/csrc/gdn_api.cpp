@@ -13,7 +13,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
 
-// Checks shared by both entry points.
+// Checks shared by every entry point.
 gdn_status_t check_common(const gdn_dims_t* d) {
   if (!d) return GDN_STATUS_INVALID_VALUE;
   if (d->num_qk_heads < 1 || d->num_v_heads < 1 || d->head_dim_k < 1 || d->head_dim_v < 1 || d->num_seqs < 0)
@@ -113,6 +113,41 @@ gdn_status_t gdn_decode_step(const gdn_dims_t* d, const void* q, const void* k, 
   a.scale = d->scale;
   a.bf16 = d->dtype == GDN_DTYPE_BFLOAT16;
   return from_hip(gdn::launch_decode(a, stream));
+}
+
+gdn_status_t gdn_decode_verify(const gdn_dims_t* d, const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, const float* state_in, float* state_out, float* token_states,
+                               void* o, hipStream_t stream) {
+  gdn_status_t st = check_common(d);
+  if (st != GDN_STATUS_SUCCESS) return st;
+  if (d->batch != d->num_seqs || d->seqlen < 1) return GDN_STATUS_INVALID_VALUE;
+  if (d->seqlen > gdn::kMaxVerifyTokens) return GDN_STATUS_NOT_SUPPORTED;
+  if (d->num_seqs == 0) return GDN_STATUS_SUCCESS;
+  if (!q || !k || !v || !g || !beta || !state_in || !o) return GDN_STATUS_INVALID_VALUE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(state_in, 16) ||
+      !aligned(state_out, 16) || !aligned(token_states, 16) || !aligned(g, 4) || !aligned(beta, 4))
+    return GDN_STATUS_MISALIGNED;
+  if (static_cast<int64_t>(d->num_seqs) * d->num_v_heads >= (int64_t(1) << 31)) return GDN_STATUS_NOT_SUPPORTED;
+
+  gdn::VerifyArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.state_in = state_in;
+  a.state_out = state_out;
+  a.token_states = token_states;
+  a.o = o;
+  a.num_seqs = d->num_seqs;
+  a.tokens = d->seqlen;
+  a.Hqk = d->num_qk_heads;
+  a.Hv = d->num_v_heads;
+  a.dk = d->head_dim_k;
+  a.dv = d->head_dim_v;
+  a.scale = d->scale;
+  a.bf16 = d->dtype == GDN_DTYPE_BFLOAT16;
+  return from_hip(gdn::launch_verify(a, stream));
 }
 
 const char* gdn_status_string(gdn_status_t s) {

@@ -30,7 +30,23 @@ struct PrefillArgs {
   bool bf16;
 };
 
+// Multi-token verify: Tv (<= kMaxVerifyTokens) consecutive steps per sequence.
+constexpr int kMaxVerifyTokens = 8;
+
+struct VerifyArgs {
+  const void *q, *k, *v;
+  const float *g, *beta;
+  const float* state_in;
+  float* state_out;     // may be null (not written) or state_in
+  float* token_states;  // may be null
+  void* o;
+  int num_seqs, tokens, Hqk, Hv, dk, dv;
+  float scale;
+  bool bf16;
+};
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace gdn

@@ -38,7 +38,8 @@ class Dims(ctypes.Structure):
 
 DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1}
 
-EXPORTED = ("gdn_fwd_chunked_workspace_size", "gdn_fwd_chunked", "gdn_decode_step", "gdn_status_string")
+EXPORTED = ("gdn_fwd_chunked_workspace_size", "gdn_fwd_chunked", "gdn_decode_step", "gdn_decode_verify",
+            "gdn_status_string")
 
 
 def _load():
@@ -53,6 +54,8 @@ def _load():
     lib.gdn_fwd_chunked.restype = ctypes.c_int
     lib.gdn_decode_step.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, fp, fp, fp, vp, vp]
     lib.gdn_decode_step.restype = ctypes.c_int
+    lib.gdn_decode_verify.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, fp, fp, fp, fp, fp, vp, vp]
+    lib.gdn_decode_verify.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     return lib
@@ -182,5 +185,58 @@ def decode_step(q, k, v, g, beta, state, *, scale=1.0, out=None):
     with torch.cuda.device(dev):
         code = lib.gdn_decode_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
                                    _ptr(out), _stream(dev))
+    _check(code)
+    return out
+
+
+def decode_verify(q, k, v, g, beta, state_in, *, state_out="in_place", token_states=None, scale=1.0, out=None):
+    """Tv consecutive decode steps per sequence from ``state_in`` (multi-token verify).
+
+    q, k [N, Tv, Hqk, dk], v [N, Tv, Hv, dv], g, beta [N, Tv, Hv], state_in [N, Hv, dk, dv] fp32.
+    ``state_out``: "in_place" (default: state_in is updated), None (not written) or a tensor.
+    ``token_states``: None, or an fp32 [N, Tv, Hv, dk, dv] tensor that receives the state after
+    every token.  Returns o [N, Tv, Hv, dv].
+    """
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    if q.dtype not in DTYPE_CODE:
+        raise TypeError("q, k, v must be float32 or bfloat16")
+    _need(q, "q", q.dtype, dev, 4)
+    N, Tv, Hqk, dk = q.shape
+    _need(k, "k", q.dtype, dev, 4)
+    _need(v, "v", q.dtype, dev, 4)
+    Hv, dv = v.shape[2], v.shape[3]
+    if k.shape != q.shape or v.shape[:2] != (N, Tv):
+        raise ValueError("q, k, v shapes disagree")
+    _need(g, "g", torch.float32, dev, 3)
+    _need(beta, "beta", torch.float32, dev, 3)
+    if g.shape != (N, Tv, Hv) or beta.shape != (N, Tv, Hv):
+        raise ValueError("g, beta must be [N, Tv, Hv]")
+    _need(state_in, "state_in", torch.float32, dev, 4)
+    if state_in.shape != (N, Hv, dk, dv):
+        raise ValueError("state_in must be [N, Hv, dk, dv]")
+    if isinstance(state_out, str):
+        if state_out != "in_place":
+            raise ValueError('state_out must be "in_place", None or a tensor')
+        state_out = state_in
+    if state_out is not None:
+        _need(state_out, "state_out", torch.float32, dev, 4)
+        if state_out.shape != (N, Hv, dk, dv):
+            raise ValueError("state_out must be [N, Hv, dk, dv]")
+    if token_states is not None:
+        _need(token_states, "token_states", torch.float32, dev, 5)
+        if token_states.shape != (N, Tv, Hv, dk, dv):
+            raise ValueError("token_states must be [N, Tv, Hv, dk, dv]")
+    if out is None:
+        out = torch.empty((N, Tv, Hv, dv), dtype=q.dtype, device=dev)
+    else:
+        _need(out, "out", q.dtype, dev, 4)
+        if out.shape != (N, Tv, Hv, dv):
+            raise ValueError("out must be [N, Tv, Hv, dv]")
+    dims = make_dims(N, Tv, N, Hqk, Hv, dk, dv, 64, scale, q.dtype)
+    with torch.cuda.device(dev):
+        code = lib.gdn_decode_verify(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                     _ptr(state_in), _ptr(state_out), _ptr(token_states), _ptr(out), _stream(dev))
     _check(code)
     return out

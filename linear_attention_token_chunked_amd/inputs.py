@@ -35,7 +35,7 @@ class Workload:
     """Shape of one synthetic workload."""
 
     name: str
-    kind: str  # "prefill" or "decode"
+    kind: str  # "prefill", "decode" or "verify"
     dtype: str  # "fp32" or "bf16" for q, k, v, o
     Hqk: int
     Hv: int
@@ -47,7 +47,7 @@ class Workload:
     init_state: bool = False
     num_packed: int = 0  # > 0: packed variable-length batch of this many sequences
     N: int = 0  # decode: independent sequences
-    steps: int = 0  # decode: consecutive single-token steps
+    steps: int = 0  # decode: consecutive single-token steps; verify: tokens per sequence
 
 
 WORKLOADS = {
@@ -62,6 +62,9 @@ WORKLOADS = {
     # 256 sequences x 32 v heads, 64 single-token steps on a 512 MiB fp32 state
     "decode_n256": Workload("decode_n256", "decode", "bf16", Hqk=16, Hv=32, dk=128, dv=128, N=256, steps=64,
                             init_state=True),
+    # multi-token verify: 256 sequences x 32 v heads, 4 drafted tokens each, from a 512 MiB live state
+    "verify_n256_t4": Workload("verify_n256_t4", "verify", "bf16", Hqk=16, Hv=32, dk=128, dv=128, N=256, steps=4,
+                               init_state=True),
     # 64 packed sequences of lognormal length, per-sequence initial states
     "varlen_64": Workload("varlen_64", "prefill", "bf16", Hqk=16, Hv=32, dk=128, dv=128, num_packed=64,
                           init_state=True),
@@ -140,8 +143,20 @@ def make_decode(N, Hqk, Hv, dk, dv, steps, dtype="bf16", seed=0, gate_scale=0.1)
     }
 
 
+def make_verify(N, Tv, Hqk, Hv, dk, dv, dtype="bf16", seed=0, gate_scale=0.1):
+    """Draw a multi-token verify call: the decode draws of make_decode for Tv steps,
+    laid out per sequence: q, k [N, Tv, Hqk, dk], v [N, Tv, Hv, dv], g, beta [N, Tv, Hv],
+    and the live state [N, Hv, dk, dv] fp32."""
+    d = make_decode(N, Hqk, Hv, dk, dv, Tv, dtype, seed=seed, gate_scale=gate_scale)
+    out = {name: d[name].transpose(0, 1).contiguous() for name in ("q", "k", "v", "g", "beta")}
+    out["state"] = d["state"]
+    return out
+
+
 def make_workload(w: Workload, seed=0, gate_scale=0.1):
     """Inputs for one named workload (see WORKLOADS)."""
+    if w.kind == "verify":
+        return make_verify(w.N, w.steps, w.Hqk, w.Hv, w.dk, w.dv, w.dtype, seed=seed, gate_scale=gate_scale)
     if w.kind == "decode":
         return make_decode(w.N, w.Hqk, w.Hv, w.dk, w.dv, w.steps, w.dtype, seed=seed, gate_scale=gate_scale)
     return make_prefill(w.B, w.T, w.Hqk, w.Hv, w.dk, w.dv, w.dtype, init_state=w.init_state, seed=seed,

@@ -41,6 +41,8 @@ def _kind(name):
         return "prefill"
     if "decode_kernel" in name:
         return "decode"
+    if "verify_kernel" in name:
+        return "verify"
     if "copyBuffer" in name or "copy" in name.lower():
         return "copy"
     return None

@@ -149,6 +149,27 @@ def decode_step(q, k, v, g, beta, state, scale=1.0):
     return o[:, 0], new_state
 
 
+def verify(q, k, v, g, beta, state, scale=1.0):
+    """Multi-token verify: Tv consecutive steps per sequence from a live state.
+
+    Speculative decoding (the archdiff model page "Qwen3.8-2.4T-A95B",
+    components list: multi-token-prediction drafting) runs every drafted token
+    through the layer; here that is ``decode_step`` applied once per token, in
+    order, each step starting from the state the previous one left.
+    q, k [N, Tv, Hqk, dk]; v [N, Tv, Hv, dv]; g, beta [N, Tv, Hv]; state [N, Hv, dk, dv].
+    Returns (o [N, Tv, Hv, dv], token_states [N, Tv, Hv, dk, dv]) in float64,
+    token_states[:, t] being the state after token t (the last is the final state).
+    """
+    q, k, v, g, beta, state = (_f64(x) for x in (q, k, v, g, beta, state))
+    N, Tv = q.shape[:2]
+    o = np.zeros((N, Tv) + v.shape[2:])
+    states = np.zeros((N, Tv) + state.shape[1:])
+    for t in range(Tv):
+        o[:, t], state = decode_step(q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], state, scale=scale)
+        states[:, t] = state
+    return o, states
+
+
 def chunk_factors(K, V, g, beta):
     """Chunk-local factors of the chunked (UT / WY) form for one chunk.
 

@@ -20,9 +20,10 @@ def declared_functions():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gdn_\w+)\s*\(", text, flags=re.M)))
 
 
-def test_header_declares_the_four_entry_points():
+def test_header_declares_the_five_entry_points():
     assert declared_functions() == sorted(
-        ["gdn_decode_step", "gdn_fwd_chunked", "gdn_fwd_chunked_workspace_size", "gdn_status_string"])
+        ["gdn_decode_step", "gdn_decode_verify", "gdn_fwd_chunked", "gdn_fwd_chunked_workspace_size",
+         "gdn_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -65,6 +66,12 @@ def call_dec(gdn, d, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, state=FAKE, o=FA
     return gdn.lib.gdn_decode_step(ctypes.byref(d), P(q), P(k), P(v), P(g), P(beta), P(state), P(o), P(0))
 
 
+def call_ver(gdn, d, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s_in=FAKE, s_out=0, ts=0, o=FAKE):
+    P = ctypes.c_void_p
+    return gdn.lib.gdn_decode_verify(ctypes.byref(d), P(q), P(k), P(v), P(g), P(beta), P(s_in), P(s_out), P(ts), P(o),
+                                     P(0))
+
+
 INVALID, NOT_SUPPORTED, MISALIGNED = 1, 2, 3
 
 
@@ -81,6 +88,8 @@ def test_null_dims_rejected(gdn):
     assert gdn.lib.gdn_decode_step(None, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
                                    P(0)) == INVALID
     assert gdn.lib.gdn_fwd_chunked_workspace_size(None) == 0
+    assert gdn.lib.gdn_decode_verify(None, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(0), P(0), P(FAKE),
+                                     P(0)) == INVALID
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -135,3 +144,16 @@ def test_decode_invalid(gdn):
 
 def test_workspace_size_is_zero_for_the_fused_prefill(gdn):
     assert gdn.fwd_chunked_workspace_size(dims(gdn)) == 0
+
+
+def test_verify_invalid(gdn):
+    assert call_ver(gdn, dims(gdn, T=0)) == INVALID              # at least one token
+    assert call_ver(gdn, dims(gdn, T=9)) == NOT_SUPPORTED        # at most eight
+    assert call_ver(gdn, dims(gdn, B=2, N=3, T=4)) == INVALID     # batch must equal N
+    assert call_ver(gdn, dims(gdn, T=4, Hv=5)) == INVALID
+    assert call_ver(gdn, dims(gdn, T=4, dk=32)) == NOT_SUPPORTED
+    assert call_ver(gdn, dims(gdn, T=4), s_in=0) == INVALID
+    assert call_ver(gdn, dims(gdn, T=4), o=0) == INVALID
+    assert call_ver(gdn, dims(gdn, T=4), s_out=FAKE + 4) == MISALIGNED
+    assert call_ver(gdn, dims(gdn, T=4), ts=FAKE + 8) == MISALIGNED
+    assert call_ver(gdn, dims(gdn, T=4, B=0, N=0)) == 0          # nothing to do

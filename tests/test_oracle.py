@@ -11,7 +11,7 @@ index in the oracle fails at least one of them.
 import numpy as np
 import pytest
 
-from oracle import chunk_factors, chunked, decode_step, recurrent, unrolled
+from oracle import chunk_factors, chunked, decode_step, recurrent, unrolled, verify
 
 RTOL = 1e-11
 
@@ -200,6 +200,34 @@ def test_p8_composition_and_decode_continuity():
         o_t, state = decode_step(q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], state)
         close(o_t[0], o_all[0, t], 1e-10)
     close(state, f_all, 1e-10)
+
+
+# ------------------------------------------------------------------ P16 ----
+@pytest.mark.parametrize("Tv", [1, 3, 6])
+def test_p16_verify_states_are_the_unrolled_prefix_states(Tv):
+    """Multi-token verify from a live state: o[:, t] and the state after token t equal the
+    brute-force product form over the first t + 1 tokens, sequence by sequence."""
+    rng = np.random.default_rng(60 + Tv)
+    N, Hqk, Hv, dk, dv = 3, 1, 2, 5, 4
+    q, k, v, g, beta = rand_inputs(rng, B=N, T=Tv, Hqk=Hqk, Hv=Hv, dk=dk, dv=dv, gate_scale=0.5)
+    S0 = rng.standard_normal((N, Hv, dk, dv))
+    o, states = verify(q, k, v, g, beta, S0, scale=0.8)
+    assert o.shape == (N, Tv, Hv, dv) and states.shape == (N, Tv, Hv, dk, dv)
+    for n in range(N):
+        for t in range(Tv):
+            sl = slice(n, n + 1), slice(0, t + 1)
+            o_u, f_u = unrolled(q[sl], k[sl], v[sl], g[sl], beta[sl], initial_state=S0[n:n + 1], scale=0.8)
+            close(o[n, t], o_u[0, t])
+            close(states[n, t], f_u[0])
+
+
+def test_p16_verify_leaves_its_input_state_alone():
+    rng = np.random.default_rng(66)
+    q, k, v, g, beta = rand_inputs(rng, B=2, T=4, Hqk=1, Hv=1, dk=3, dv=3)
+    S0 = rng.standard_normal((2, 1, 3, 3))
+    keep = S0.copy()
+    verify(q, k, v, g, beta, S0)
+    assert np.array_equal(S0, keep)
 
 
 # ------------------------------------------------------------------- P9 ----
