@@ -13,6 +13,7 @@ The same JSON line also carries
                 heads (512 MiB fp32 state): algorithmic GB/s against 8 TB/s;
   verify        gdn_decode_verify, 4 drafted tokens per sequence from the same
                 kind of live state: algorithmic GB/s against 8 TB/s;
+  epilogue      gdn_output_norm_gate over the prefill output: GB/s against 8 TB/s;
   cpu_baseline  the fp64 oracle on the host cores over the same workload.
 Inputs are seeded synthetic tensors (linear_attention_token_chunked_amd.inputs).
 Every timed loop starts after W untimed steps and at least --warm-seconds of
@@ -255,6 +256,29 @@ def bench_verify(gdn, torch, steps=20):
     }
 
 
+def bench_epilogue(gdn, torch, steps=50):
+    """Output epilogue (zero-centred RMSNorm + sigmoid gate) over the prefill_b4_t4096 output."""
+    from linear_attention_token_chunked_amd.inputs import make_epilogue
+
+    rows, dv = 4 * 4096 * 16, 128
+    dev = {k: v.cuda() for k, v in make_epilogue(rows, dv, "bf16").items()}
+    y = torch.empty_like(dev["o"])
+
+    def step():
+        gdn.output_norm_gate(dev["o"], dev["z"], dev["w"], out=y)
+
+    wall, mean_ms, per = time_launches(step, steps, 5, torch)
+    us = mean_ms * 1e3
+    nbytes = 3 * rows * dv * dev["o"].element_size() + dv * 4
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {
+        "workload": "prefill_b4_t4096 output (262144 rows x 128, bf16)", "rows": rows, "dv": dv,
+        "us_per_call_mean": us, "bytes_per_call": nbytes, "GBps": gbps,
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -296,6 +320,7 @@ def main():
     traffic = measured_traffic("prefill", args.workload)
     dec = None if args.no_decode else bench_decode(gdn, torch)
     ver = None if args.no_decode else bench_verify(gdn, torch)
+    epi = None if args.no_decode else bench_epilogue(gdn, torch)
     extra = {}
     if args.all:
         for name in ("prefill_t65536_gqa", "varlen_64"):
@@ -329,6 +354,7 @@ def main():
         "prefill": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in res.items()},
         "decode": dec,
         "verify": ver,
+        "epilogue": epi,
         "cpu_baseline": cpu,
     }
     if extra:

@@ -152,6 +152,26 @@ gdn_status_t gdn_decode_verify(const gdn_dims_t* d, const void* q, const void* k
                                const float* g, const float* beta, const float* state_in,
                                float* state_out, float* token_states, void* o, hipStream_t stream);
 
+/*
+ * Output epilogue around the mixer: the podcast transcript on "On the Design
+ * of Qwen3.8-Next Architecture" (cue 14) adds a sigmoid output gate and a
+ * zero-centred RMSNorm to the gated delta rule, and the archdiff model page
+ * "Qwen3.8-2.4T-A95B" (components list) writes the gate as sigmoid(x W_g) o.
+ * For every row r (one token of one value head, dv values):
+ *   y[r] = sigmoid(z[r]) * (o[r] / sqrt(mean_j o[r, j]^2 + eps)) * (1 + weight)
+ * with z the gate pre-activations (x W_g, computed by the caller) and weight
+ * the zero-centred per-channel norm weight (the scale is 1 + weight).
+ *
+ *   rows     number of rows, e.g. B * T * Hv for a prefill output; >= 0
+ *   dv       values per row: 64 or 128 (NOT_SUPPORTED otherwise)
+ *   eps      >= 0
+ *   dtype    element type of o, z and y (fp32 or bf16); y is rounded to nearest even
+ *   o, z, y  [rows, dv], 16-byte aligned device buffers; y may be o (in place)
+ *   weight   [dv] fp32, 16-byte aligned device buffer
+ */
+gdn_status_t gdn_output_norm_gate(int64_t rows, int32_t dv, float eps, gdn_dtype_t dtype, const void* o,
+                                  const void* z, const float* weight, void* y, hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* gdn_status_string(gdn_status_t s);
 

@@ -150,6 +150,28 @@ gdn_status_t gdn_decode_verify(const gdn_dims_t* d, const void* q, const void* k
   return from_hip(gdn::launch_verify(a, stream));
 }
 
+gdn_status_t gdn_output_norm_gate(int64_t rows, int32_t dv, float eps, gdn_dtype_t dtype, const void* o,
+                                  const void* z, const float* weight, void* y, hipStream_t stream) {
+  if (rows < 0 || dv < 1 || !(eps >= 0.f)) return GDN_STATUS_INVALID_VALUE;
+  if (dtype != GDN_DTYPE_FLOAT32 && dtype != GDN_DTYPE_BFLOAT16) return GDN_STATUS_INVALID_VALUE;
+  if (dv != 64 && dv != 128) return GDN_STATUS_NOT_SUPPORTED;
+  if (rows == 0) return GDN_STATUS_SUCCESS;
+  if (!o || !z || !weight || !y) return GDN_STATUS_INVALID_VALUE;
+  if (!aligned(o, 16) || !aligned(z, 16) || !aligned(y, 16) || !aligned(weight, 16)) return GDN_STATUS_MISALIGNED;
+  // 16 threads per row; the grid size must fit in 32 bits.
+  if (rows >= (int64_t(1) << 35)) return GDN_STATUS_NOT_SUPPORTED;
+  gdn::EpilogueArgs a;
+  a.o = o;
+  a.z = z;
+  a.weight = weight;
+  a.y = y;
+  a.rows = rows;
+  a.dv = dv;
+  a.eps = eps;
+  a.bf16 = dtype == GDN_DTYPE_BFLOAT16;
+  return from_hip(gdn::launch_norm_gate(a, stream));
+}
+
 const char* gdn_status_string(gdn_status_t s) {
   switch (s) {
     case GDN_STATUS_SUCCESS: return "GDN_STATUS_SUCCESS";

@@ -45,7 +45,19 @@ struct VerifyArgs {
   bool bf16;
 };
 
+// Output epilogue: rows of dv values, y = sigmoid(z) * o / rms(o) * (1 + w).
+struct EpilogueArgs {
+  const void *o, *z;
+  const float* weight;
+  void* y;
+  int64_t rows;
+  int dv;
+  float eps;
+  bool bf16;
+};
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_norm_gate(const EpilogueArgs& a, hipStream_t stream);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 

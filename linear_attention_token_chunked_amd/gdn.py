@@ -39,7 +39,7 @@ class Dims(ctypes.Structure):
 DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1}
 
 EXPORTED = ("gdn_fwd_chunked_workspace_size", "gdn_fwd_chunked", "gdn_decode_step", "gdn_decode_verify",
-            "gdn_status_string")
+            "gdn_output_norm_gate", "gdn_status_string")
 
 
 def _load():
@@ -56,6 +56,9 @@ def _load():
     lib.gdn_decode_step.restype = ctypes.c_int
     lib.gdn_decode_verify.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, fp, fp, fp, fp, fp, vp, vp]
     lib.gdn_decode_verify.restype = ctypes.c_int
+    lib.gdn_output_norm_gate.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_int, vp, vp, fp, vp,
+                                         vp]
+    lib.gdn_output_norm_gate.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     return lib
@@ -238,5 +241,40 @@ def decode_verify(q, k, v, g, beta, state_in, *, state_out="in_place", token_sta
     with torch.cuda.device(dev):
         code = lib.gdn_decode_verify(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                      _ptr(state_in), _ptr(state_out), _ptr(token_states), _ptr(out), _stream(dev))
+    _check(code)
+    return out
+
+
+def output_norm_gate(o, z, weight, *, eps=1e-6, out=None):
+    """y = sigmoid(z) * o / sqrt(mean(o^2) + eps) * (1 + weight) over the last dim (dv) of o.
+
+    o, z: contiguous tensors of the same shape [..., dv] (fp32 or bf16); weight: fp32 [dv].
+    ``out`` may be ``o`` itself (in place).  Returns y.
+    """
+    dev = o.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    if o.dtype not in DTYPE_CODE:
+        raise TypeError("o, z must be float32 or bfloat16")
+    if o.dim() < 1:
+        raise ValueError("o must have a last (dv) dimension")
+    _need(o, "o", o.dtype, dev, o.dim())
+    _need(z, "z", o.dtype, dev, o.dim())
+    if z.shape != o.shape:
+        raise ValueError("z must have the shape of o")
+    dv = o.shape[-1]
+    _need(weight, "weight", torch.float32, dev, 1)
+    if weight.shape[0] != dv:
+        raise ValueError("weight must be [dv]")
+    if out is None:
+        out = torch.empty_like(o)
+    else:
+        _need(out, "out", o.dtype, dev, o.dim())
+        if out.shape != o.shape:
+            raise ValueError("out must have the shape of o")
+    rows = o.numel() // dv if dv else 0
+    with torch.cuda.device(dev):
+        code = lib.gdn_output_norm_gate(ctypes.c_int64(rows), ctypes.c_int32(dv), ctypes.c_float(eps),
+                                        DTYPE_CODE[o.dtype], _ptr(o), _ptr(z), _ptr(weight), _ptr(out), _stream(dev))
     _check(code)
     return out

@@ -153,6 +153,17 @@ def make_verify(N, Tv, Hqk, Hv, dk, dv, dtype="bf16", seed=0, gate_scale=0.1):
     return out
 
 
+def make_epilogue(rows, dv, dtype="bf16", seed=0):
+    """Draw output-epilogue inputs: mixer outputs o and gate pre-activations z [rows, dv]
+    ~ N(0, 1), and the zero-centred norm weight w [dv] ~ 0.1 N(0, 1) fp32."""
+    rng = np.random.default_rng(seed)
+    return {
+        "o": _cast(rng.standard_normal((rows, dv)), dtype),
+        "z": _cast(rng.standard_normal((rows, dv)), dtype),
+        "w": _cast(0.1 * rng.standard_normal(dv), "fp32"),
+    }
+
+
 def make_workload(w: Workload, seed=0, gate_scale=0.1):
     """Inputs for one named workload (see WORKLOADS)."""
     if w.kind == "verify":

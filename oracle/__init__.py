@@ -3,6 +3,8 @@
 Test infrastructure only: imported by tests/, __graft_entry__.smoke() and the
 cpu_baseline leg of bench.py, never by the product path.
 """
-from .gdn_oracle import chunk_factors, chunked, decode_step, recurrent, sequence_bounds, unrolled, verify
+from .gdn_oracle import (chunk_factors, chunked, decode_step, output_norm_gate, recurrent, sequence_bounds,
+                         unrolled, verify)
 
-__all__ = ["recurrent", "chunked", "chunk_factors", "unrolled", "decode_step", "verify", "sequence_bounds"]
+__all__ = ["recurrent", "chunked", "chunk_factors", "unrolled", "decode_step", "verify", "output_norm_gate",
+           "sequence_bounds"]

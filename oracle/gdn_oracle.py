@@ -170,6 +170,22 @@ def verify(q, k, v, g, beta, state, scale=1.0):
     return o, states
 
 
+def output_norm_gate(o, z, weight, eps=1e-6):
+    """Output epilogue around the mixer, per row of dv values (the last axis).
+
+    The podcast transcript (cue 14) adds a sigmoid output gate and a
+    zero-centred RMSNorm to the rule; the archdiff model page "Qwen3.8-2.4T-A95B"
+    writes the gate as sigmoid(x W_g) times o.  Readings (R21): the norm comes
+    first and the gate multiplies its result; the norm divides by the root of
+    the mean square over the row plus eps; "zero-centred" means the stored
+    weight w scales by 1 + w.  z stands for the pre-activation x W_g.
+    """
+    o, z, weight = (_f64(x) for x in (o, z, weight))
+    rms = np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    gate = 1.0 / (1.0 + np.exp(-z))
+    return gate * (o / rms) * (1.0 + weight)
+
+
 def chunk_factors(K, V, g, beta):
     """Chunk-local factors of the chunked (UT / WY) form for one chunk.
 

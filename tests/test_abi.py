@@ -20,10 +20,10 @@ def declared_functions():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gdn_\w+)\s*\(", text, flags=re.M)))
 
 
-def test_header_declares_the_five_entry_points():
+def test_header_declares_the_six_entry_points():
     assert declared_functions() == sorted(
         ["gdn_decode_step", "gdn_decode_verify", "gdn_fwd_chunked", "gdn_fwd_chunked_workspace_size",
-         "gdn_status_string"])
+         "gdn_output_norm_gate", "gdn_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -157,3 +157,19 @@ def test_verify_invalid(gdn):
     assert call_ver(gdn, dims(gdn, T=4), s_out=FAKE + 4) == MISALIGNED
     assert call_ver(gdn, dims(gdn, T=4), ts=FAKE + 8) == MISALIGNED
     assert call_ver(gdn, dims(gdn, T=4, B=0, N=0)) == 0          # nothing to do
+
+
+def test_norm_gate_invalid(gdn):
+    P = ctypes.c_void_p
+    f = lambda rows=4, dv=128, eps=1e-6, dt=1, o=FAKE, z=FAKE, w=FAKE, y=FAKE: gdn.lib.gdn_output_norm_gate(
+        ctypes.c_int64(rows), ctypes.c_int32(dv), ctypes.c_float(eps), dt, P(o), P(z), P(w), P(y), P(0))
+    assert f(rows=-1) == INVALID
+    assert f(eps=-1.0) == INVALID
+    assert f(eps=float("nan")) == INVALID
+    assert f(dt=5) == INVALID
+    assert f(dv=96) == NOT_SUPPORTED
+    assert f(o=0) == INVALID
+    assert f(w=0) == INVALID
+    assert f(z=FAKE + 8) == MISALIGNED
+    assert f(w=FAKE + 4) == MISALIGNED
+    assert f(rows=0) == 0                                          # nothing to do

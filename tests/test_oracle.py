@@ -11,7 +11,7 @@ index in the oracle fails at least one of them.
 import numpy as np
 import pytest
 
-from oracle import chunk_factors, chunked, decode_step, recurrent, unrolled, verify
+from oracle import chunk_factors, chunked, decode_step, output_norm_gate, recurrent, unrolled, verify
 
 RTOL = 1e-11
 
@@ -228,6 +228,47 @@ def test_p16_verify_leaves_its_input_state_alone():
     keep = S0.copy()
     verify(q, k, v, g, beta, S0)
     assert np.array_equal(S0, keep)
+
+
+# ------------------------------------------------------------------ P17 ----
+# The output epilogue: closed forms on rows whose mean square is known.
+def _sig(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def test_p17_constant_rows_give_gate_times_scale():
+    rng = np.random.default_rng(70)
+    dv = 8
+    c = np.array([[2.5], [-0.75]]) * np.ones((2, dv))          # rows of one value: rms = |c|
+    z = rng.standard_normal((2, dv))
+    w = 0.3 * rng.standard_normal(dv)
+    close(output_norm_gate(c, z, w, eps=0.0), np.sign(c) * _sig(z) * (1 + w))
+    eps = 0.5                                                    # eps sits under the root
+    close(output_norm_gate(c, z, w, eps=eps), c / np.sqrt(c ** 2 + eps) * _sig(z) * (1 + w))
+
+
+def test_p17_one_hot_rows_pin_the_mean_over_the_row():
+    dv, a, j = 16, -3.0, 5
+    o = np.zeros((1, dv))
+    o[0, j] = a                                                  # mean square a^2 / dv
+    z = np.linspace(-2, 2, dv)[None]
+    w = np.linspace(-0.2, 0.2, dv)
+    y = output_norm_gate(o, z, w, eps=0.0)
+    want = np.zeros((1, dv))
+    want[0, j] = np.sign(a) * np.sqrt(dv) * _sig(z[0, j]) * (1 + w[j])
+    close(y, want)
+
+
+def test_p17_gate_at_zero_halves_and_norm_is_scale_free_and_odd():
+    rng = np.random.default_rng(71)
+    o = rng.standard_normal((4, 32))
+    w = np.zeros(32)
+    y0 = output_norm_gate(o, np.zeros_like(o), w, eps=0.0)
+    close(np.mean((2 * y0) ** 2, axis=-1), np.ones(4))          # sigmoid(0) = 1/2, unit mean square
+    z = rng.standard_normal((4, 32))
+    close(output_norm_gate(7.0 * o, z, w, eps=0.0), output_norm_gate(o, z, w, eps=0.0))
+    close(output_norm_gate(-o, z, w, eps=0.0), -output_norm_gate(o, z, w, eps=0.0))
+    assert np.all(np.abs(output_norm_gate(o, np.full_like(o, -700.0), w)) < 1e-300)   # closed gate
 
 
 # ------------------------------------------------------------------- P9 ----
