@@ -14,6 +14,7 @@ The same JSON line also carries
   verify        gdn_decode_verify, 4 drafted tokens per sequence from the same
                 kind of live state: algorithmic GB/s against 8 TB/s;
   epilogue      gdn_output_norm_gate over the prefill output: GB/s against 8 TB/s;
+  short_conv    gdn_short_conv with L2 norm over the prefill's q: GB/s against 8 TB/s;
   cpu_baseline  the fp64 oracle on the host cores over the same workload.
 Inputs are seeded synthetic tensors (linear_attention_token_chunked_amd.inputs).
 Every timed loop starts after W untimed steps and at least --warm-seconds of
@@ -279,6 +280,30 @@ def bench_epilogue(gdn, torch, steps=50):
     }
 
 
+def bench_short_conv(gdn, torch, steps=50):
+    """Pre-mixer short convolution + per-head L2 norm over q (or k) of prefill_b4_t4096."""
+    from linear_attention_token_chunked_amd.inputs import make_conv
+
+    B, T, H, hd = 4, 4096, 16, 128
+    inp = make_conv(B, T, H, hd, "bf16")
+    x, w = inp["x"].cuda(), inp["w"].cuda()
+    y = torch.empty_like(x)
+
+    def step():
+        gdn.short_conv(x, w, l2norm=True, out=y)
+
+    wall, mean_ms, per = time_launches(step, steps, 5, torch)
+    us = mean_ms * 1e3
+    nbytes = 2 * x.numel() * x.element_size() + w.numel() * 4
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {
+        "workload": "q of prefill_b4_t4096 (4 x 4096 tokens x 16 heads x 128, bf16), width 4, L2 norm",
+        "us_per_call_mean": us, "bytes_per_call": nbytes, "GBps": gbps,
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -321,6 +346,7 @@ def main():
     dec = None if args.no_decode else bench_decode(gdn, torch)
     ver = None if args.no_decode else bench_verify(gdn, torch)
     epi = None if args.no_decode else bench_epilogue(gdn, torch)
+    conv = None if args.no_decode else bench_short_conv(gdn, torch)
     extra = {}
     if args.all:
         for name in ("prefill_t65536_gqa", "varlen_64"):
@@ -355,6 +381,7 @@ def main():
         "decode": dec,
         "verify": ver,
         "epilogue": epi,
+        "short_conv": conv,
         "cpu_baseline": cpu,
     }
     if extra:

@@ -172,6 +172,35 @@ gdn_status_t gdn_decode_verify(const gdn_dims_t* d, const void* q, const void* k
 gdn_status_t gdn_output_norm_gate(int64_t rows, int32_t dv, float eps, gdn_dtype_t dtype, const void* o,
                                   const void* z, const float* weight, void* y, hipStream_t stream);
 
+/*
+ * Pre-mixer step: short causal convolution along the tokens, per channel, and
+ * optionally an L2 normalisation of every head.  [Transcript] cue 14 of the
+ * podcast on "On the Design of Qwen3.8-Next Architecture" lists short causal
+ * convolutions around the rule without a width: the width built here is
+ * GDN_SHORT_CONV_WIDTH = 4.  For channel c of token t of a sequence starting
+ * at token s (tokens before s count as zero):
+ *   y[t, c] = sum_{i < 4} weight[c, i] * x[t - 3 + i, c]
+ * and with l2norm != 0 every (token, head) row of head_dim channels is then
+ * divided by sqrt(sum of its squares + eps): the per-head q/k normalisation of
+ * the archdiff model page "Qwen3.8-2.4T-A95B" (QK-Norm), to unit L2 norm, the
+ * scale at which a write with beta = 1 replaces what is stored under a key.
+ *
+ *   batch, seqlen      B rows of T tokens (with cu_seqlens: B = 1, T = total tokens)
+ *   num_seqs           N = B, or len(cu_seqlens) - 1
+ *   cu_seqlens         [N + 1] int32 on the device, or NULL (the batch rows are the
+ *                      sequences); same contract as for gdn_fwd_chunked
+ *   heads, head_dim    channels per token = heads * head_dim; head_dim 64 or 128
+ *   eps                >= 0
+ *   dtype              element type of x and y (fp32 or bf16); y rounded to nearest even
+ *   x, y               [B, T, heads, head_dim], 16-byte aligned; y must not overlap x
+ *   weight             [heads * head_dim, 4] fp32, 16-byte aligned (tap i multiplies
+ *                      token t - 3 + i)
+ */
+#define GDN_SHORT_CONV_WIDTH 4
+gdn_status_t gdn_short_conv(int32_t batch, int32_t seqlen, int32_t num_seqs, const int32_t* cu_seqlens,
+                            int32_t heads, int32_t head_dim, int32_t l2norm, float eps, gdn_dtype_t dtype,
+                            const void* x, const float* weight, void* y, hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* gdn_status_string(gdn_status_t s);
 

@@ -1,0 +1,159 @@
+// Pre-mixer step of the GDN layer: short causal convolution along the tokens,
+// per channel, and (for q and k) an L2 normalisation of every head, gfx950.
+//
+// The podcast transcript on "On the Design of Qwen3.8-Next Architecture"
+// (cue 14) lists short causal convolutions among what the model adds around
+// the gated delta rule; it gives no width, and this library builds width 4.
+// The archdiff model page "Qwen3.8-2.4T-A95B" normalises q and k per head
+// (QK-Norm); here to unit L2 norm, the scale at which the delta rule's write
+// with beta = 1 replaces exactly what is stored under a key.
+// For channel c of token t of a sequence that starts at token s:
+//   y[t, c] = sum_{i < W} w[c, i] * x[t - (W - 1) + i, c],   x[u] = 0 for u < s,
+// then, with l2norm, y[t, head] /= sqrt(sum over the head's channels of y^2 + eps).
+// The kernel is bound by HBM bandwidth: every token row is read once and
+// written once.  Sixteen lanes share a (token, head) row of hd channels, so a
+// row's norm reduces inside a 16-lane group.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace gdn {
+namespace {
+
+constexpr int kConvThreads = 256;
+constexpr int kConvWidth = 4;
+
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  x += __shfl_xor(x, 4);
+  x += __shfl_xor(x, 8);
+  return x;
+}
+
+// A 16-lane group walks a run of kRun consecutive tokens of one head: it
+// loads the head's taps once and slides a window of the last W token rows
+// through registers, so every row is loaded once.
+constexpr int kRun = 8;
+
+template <class T, int HD, bool L2>
+__global__ __launch_bounds__(kConvThreads) void conv_kernel(const T* __restrict__ x, const float* __restrict__ w,
+                                                            T* __restrict__ y, const int32_t* __restrict__ cu,
+                                                            int num_seqs, int seqlen, int heads, int tokens,
+                                                            int runs, float eps) {
+  constexpr int EPL = HD / 16;  // channels per lane
+  constexpr int W = kConvWidth;
+  static_assert(W == 4, "one 16-byte load of taps per channel");
+  typedef T lane_vec __attribute__((ext_vector_type(EPL)));
+  const int lane16 = threadIdx.x & 15;
+  const int grp = blockIdx.x * (kConvThreads / 16) + (threadIdx.x >> 4);  // run * heads + head
+  if (grp >= runs * heads) return;  // whole 16-lane groups leave together
+  const int run = grp / heads;
+  const int h = grp - run * heads;
+  const int t0 = run * kRun;
+  // the sequence of the run's first token, and where the next one starts
+  int start, next;
+  if (cu) {
+    int lo = 0, hi = num_seqs;  // the last n with cu[n] <= t0
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (cu[mid] <= t0) lo = mid; else hi = mid;
+    }
+    start = cu[lo];
+    next = cu[lo + 1];  // > t0: lo is the last sequence starting at or before t0
+  } else {
+    start = t0 - t0 % seqlen;
+    next = start + seqlen;
+  }
+  const int c0 = h * HD + lane16 * EPL;  // first channel of this lane
+  floatx4 taps[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) taps[e] = *reinterpret_cast<const floatx4*>(w + (c0 + e) * W);
+  const T* xl = x + static_cast<size_t>(h) * HD + lane16 * EPL;  // this lane's channels of token 0
+  T* yl = y + static_cast<size_t>(h) * HD + lane16 * EPL;
+  const size_t tstride = static_cast<size_t>(heads) * HD;
+  // window of the W - 1 rows before the current token (zero before the sequence start)
+  float win[W - 1][EPL];
+#pragma unroll
+  for (int i = 0; i < W - 1; ++i) {
+    const int u = t0 - (W - 1) + i;
+    const bool live = u >= start && u >= 0;
+    lane_vec v = {};
+    if (live) v = *reinterpret_cast<const lane_vec*>(xl + static_cast<size_t>(u) * tstride);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) win[i][e] = live ? to_float(v[e]) : 0.f;
+  }
+#pragma unroll
+  for (int r = 0; r < kRun; ++r) {
+    const int t = t0 + r;
+    if (t >= tokens) break;
+    if (t == next) {  // a new sequence starts here: forget the window
+      start = t;
+      if (cu) {  // the last sequence starting at or before t (empty ones start and end at t)
+        int lo = 0, hi = num_seqs;
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (cu[mid] <= t) lo = mid; else hi = mid;
+        }
+        next = cu[lo + 1];
+      } else {
+        next = t + seqlen;
+      }
+#pragma unroll
+      for (int i = 0; i < W - 1; ++i)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) win[i][e] = 0.f;
+    }
+    const lane_vec v = *reinterpret_cast<const lane_vec*>(xl + static_cast<size_t>(t) * tstride);
+    float cur[EPL], acc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      cur[e] = to_float(v[e]);
+      acc[e] = taps[e][0] * win[0][e] + taps[e][1] * win[1][e] + taps[e][2] * win[2][e] + taps[e][3] * cur[e];
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      win[0][e] = win[1][e];
+      win[1][e] = win[2][e];
+      win[2][e] = cur[e];
+    }
+    if constexpr (L2) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) ss += acc[e] * acc[e];
+      const float rs = rsqrtf(row16_sum(ss) + eps);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] *= rs;
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4)
+      *reinterpret_cast<typename Vec4<T>::type*>(yl + static_cast<size_t>(t) * tstride + e) =
+          pack4<T>(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+  }
+}
+
+template <class T, int HD>
+hipError_t launch(const ConvArgs& a, hipStream_t stream) {
+  if (a.tokens == 0) return hipSuccess;
+  const int runs = (a.tokens + kRun - 1) / kRun;
+  const int64_t groups = static_cast<int64_t>(runs) * a.heads;
+  const dim3 grid(static_cast<unsigned>((groups + kConvThreads / 16 - 1) / (kConvThreads / 16)));
+  if (a.l2norm)
+    conv_kernel<T, HD, true><<<grid, dim3(kConvThreads), 0, stream>>>(
+        static_cast<const T*>(a.x), a.weight, static_cast<T*>(a.y), a.cu_seqlens, a.num_seqs, a.seqlen, a.heads,
+        a.tokens, runs, a.eps);
+  else
+    conv_kernel<T, HD, false><<<grid, dim3(kConvThreads), 0, stream>>>(
+        static_cast<const T*>(a.x), a.weight, static_cast<T*>(a.y), a.cu_seqlens, a.num_seqs, a.seqlen, a.heads,
+        a.tokens, runs, a.eps);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
+  if (a.head_dim == 128) return a.bf16 ? launch<bf16, 128>(a, stream) : launch<float, 128>(a, stream);
+  if (a.head_dim == 64) return a.bf16 ? launch<bf16, 64>(a, stream) : launch<float, 64>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

@@ -172,6 +172,42 @@ gdn_status_t gdn_output_norm_gate(int64_t rows, int32_t dv, float eps, gdn_dtype
   return from_hip(gdn::launch_norm_gate(a, stream));
 }
 
+gdn_status_t gdn_short_conv(int32_t batch, int32_t seqlen, int32_t num_seqs, const int32_t* cu_seqlens,
+                            int32_t heads, int32_t head_dim, int32_t l2norm, float eps, gdn_dtype_t dtype,
+                            const void* x, const float* weight, void* y, hipStream_t stream) {
+  if (batch < 0 || seqlen < 0 || num_seqs < 0 || heads < 1 || head_dim < 1 || !(eps >= 0.f))
+    return GDN_STATUS_INVALID_VALUE;
+  if (dtype != GDN_DTYPE_FLOAT32 && dtype != GDN_DTYPE_BFLOAT16) return GDN_STATUS_INVALID_VALUE;
+  if (cu_seqlens) {
+    if (batch != 1) return GDN_STATUS_INVALID_VALUE;
+  } else if (num_seqs != batch) {
+    return GDN_STATUS_INVALID_VALUE;
+  }
+  if (head_dim != 64 && head_dim != 128) return GDN_STATUS_NOT_SUPPORTED;
+  const int64_t tokens = static_cast<int64_t>(batch) * seqlen;
+  if (tokens == 0 || num_seqs == 0) return GDN_STATUS_SUCCESS;
+  if (!x || !weight || !y || x == y) return GDN_STATUS_INVALID_VALUE;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(weight, 16) || !aligned(cu_seqlens, 4))
+    return GDN_STATUS_MISALIGNED;
+  // tokens, and runs of 8 tokens times heads, are 32-bit indices in the kernel
+  if (tokens >= (int64_t(1) << 31) || (tokens + 7) / 8 * heads >= (int64_t(1) << 31) - 64)
+    return GDN_STATUS_NOT_SUPPORTED;
+  gdn::ConvArgs a;
+  a.x = x;
+  a.weight = weight;
+  a.y = y;
+  a.cu_seqlens = cu_seqlens;
+  a.tokens = static_cast<int>(tokens);
+  a.seqlen = seqlen;
+  a.num_seqs = num_seqs;
+  a.heads = heads;
+  a.head_dim = head_dim;
+  a.l2norm = l2norm != 0;
+  a.eps = eps;
+  a.bf16 = dtype == GDN_DTYPE_BFLOAT16;
+  return from_hip(gdn::launch_conv(a, stream));
+}
+
 const char* gdn_status_string(gdn_status_t s) {
   switch (s) {
     case GDN_STATUS_SUCCESS: return "GDN_STATUS_SUCCESS";

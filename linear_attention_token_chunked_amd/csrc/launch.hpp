@@ -56,7 +56,21 @@ struct EpilogueArgs {
   bool bf16;
 };
 
+// Short causal convolution (width 4) along the tokens, per channel, optionally
+// followed by an L2 normalisation of every (token, head) row.
+struct ConvArgs {
+  const void* x;
+  const float* weight;  // [heads * head_dim, 4]
+  void* y;
+  const int32_t* cu_seqlens;  // may be null: batch rows are the sequences
+  int tokens, seqlen, num_seqs, heads, head_dim;
+  bool l2norm;
+  float eps;
+  bool bf16;
+};
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_conv(const ConvArgs& a, hipStream_t stream);
 hipError_t launch_norm_gate(const EpilogueArgs& a, hipStream_t stream);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);

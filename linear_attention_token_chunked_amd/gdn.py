@@ -39,7 +39,7 @@ class Dims(ctypes.Structure):
 DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1}
 
 EXPORTED = ("gdn_fwd_chunked_workspace_size", "gdn_fwd_chunked", "gdn_decode_step", "gdn_decode_verify",
-            "gdn_output_norm_gate", "gdn_status_string")
+            "gdn_output_norm_gate", "gdn_short_conv", "gdn_status_string")
 
 
 def _load():
@@ -59,6 +59,9 @@ def _load():
     lib.gdn_output_norm_gate.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_int, vp, vp, fp, vp,
                                          vp]
     lib.gdn_output_norm_gate.restype = ctypes.c_int
+    i32 = ctypes.c_int32
+    lib.gdn_short_conv.argtypes = [i32, i32, i32, vp, i32, i32, i32, ctypes.c_float, ctypes.c_int, vp, fp, vp, vp]
+    lib.gdn_short_conv.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     return lib
@@ -276,5 +279,42 @@ def output_norm_gate(o, z, weight, *, eps=1e-6, out=None):
     with torch.cuda.device(dev):
         code = lib.gdn_output_norm_gate(ctypes.c_int64(rows), ctypes.c_int32(dv), ctypes.c_float(eps),
                                         DTYPE_CODE[o.dtype], _ptr(o), _ptr(z), _ptr(weight), _ptr(out), _stream(dev))
+    _check(code)
+    return out
+
+
+SHORT_CONV_WIDTH = 4
+
+
+def short_conv(x, weight, *, cu_seqlens=None, l2norm=False, eps=1e-6, out=None):
+    """Short causal convolution (width 4) along the tokens of x [B, T, heads, head_dim], per
+    channel, restarting at every sequence start; then, with ``l2norm``, every (token, head) row
+    scaled to unit L2 norm.  weight: fp32 [heads * head_dim, 4], tap i multiplying token t - 3 + i.
+    cu_seqlens: int32 [N + 1] on the device (then B must be 1), or None.  Returns y (a new tensor,
+    or ``out``, which must not be x)."""
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    if x.dtype not in DTYPE_CODE:
+        raise TypeError("x must be float32 or bfloat16")
+    _need(x, "x", x.dtype, dev, 4)
+    B, T, H, hd = x.shape
+    _need(weight, "weight", torch.float32, dev, 2)
+    if weight.shape != (H * hd, SHORT_CONV_WIDTH):
+        raise ValueError("weight must be [heads * head_dim, 4]")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev, 1)
+        N = cu_seqlens.shape[0] - 1
+    else:
+        N = B
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _need(out, "out", x.dtype, dev, 4)
+        if out.shape != x.shape:
+            raise ValueError("out must have the shape of x")
+    with torch.cuda.device(dev):
+        code = lib.gdn_short_conv(B, T, N, _ptr(cu_seqlens), H, hd, int(bool(l2norm)), ctypes.c_float(eps),
+                                  DTYPE_CODE[x.dtype], _ptr(x), _ptr(weight), _ptr(out), _stream(dev))
     _check(code)
     return out

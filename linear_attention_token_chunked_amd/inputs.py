@@ -164,6 +164,22 @@ def make_epilogue(rows, dv, dtype="bf16", seed=0):
     }
 
 
+def make_conv(B, T, heads, head_dim, dtype="bf16", seed=0, num_packed=0):
+    """Draw short-convolution inputs: pre-convolution activations x [B, T, heads, head_dim]
+    ~ N(0, 1), taps [heads * head_dim, 4] ~ N(0, 1) / 2 fp32, and (num_packed > 0, B = 1)
+    cu_seqlens for that many sequences of lognormal length over the T tokens."""
+    rng = np.random.default_rng(seed)
+    out = {
+        "x": _cast(rng.standard_normal((B, T, heads, head_dim)), dtype),
+        "w": _cast(0.5 * rng.standard_normal((heads * head_dim, 4)), "fp32"),
+        "cu_seqlens": None,
+    }
+    if num_packed:
+        cuts = np.sort(rng.choice(np.arange(1, T), size=num_packed - 1, replace=False))
+        out["cu_seqlens"] = torch.from_numpy(np.concatenate([[0], cuts, [T]]).astype(np.int32))
+    return out
+
+
 def make_workload(w: Workload, seed=0, gate_scale=0.1):
     """Inputs for one named workload (see WORKLOADS)."""
     if w.kind == "verify":

@@ -4,7 +4,7 @@ Test infrastructure only: imported by tests/, __graft_entry__.smoke() and the
 cpu_baseline leg of bench.py, never by the product path.
 """
 from .gdn_oracle import (chunk_factors, chunked, decode_step, output_norm_gate, recurrent, sequence_bounds,
-                         unrolled, verify)
+                         short_conv, unrolled, verify)
 
 __all__ = ["recurrent", "chunked", "chunk_factors", "unrolled", "decode_step", "verify", "output_norm_gate",
-           "sequence_bounds"]
+           "short_conv", "sequence_bounds"]

@@ -186,6 +186,33 @@ def output_norm_gate(o, z, weight, eps=1e-6):
     return gate * (o / rms) * (1.0 + weight)
 
 
+def short_conv(x, weight, cu_seqlens=None, l2norm=False, eps=1e-6):
+    """Pre-mixer short causal convolution along the tokens, per channel.
+
+    The podcast transcript (cue 14) lists short causal convolutions around the
+    rule without a width; the width here is that of ``weight`` (4 for the GPU
+    path).  Readings (R23): tap i of W multiplies token t - (W - 1) + i, tokens
+    before a sequence's start count as zero, there is no activation after it;
+    with l2norm every (token, head) row is then divided by
+    sqrt(sum of squares + eps) (the per-head q/k normalisation, to unit norm).
+    x [B, T, heads, hd]; weight [heads * hd, W]; returns y in float64.
+    """
+    x, weight = _f64(x), _f64(weight)
+    B, T, H, hd = x.shape
+    W = weight.shape[1]
+    wc = weight.reshape(H, hd, W)
+    y = np.zeros_like(x)
+    for b, s, e in sequence_bounds(B, T, cu_seqlens):
+        for t in range(s, e):
+            for i in range(W):
+                u = t - (W - 1) + i
+                if u >= s:
+                    y[b, t] += wc[:, :, i] * x[b, u]
+    if l2norm:
+        y = y / np.sqrt(np.sum(y * y, axis=-1, keepdims=True) + eps)
+    return y
+
+
 def chunk_factors(K, V, g, beta):
     """Chunk-local factors of the chunked (UT / WY) form for one chunk.
 

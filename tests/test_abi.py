@@ -20,10 +20,10 @@ def declared_functions():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gdn_\w+)\s*\(", text, flags=re.M)))
 
 
-def test_header_declares_the_six_entry_points():
+def test_header_declares_the_seven_entry_points():
     assert declared_functions() == sorted(
         ["gdn_decode_step", "gdn_decode_verify", "gdn_fwd_chunked", "gdn_fwd_chunked_workspace_size",
-         "gdn_output_norm_gate", "gdn_status_string"])
+         "gdn_output_norm_gate", "gdn_short_conv", "gdn_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -173,3 +173,19 @@ def test_norm_gate_invalid(gdn):
     assert f(z=FAKE + 8) == MISALIGNED
     assert f(w=FAKE + 4) == MISALIGNED
     assert f(rows=0) == 0                                          # nothing to do
+
+
+def test_short_conv_invalid(gdn):
+    P = ctypes.c_void_p
+    f = lambda B=1, T=8, N=1, cu=0, H=2, hd=128, l2=1, eps=1e-6, dt=1, x=FAKE, w=FAKE, y=FAKE + 4096: \
+        gdn.lib.gdn_short_conv(B, T, N, P(cu), H, hd, l2, ctypes.c_float(eps), dt, P(x), P(w), P(y), P(0))
+    assert f(T=-1) == INVALID
+    assert f(H=0) == INVALID
+    assert f(B=2, N=3) == INVALID                       # N != B without cu_seqlens
+    assert f(B=2, N=2, cu=FAKE) == INVALID              # packed input needs B == 1
+    assert f(hd=96) == NOT_SUPPORTED
+    assert f(eps=-1.0) == INVALID
+    assert f(x=0) == INVALID
+    assert f(y=FAKE) == INVALID                         # y must not be x
+    assert f(w=FAKE + 4) == MISALIGNED
+    assert f(T=0) == 0                                  # nothing to do

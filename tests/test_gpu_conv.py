@@ -1,0 +1,54 @@
+"""GPU parity of gdn_short_conv (short causal convolution along the tokens, per channel, with
+optional per-head L2 normalisation) against the fp64 oracle, through the C ABI."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import short_conv as oracle_conv
+from parity import TOL, assert_close, f64, flush
+
+from linear_attention_token_chunked_amd.inputs import make_conv
+
+pytestmark = pytest.mark.gpu
+DT = {"bf16": torch.bfloat16, "fp32": torch.float32}
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    from linear_attention_token_chunked_amd import gdn as m
+
+    return m
+
+
+@pytest.mark.parametrize("dtype,B,T,H,hd,l2,packed", [
+    ("bf16", 2, 70, 4, 128, True, 0),
+    ("bf16", 1, 300, 2, 128, False, 5),    # packed, several sequences, some shorter than the taps
+    ("fp32", 3, 17, 2, 64, True, 0),
+    ("fp32", 1, 64, 3, 128, False, 0),
+    ("bf16", 1, 3, 1, 64, True, 0),        # shorter than the filter
+    ("fp32", 1, 41, 2, 64, True, 7),
+])
+def test_short_conv_matches_oracle(gdn, dtype, B, T, H, hd, l2, packed):
+    flush(f"short conv {dtype} B={B} T={T} H={H} hd={hd} l2={l2} packed={packed}")
+    inp = make_conv(B, T, H, hd, dtype, seed=T + H, num_packed=packed)
+    cu = inp["cu_seqlens"]
+    y = gdn.short_conv(inp["x"].cuda(), inp["w"].cuda(), cu_seqlens=cu.cuda() if cu is not None else None,
+                       l2norm=l2, eps=1e-6)
+    ref = oracle_conv(inp["x"], inp["w"], cu_seqlens=cu, l2norm=l2, eps=1e-6)
+    assert_close("y", f64(y), ref, TOL[DT[dtype]])
+
+
+def test_short_conv_b4_t4096_qk_shape(gdn):
+    """q/k of prefill_b4_t4096 (4 x 4096 tokens, 16 heads x 128), L2-normalised; rows sampled."""
+    flush("short conv full 4x4096x16x128")
+    inp = make_conv(4, 4096, 16, 128, "bf16", seed=0)
+    y = gdn.short_conv(inp["x"].cuda(), inp["w"].cuda(), l2norm=True)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y.float()).all())
+    norms = y.float().pow(2).sum(-1).sqrt()
+    assert float((norms - 1).abs().max()) < 1e-2
+    for b, t0 in [(0, 0), (3, 4090), (1, 1000), (2, 2047)]:
+        sl = slice(max(0, t0 - 3), t0 + 4)
+        ref = oracle_conv(inp["x"][b:b + 1, :t0 + 4], inp["w"], l2norm=True)[0, sl]
+        assert_close(f"y rows {b},{t0}", f64(y[b, sl]), ref, TOL[torch.bfloat16])

@@ -11,7 +11,8 @@ index in the oracle fails at least one of them.
 import numpy as np
 import pytest
 
-from oracle import chunk_factors, chunked, decode_step, output_norm_gate, recurrent, unrolled, verify
+from oracle import (chunk_factors, chunked, decode_step, output_norm_gate, recurrent, short_conv, unrolled,
+                    verify)
 
 RTOL = 1e-11
 
@@ -269,6 +270,54 @@ def test_p17_gate_at_zero_halves_and_norm_is_scale_free_and_odd():
     close(output_norm_gate(7.0 * o, z, w, eps=0.0), output_norm_gate(o, z, w, eps=0.0))
     close(output_norm_gate(-o, z, w, eps=0.0), -output_norm_gate(o, z, w, eps=0.0))
     assert np.all(np.abs(output_norm_gate(o, np.full_like(o, -700.0), w)) < 1e-300)   # closed gate
+
+
+# ------------------------------------------------------------------ P18 ----
+# The pre-mixer short convolution: impulse response, restart and closed forms.
+def test_p18_impulse_response_is_the_reversed_taps():
+    rng = np.random.default_rng(80)
+    W, T, H, hd = 4, 12, 2, 3
+    w = rng.standard_normal((H * hd, W))
+    x = np.zeros((1, T, H, hd))
+    s0, h, c = 5, 1, 2
+    x[0, s0, h, c] = 1.0
+    y = short_conv(x, w)
+    want = np.zeros_like(x)
+    for d in range(W):                                   # token s0 + d sees the impulse through tap W-1-d
+        want[0, s0 + d, h, c] = w[h * hd + c, W - 1 - d]
+    close(y, want)
+
+
+def test_p18_constant_input_and_sequence_starts():
+    rng = np.random.default_rng(81)
+    W, H, hd = 4, 1, 5
+    w = rng.standard_normal((H * hd, W))
+    cu = np.array([0, 2, 9, 10, 16])
+    T = int(cu[-1])
+    x = np.ones((1, T, H, hd)) * 1.5
+    y = short_conv(x, w, cu_seqlens=cu)
+    full = 1.5 * w.sum(axis=1).reshape(H, hd)
+    for n in range(len(cu) - 1):
+        s, e = int(cu[n]), int(cu[n + 1])
+        for t in range(s, e):
+            k = min(t - s + 1, W)                          # only the taps on tokens of the same sequence
+            close(y[0, t], 1.5 * w[:, W - k:].sum(axis=1).reshape(H, hd))
+        if e - s >= W:
+            close(y[0, e - 1], full)
+
+
+def test_p18_causal_and_l2_normalised_rows():
+    rng = np.random.default_rng(82)
+    x = rng.standard_normal((2, 9, 3, 4))
+    w = rng.standard_normal((12, 4))
+    y = short_conv(x, w)
+    x2 = x.copy()
+    x2[:, 6:] += rng.standard_normal(x2[:, 6:].shape)   # change only tokens 6..8
+    close(short_conv(x2, w)[:, :6], y[:, :6])
+    yn = short_conv(x, w, l2norm=True, eps=0.0)
+    close(np.sum(yn * yn, axis=-1), np.ones(yn.shape[:-1]))
+    close(yn, y / np.linalg.norm(y, axis=-1, keepdims=True))
+    close(short_conv(3.0 * x, w, l2norm=True, eps=0.0), yn)
 
 
 # ------------------------------------------------------------------- P9 ----
