@@ -11,8 +11,8 @@ index in the oracle fails at least one of them.
 import numpy as np
 import pytest
 
-from oracle import (chunk_factors, chunked, decode_step, output_norm_gate, recurrent, short_conv, unrolled,
-                    verify)
+from oracle import (chunk_factors, chunked, decode_step, output_norm_gate, recurrent, recurrent_grads, short_conv,
+                    unrolled, verify)
 
 RTOL = 1e-11
 
@@ -318,6 +318,68 @@ def test_p18_causal_and_l2_normalised_rows():
     close(np.sum(yn * yn, axis=-1), np.ones(yn.shape[:-1]))
     close(yn, y / np.linalg.norm(y, axis=-1, keepdims=True))
     close(short_conv(3.0 * x, w, l2norm=True, eps=0.0), yn)
+
+
+# ------------------------------------------------------------------ P19 ----
+# The backward oracle: automatic differentiation, checked against central finite
+# differences of the forward oracle (an independent route to the same numbers).
+def _loss(q, k, v, g, beta, S0, d_o, d_f, cu, scale):
+    o, f = recurrent(q, k, v, g, beta, initial_state=S0, cu_seqlens=cu, scale=scale)
+    return float(np.sum(o * d_o) + np.sum(f * d_f))
+
+
+@pytest.mark.parametrize("cu", [None, np.array([0, 2, 2, 7])])
+def test_p19_gradients_match_finite_differences(cu):
+    rng = np.random.default_rng(90)
+    B, T = (2, 4) if cu is None else (1, 7)
+    Hqk, Hv, dk, dv = 1, 2, 3, 2
+    q, k, v, g, beta = rand_inputs(rng, B=B, T=T, Hqk=Hqk, Hv=Hv, dk=dk, dv=dv, unit_keys=False, gate_scale=0.5)
+    N = B if cu is None else len(cu) - 1
+    S0 = rng.standard_normal((N, Hv, dk, dv))
+    d_o = rng.standard_normal((B, T, Hv, dv))
+    d_f = rng.standard_normal((N, Hv, dk, dv))
+    grads = recurrent_grads(q, k, v, g, beta, d_o, initial_state=S0, d_final=d_f, cu_seqlens=cu, scale=0.7)
+    args = dict(q=q, k=k, v=v, g=g, beta=beta, S0=S0)
+    names = dict(q="dq", k="dk", v="dv", g="dg", beta="dbeta", S0="d_initial_state")
+    h = 1e-6
+    for name, x in args.items():
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + h
+            up = _loss(**args, d_o=d_o, d_f=d_f, cu=cu, scale=0.7)
+            x[idx] = keep - h
+            dn = _loss(**args, d_o=d_o, d_f=d_f, cu=cu, scale=0.7)
+            x[idx] = keep
+            fd[idx] = (up - dn) / (2 * h)
+        close(grads[names[name]], fd, 1e-7)
+
+
+def test_p19_identity_gates_give_closed_form_gradients():
+    """beta = 0 and g = 0: o_t = scale S0^T q_t and the final state is S0, so dq_t = scale S0 d_o_t,
+    dS0 = scale sum_t q_t d_o_t^T + d_final, dv = 0, and dbeta, dg follow from one step's algebra."""
+    rng = np.random.default_rng(91)
+    T, dk, dv = 5, 4, 3
+    q = rng.standard_normal((1, T, 1, dk))
+    k = rng.standard_normal((1, T, 1, dk))
+    v = rng.standard_normal((1, T, 1, dv))
+    g = np.zeros((1, T, 1))
+    beta = np.zeros((1, T, 1))
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    d_o = rng.standard_normal((1, T, 1, dv))
+    d_f = rng.standard_normal((1, 1, dk, dv))
+    gr = recurrent_grads(q, k, v, g, beta, d_o, initial_state=S0, d_final=d_f, scale=0.5)
+    close(gr["dq"][0, :, 0], 0.5 * np.einsum("ij,tj->ti", S0[0, 0], d_o[0, :, 0]))
+    close(gr["d_initial_state"][0, 0], 0.5 * np.einsum("ti,tj->ij", q[0, :, 0], d_o[0, :, 0]) + d_f[0, 0])
+    close(gr["dv"], np.zeros_like(v))
+    close(gr["dk"], np.zeros_like(k))
+    # d/d beta_t: the write adds k_t (v_t - S0^T k_t)^T, seen by o_s (s >= t) and the final state
+    for t in range(T):
+        Gt = 0.5 * np.einsum("si,sj->ij", q[0, t:, 0], d_o[0, t:, 0]) + d_f[0, 0]
+        err = v[0, t, 0] - S0[0, 0].T @ k[0, t, 0]
+        close(gr["dbeta"][0, t, 0], k[0, t, 0] @ Gt @ err)
+        # d/d g_t: alpha_t scales the whole state once, seen the same way
+        close(gr["dg"][0, t, 0], np.sum(Gt * S0[0, 0]))
 
 
 # ------------------------------------------------------------------- P9 ----
