@@ -15,6 +15,9 @@ The same JSON line also carries
                 kind of live state: algorithmic GB/s against 8 TB/s;
   epilogue      gdn_output_norm_gate over the prefill output: GB/s against 8 TB/s;
   short_conv    gdn_short_conv with L2 norm over the prefill's q: GB/s against 8 TB/s;
+  bwd           gdn_bwd_chunked (all gradients) over the prefill's inputs: the
+                recurrence's algorithmic fp32 TFLOP/s against the 157.3 TFLOP/s
+                fp32 vector peak;
   cpu_baseline  the fp64 oracle on the host cores over the same workload.
 Inputs are seeded synthetic tensors (linear_attention_token_chunked_amd.inputs).
 Every timed loop starts after W untimed steps and at least --warm-seconds of
@@ -67,6 +70,13 @@ def decode_bytes(N, Hqk, Hv, dk, dv, s_in):
 def verify_bytes(N, Tv, Hqk, Hv, dk, dv, s_in):
     """Per call: the fp32 state read and written once, and Tv tokens' q, k, v, o, g, beta."""
     return N * Hv * dk * dv * 4 * 2 + Tv * (N * (2 * Hqk * dk + 2 * Hv * dv) * s_in + N * Hv * 8)
+
+
+def bwd_flops_per_token_head(dk, dv):
+    """fp32 flops of one token's recompute (Mt = a M, r = Mt^T k, M' = Mt + k u^T, o = M'^T q: 7 per
+    state element) and adjoint (dM += q do^T, dq, du, dk's two products, dMt, dg: 2 each; dM = a dMt: 1;
+    15 per element) for one value head."""
+    return 22 * dk * dv
 
 
 def source_hash(path):
@@ -304,6 +314,33 @@ def bench_short_conv(gdn, torch, steps=50):
     }
 
 
+def bench_bwd(gdn, torch, steps=10):
+    """Backward pass (gradients of q, k, v, g, beta and the initial state) over prefill_b4_t4096."""
+    from linear_attention_token_chunked_amd.inputs import WORKLOADS, make_cotangents, make_workload
+
+    w = WORKLOADS["prefill_b4_t4096"]
+    dev = {k: (v.cuda() if v is not None else None) for k, v in make_workload(w).items()}
+    cot = make_cotangents(w.B, w.T, w.Hv, w.dv, w.B, w.dk, w.dtype)
+    d_o, d_fin = cot["d_o"].cuda(), cot["d_final"].cuda()
+    dims = gdn.make_dims(w.B, w.T, w.B, w.Hqk, w.Hv, w.dk, w.dv, w.chunk, 1.0, dev["q"].dtype)
+    ws = torch.empty(gdn.bwd_chunked_workspace_size(dims), dtype=torch.uint8, device="cuda")
+
+    def step():
+        gdn.bwd_chunked(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], d_o, initial_state=dev["initial_state"],
+                        d_final_state=d_fin, scale=w.dk ** -0.5, workspace=ws)
+
+    wall, mean_ms, per = time_launches(step, steps, 2, torch)
+    tokens = w.B * w.T
+    flops = bwd_flops_per_token_head(w.dk, w.dv) * tokens * w.Hv
+    tflops = flops / (mean_ms * 1e-3) / 1e12
+    return {
+        "workload": w.name, "tokens": tokens, "ms_per_call_mean": mean_ms, "ms_per_call_median": per[len(per) // 2],
+        "Mtok_s": tokens / (mean_ms * 1e-3) / 1e6, "flops_per_call": flops, "tflops": tflops,
+        "roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_FP32_TFLOPS, 4), "traffic": None},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -347,6 +384,7 @@ def main():
     ver = None if args.no_decode else bench_verify(gdn, torch)
     epi = None if args.no_decode else bench_epilogue(gdn, torch)
     conv = None if args.no_decode else bench_short_conv(gdn, torch)
+    bwd = None if args.no_decode else bench_bwd(gdn, torch)
     extra = {}
     if args.all:
         for name in ("prefill_t65536_gqa", "varlen_64"):
@@ -382,6 +420,7 @@ def main():
         "verify": ver,
         "epilogue": epi,
         "short_conv": conv,
+        "bwd": bwd,
         "cpu_baseline": cpu,
     }
     if extra:

@@ -201,6 +201,59 @@ gdn_status_t gdn_short_conv(int32_t batch, int32_t seqlen, int32_t num_seqs, con
                             int32_t heads, int32_t head_dim, int32_t l2norm, float eps, gdn_dtype_t dtype,
                             const void* x, const float* weight, void* y, hipStream_t stream);
 
+/*
+ * Bytes of device workspace gdn_bwd_chunked needs for these dims, each part
+ * rounded up to 256 bytes: (N + 1) int32 chunk offsets; two fp32 states
+ * (dk x dv) per value head and chunk, the state entering the chunk and the
+ * gradient of the state leaving it, for (floor(B * T / 64) + N) chunks (a bound
+ * on the chunks of any split of the tokens into N sequences); and two fp32
+ * values per token, value head and value channel (the chunk form's corrected
+ * values U and their gradient).  0 for dims with negative sizes.
+ */
+size_t gdn_bwd_chunked_workspace_size(const gdn_dims_t* d);
+
+/*
+ * Backward pass of gdn_fwd_chunked: the gradients of a scalar loss L with
+ * respect to q, k, v, g, beta and the initial state, given dL/do for every
+ * output token and dL/d(final state).  The report on "On the Design of
+ * Qwen3.8-Next Architecture" (paper page, Abstract) weighs every change on
+ * training cost as well as inference; the recurrence differentiated is the
+ * one at the top of this file (podcast transcript, cue 14), token by token.
+ * The result is the exact derivative of that recurrence (up to fp32
+ * rounding), whatever chunk form a forward pass used: per token, in stored
+ * layout, with alpha = exp(g), Mt = alpha M, r = Mt^T k, u = beta (v - r),
+ * M' = Mt + k u^T and o = scale M'^T q, walking the tokens in reverse with dM
+ * the gradient of the state after the token:
+ *   dM += scale q do^T,  dq = scale M' do,  du = dM^T k,  dv = beta du,
+ *   dbeta = du . (v - r),  dr = -beta du,  dk = dM u + Mt dr,
+ *   dMt = dM + k dr^T,  dg = <dMt, Mt>,  dM <- alpha dMt.
+ * The work runs chunk by chunk on the matrix cores: a forward pass stores each
+ * chunk's starting state and U in the workspace, a reverse pass over the chunks
+ * carries dM (and stores it per chunk with dZ = (I + A)^-T dU), and a final
+ * pass forms every token's gradients, all chunks at once.
+ *
+ *   d, q, k, v, g, beta, initial_state, cu_seqlens: as for gdn_fwd_chunked
+ *                  (the same inputs as the forward pass being differentiated)
+ *   d_o            [B, T, Hv, dv]   dtype, 16-byte aligned: dL/do
+ *   d_final_state  [N, Hv, dk, dv]  fp32, 16-byte aligned, or NULL for zeros
+ *   dq, dk         [B, T, Hqk, dk]  fp32, 16-byte aligned; summed over the value
+ *                                   heads that share a query/key head
+ *   dv             [B, T, Hv, dv]   fp32, 16-byte aligned
+ *   dg, dbeta      [B, T, Hv]       fp32, 4-byte aligned
+ *   d_initial_state [N, Hv, dk, dv] fp32, 16-byte aligned, or NULL (not written)
+ *   workspace      at least gdn_bwd_chunked_workspace_size(d) bytes, 256-byte
+ *                  aligned; its contents on entry and exit are unspecified
+ * Every gradient element is written (the kernels clear dq, dk, dg and dbeta on
+ * the stream first).  Outputs must not overlap each other or any input.
+ * Supported: dk = dv in {64, 128}, C = 64, dtype bf16; dtype fp32 with dk = 64.
+ */
+gdn_status_t gdn_bwd_chunked(const gdn_dims_t* d, const void* q, const void* k, const void* v,
+                             const float* g, const float* beta, const float* initial_state,
+                             const int32_t* cu_seqlens, const void* d_o, const float* d_final_state,
+                             float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                             float* d_initial_state, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* gdn_status_string(gdn_status_t s);
 

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace gdn {
 
 typedef __bf16 bf16;
@@ -109,6 +111,92 @@ __device__ __forceinline__ typename Mma<T>::frag lds_frag(const T* row, int kg, 
 }
 
 __device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP row shifts
+// and row broadcasts (no LDS round trips).
+__device__ __forceinline__ float wave_inclusive_sum(float x) {
+#define GDN_DPP_ADD(ctrl, rows)                                                                               \
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, rows, 0xf, false))
+  GDN_DPP_ADD(0x111, 0xf);  // row_shr:1
+  GDN_DPP_ADD(0x112, 0xf);  // row_shr:2
+  GDN_DPP_ADD(0x114, 0xf);  // row_shr:4
+  GDN_DPP_ADD(0x118, 0xf);  // row_shr:8
+  GDN_DPP_ADD(0x142, 0xa);  // row_bcast:15 into rows 1 and 3
+  GDN_DPP_ADD(0x143, 0xc);  // row_bcast:31 into rows 2 and 3
+#undef GDN_DPP_ADD
+  return x;
+}
+
+// Every lane gets x from lane S of its group of four (DPP quad permutation).
+template <int S>
+__device__ __forceinline__ float quad_bcast(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x55 * S, 0xf, 0xf, false));
+}
+
+// Column cc of (I + A)^-1 for a 16x16 strictly lower A by right-looking
+// forward substitution, four lanes per column: the lane with q = lane % 4
+// holds rows 4q..4q+3 in x.  Once x_j is final (step j) it is broadcast
+// within the quad and every row i > j takes x_i -= A_ij x_j; At[j][i] = A_ij
+// (zero for i <= j, so the other rows are unchanged).
+// The 15 columns of A the lane needs are loaded first, so the substitution
+// waits for LDS once rather than once per step.
+template <int... J>
+__device__ __forceinline__ void unit_lower_inverse_column(floatx4& x, const float* At, int ld, int q,
+                                                          std::integer_sequence<int, J...>) {
+  floatx4 a[sizeof...(J)];
+  ((a[J] = *reinterpret_cast<const floatx4*>(At + J * ld + 4 * q)), ...);
+  ((x -= a[J] * quad_bcast<J / 4>(x[J % 4])), ...);
+}
+
+// 16x16 tile products whose contraction is one 16-wide block: lane group g
+// supplies k = 4g..4g+3, which is the row set it owns in an accumulator tile.
+template <class T> struct Mma16;
+template <> struct Mma16<bf16> {
+  typedef bf16x4 frag;
+  __device__ __forceinline__ static void mma(floatx4& c, const frag& a, const frag& b) {
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, a), __builtin_bit_cast(s4, b), c, 0, 0,
+                                                   0);
+  }
+  __device__ __forceinline__ static frag chain(const floatx4& t) {
+    frag f;
+    f[0] = static_cast<bf16>(t[0]);
+    f[1] = static_cast<bf16>(t[1]);
+    f[2] = static_cast<bf16>(t[2]);
+    f[3] = static_cast<bf16>(t[3]);
+    return f;
+  }
+};
+template <> struct Mma16<float> {
+  typedef floatx4 frag;
+  __device__ __forceinline__ static void mma(floatx4& c, const frag& a, const frag& b) { Mma<float>::mma(c, a, b); }
+  __device__ __forceinline__ static frag chain(const floatx4& t) { return t; }
+};
+
+// Four consecutive rows of one column of a row-major LDS tile, as lane data
+// for the accumulator layout: lane (lg, lr) gets X[r0 + 4lg + e][c0 + lr],
+// e = 0..3 (c0 a multiple of 16).  bf16 uses the gfx950 transposing LDS read:
+// in each 16-lane group, lane i returns element i%4 of the 8-byte loads of
+// lanes 4e + i/4, so lane j loads row r0 + 4lg + j/4 at the 4-column run
+// c0 + 4(j%4).  fp32 reads the four values one by one.
+template <class T>
+__device__ __forceinline__ typename Vec4<T>::type lds_col4(const T* base, int ld, int r0, int c0, int lane) {
+  const int lg = lane >> 4, lr = lane & 15;
+  if constexpr (sizeof(T) == 2) {
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    const T* ptr = base + (r0 + 4 * lg + (lr >> 2)) * ld + c0 + 4 * (lr & 3);
+    const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<__attribute__((address_space(3))) s4*>(reinterpret_cast<size_t>(ptr)));
+    return __builtin_bit_cast(typename Vec4<T>::type, v);
+  } else {
+    typename Vec4<T>::type v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = base[(r0 + 4 * lg + e) * ld + c0 + lr];
+    return v;
+  }
+}
 
 // Workgroup barrier that orders LDS only: waits for this wave's LDS (and
 // scalar) operations, then s_barrier.  Unlike __syncthreads() it does not wait

@@ -208,6 +208,76 @@ gdn_status_t gdn_short_conv(int32_t batch, int32_t seqlen, int32_t num_seqs, con
   return from_hip(gdn::launch_conv(a, stream));
 }
 
+size_t gdn_bwd_chunked_workspace_size(const gdn_dims_t* d) {
+  if (!d || d->batch < 0 || d->seqlen < 0 || d->num_seqs < 0 || d->num_v_heads < 1 || d->head_dim_k < 1 ||
+      d->head_dim_v < 1)
+    return 0;
+  return gdn::bwd_workspace_bytes(static_cast<int64_t>(d->batch) * d->seqlen, d->num_seqs, d->num_v_heads,
+                                  d->head_dim_k, d->head_dim_v);
+}
+
+gdn_status_t gdn_bwd_chunked(const gdn_dims_t* d, const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, const float* initial_state, const int32_t* cu_seqlens,
+                             const void* d_o, const float* d_final_state, float* dq, float* dk, float* dv,
+                             float* dg, float* dbeta, float* d_initial_state, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  gdn_status_t st = check_common(d);
+  if (st != GDN_STATUS_SUCCESS) return st;
+  if (d->batch < 0 || d->seqlen < 0) return GDN_STATUS_INVALID_VALUE;
+  if (cu_seqlens) {
+    if (d->batch != 1) return GDN_STATUS_INVALID_VALUE;
+  } else if (d->num_seqs != d->batch) {
+    return GDN_STATUS_INVALID_VALUE;
+  }
+  if (d->chunk_size != 64) return GDN_STATUS_NOT_SUPPORTED;
+  if (d->head_dim_k != d->head_dim_v) return GDN_STATUS_NOT_SUPPORTED;
+  if (d->dtype == GDN_DTYPE_FLOAT32 && d->head_dim_k != 64) return GDN_STATUS_NOT_SUPPORTED;
+  const bool has_tokens = static_cast<int64_t>(d->batch) * d->seqlen > 0;
+  if (has_tokens && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
+    return GDN_STATUS_INVALID_VALUE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(d_o, 16) || !aligned(g, 4) ||
+      !aligned(beta, 4) || !aligned(initial_state, 16) || !aligned(d_final_state, 16) ||
+      !aligned(cu_seqlens, 4) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(dg, 4) ||
+      !aligned(dbeta, 4) || !aligned(d_initial_state, 16) || !aligned(workspace, 256))
+    return GDN_STATUS_MISALIGNED;
+  if (d->num_seqs == 0) return GDN_STATUS_SUCCESS;
+  const size_t need = gdn_bwd_chunked_workspace_size(d);
+  if (workspace_bytes < need) return GDN_STATUS_WORKSPACE_TOO_SMALL;
+  if (need > 0 && !workspace) return GDN_STATUS_INVALID_VALUE;
+  // Token indices are 32-bit inside the kernels, and so is the grid of up to 16 workgroups per unit.
+  if (static_cast<int64_t>(d->batch) * d->seqlen >= (int64_t(1) << 31) ||
+      static_cast<int64_t>(d->num_seqs) * d->num_v_heads * 16 >= (int64_t(1) << 31))
+    return GDN_STATUS_NOT_SUPPORTED;
+
+  gdn::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = d_o;
+  a.g = g;
+  a.beta = beta;
+  a.initial_state = initial_state;
+  a.d_final_state = d_final_state;
+  a.cu_seqlens = cu_seqlens;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dg = dg;
+  a.dbeta = dbeta;
+  a.d_initial_state = d_initial_state;
+  a.workspace = workspace;
+  a.batch = d->batch;
+  a.seqlen = d->seqlen;
+  a.num_seqs = d->num_seqs;
+  a.Hqk = d->num_qk_heads;
+  a.Hv = d->num_v_heads;
+  a.head_dim_k = d->head_dim_k;
+  a.head_dim_v = d->head_dim_v;
+  a.scale = d->scale;
+  a.bf16 = d->dtype == GDN_DTYPE_BFLOAT16;
+  return from_hip(gdn::launch_bwd(a, stream));
+}
+
 const char* gdn_status_string(gdn_status_t s) {
   switch (s) {
     case GDN_STATUS_SUCCESS: return "GDN_STATUS_SUCCESS";

@@ -28,6 +28,12 @@ struct PrefillArgs {
   int batch, seqlen, num_seqs, Hqk, Hv, dk, dv, chunk;
   float scale;
   bool bf16;
+  // Set by the backward pass only: keep every chunk's starting state
+  // ([chunk][Hv][dk][dv], chunk = chunk_base[n] + local index) and U (the
+  // chunk form's corrected values, [token][Hv][dv]) in fp32, and skip o.
+  float* save_state = nullptr;
+  float* save_u = nullptr;
+  const int32_t* chunk_base = nullptr;  // [N + 1] with cu_seqlens, else null (n * ceil(T / C))
 };
 
 // Multi-token verify: Tv (<= kMaxVerifyTokens) consecutive steps per sequence.
@@ -69,7 +75,24 @@ struct ConvArgs {
   bool bf16;
 };
 
+// Backward pass of a prefill: fp32 gradients of q, k, v, g, beta and the initial state.
+struct BwdArgs {
+  const void *q, *k, *v, *dout;
+  const float *g, *beta;
+  const float* initial_state;  // may be null (zeros)
+  const float* d_final_state;  // may be null (zeros)
+  const int32_t* cu_seqlens;   // may be null
+  float *dq, *dk, *dv, *dg, *dbeta;
+  float* d_initial_state;      // may be null (not written)
+  void* workspace;             // bwd_workspace_bytes, 256-byte aligned
+  int batch, seqlen, num_seqs, Hqk, Hv, head_dim_k, head_dim_v;
+  float scale;
+  bool bf16;
+};
+size_t bwd_workspace_bytes(int64_t tokens, int num_seqs, int Hv, int dk, int dv);
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_conv(const ConvArgs& a, hipStream_t stream);
 hipError_t launch_norm_gate(const EpilogueArgs& a, hipStream_t stream);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);

@@ -49,92 +49,6 @@ namespace {
 constexpr int C = 64;                    // chunk length
 constexpr int NP = 4;                    // producer wavefronts (consumer wavefronts: a template parameter)
 constexpr int PTHREADS = 64 * NP;
-constexpr float kLog2e = 1.4426950408889634f;
-
-// Inclusive prefix sum over the 64 lanes of a wavefront with DPP row shifts
-// and row broadcasts (no LDS round trips).
-__device__ __forceinline__ float wave_inclusive_sum(float x) {
-#define GDN_DPP_ADD(ctrl, rows)                                                                               \
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, rows, 0xf, false))
-  GDN_DPP_ADD(0x111, 0xf);  // row_shr:1
-  GDN_DPP_ADD(0x112, 0xf);  // row_shr:2
-  GDN_DPP_ADD(0x114, 0xf);  // row_shr:4
-  GDN_DPP_ADD(0x118, 0xf);  // row_shr:8
-  GDN_DPP_ADD(0x142, 0xa);  // row_bcast:15 into rows 1 and 3
-  GDN_DPP_ADD(0x143, 0xc);  // row_bcast:31 into rows 2 and 3
-#undef GDN_DPP_ADD
-  return x;
-}
-
-// Every lane gets x from lane S of its group of four (DPP quad permutation).
-template <int S>
-__device__ __forceinline__ float quad_bcast(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x55 * S, 0xf, 0xf, false));
-}
-
-// Column cc of (I + A)^-1 for a 16x16 strictly lower A by right-looking
-// forward substitution, four lanes per column: the lane with q = lane % 4
-// holds rows 4q..4q+3 in x.  Once x_j is final (step j) it is broadcast
-// within the quad and every row i > j takes x_i -= A_ij x_j; At[j][i] = A_ij
-// (zero for i <= j, so the other rows are unchanged).
-// The 15 columns of A the lane needs are loaded first, so the substitution
-// waits for LDS once rather than once per step.
-template <int... J>
-__device__ __forceinline__ void unit_lower_inverse_column(floatx4& x, const float* At, int ld, int q,
-                                                          std::integer_sequence<int, J...>) {
-  floatx4 a[sizeof...(J)];
-  ((a[J] = *reinterpret_cast<const floatx4*>(At + J * ld + 4 * q)), ...);
-  ((x -= a[J] * quad_bcast<J / 4>(x[J % 4])), ...);
-}
-
-// 16x16 tile products whose contraction is one 16-wide block: lane group g
-// supplies k = 4g..4g+3, which is the row set it owns in an accumulator tile.
-template <class T> struct Mma16;
-template <> struct Mma16<bf16> {
-  typedef bf16x4 frag;
-  __device__ __forceinline__ static void mma(floatx4& c, const frag& a, const frag& b) {
-    typedef short s4 __attribute__((ext_vector_type(4)));
-    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, a), __builtin_bit_cast(s4, b), c, 0, 0,
-                                                   0);
-  }
-  __device__ __forceinline__ static frag chain(const floatx4& t) {
-    frag f;
-    f[0] = static_cast<bf16>(t[0]);
-    f[1] = static_cast<bf16>(t[1]);
-    f[2] = static_cast<bf16>(t[2]);
-    f[3] = static_cast<bf16>(t[3]);
-    return f;
-  }
-};
-template <> struct Mma16<float> {
-  typedef floatx4 frag;
-  __device__ __forceinline__ static void mma(floatx4& c, const frag& a, const frag& b) { Mma<float>::mma(c, a, b); }
-  __device__ __forceinline__ static frag chain(const floatx4& t) { return t; }
-};
-
-// Four consecutive rows of one column of a row-major LDS tile, as lane data
-// for the accumulator layout: lane (lg, lr) gets X[r0 + 4lg + e][c0 + lr],
-// e = 0..3 (c0 a multiple of 16).  bf16 uses the gfx950 transposing LDS read:
-// in each 16-lane group, lane i returns element i%4 of the 8-byte loads of
-// lanes 4e + i/4, so lane j loads row r0 + 4lg + j/4 at the 4-column run
-// c0 + 4(j%4).  fp32 reads the four values one by one.
-template <class T>
-__device__ __forceinline__ typename Vec4<T>::type lds_col4(const T* base, int ld, int r0, int c0, int lane) {
-  const int lg = lane >> 4, lr = lane & 15;
-  if constexpr (sizeof(T) == 2) {
-    typedef short s4 __attribute__((ext_vector_type(4)));
-    const T* ptr = base + (r0 + 4 * lg + (lr >> 2)) * ld + c0 + 4 * (lr & 3);
-    const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        reinterpret_cast<__attribute__((address_space(3))) s4*>(reinterpret_cast<size_t>(ptr)));
-    return __builtin_bit_cast(typename Vec4<T>::type, v);
-  } else {
-    typename Vec4<T>::type v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = base[(r0 + 4 * lg + e) * ld + c0 + lr];
-    return v;
-  }
-}
-
 // The bf16 V tile is read only down its columns; it stores the 16-column
 // blocks of a row at swizzled places: block b of row r sits at block
 // b ^ swz(r).  A transposing read covers four rows of one block per 16-lane
@@ -312,6 +226,8 @@ struct Params {
   const int32_t* cu;
   void* o;
   float* hT;
+  float *save_state, *save_u;
+  const int32_t* chunk_base;
   int T, Hqk, Hv, nunits, nslices;
   float scale;
 };
@@ -419,7 +335,9 @@ template <int W> struct OutPTiles;
 template <> struct OutPTiles<0> { static constexpr int n = 4, ti[4] = {0, 1, 1, 3}, tj[4] = {0, 0, 1, 0}; };
 template <> struct OutPTiles<1> { static constexpr int n = 4, ti[4] = {2, 2, 3, 3}, tj[4] = {1, 2, 1, 2}; };
 
-template <class T, int DK, int DV, int BV, int NSTAGE, int NCW, bool OUTW>
+// SAVE: the variant a backward pass runs first; it keeps each chunk's starting
+// state and U (fp32) and writes no output.
+template <class T, int DK, int DV, int BV, int NSTAGE, int NCW, bool OUTW, bool SAVE>
 __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kernel(Params p) {
   using L = Layout<T, DK, BV, NSTAGE, NCW, OUTW>;
   using MM = Mma<T>;
@@ -642,6 +560,18 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
         for (int s = 0; s < 4; ++s) Ms[a][j][s] = p.h0 ? h0[slane + MM::state_row(a, 0, s) * DV + 16 * j] : 0.f;
   }
 
+  // The state at the start of chunk c (SAVE).
+  auto save_state = [&](int c) __attribute__((always_inline)) {
+    const int cb = p.chunk_base ? p.chunk_base[n] : n * ((p.T + C - 1) / C);
+    float* d = p.save_state + (static_cast<size_t>(cb + c) * p.Hv + h) * DK * DV;
+#pragma unroll
+    for (int a = 0; a < KT; ++a)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) d[slane + MM::state_row(a, 0, s) * DV + 16 * j] = Ms[a][j][s];
+  };
+
   // seg 1: Y = K M; Z = beta (V - exp(G) Y).  With one state tile per wave the
   // state part of the output, O^T = diag-scaled (Q M)^T, is formed here too,
   // next to K M which takes the same operands; with two, holding it until
@@ -741,7 +671,10 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
         }
       }
     }
-    if constexpr (OUTW) {
+    if constexpr (SAVE) {
+      (void)cs;
+      (void)Lc;
+    } else if constexpr (OUTW) {
       T* orow = og + static_cast<size_t>(cs + lr) * v_tok + static_cast<size_t>(h) * DV + wcol + 4 * lg;
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
@@ -825,6 +758,20 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
         Z[b][j] = u;  // Z_b is not needed any more
       }
     }
+    if constexpr (SAVE) {  // U rows of the chunk's tokens
+      const int cs = bos + c * C, Lc = min(C, eos - cs);
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * b + 4 * lg + i;
+          if (t < Lc) {
+            float* u = p.save_u + (static_cast<size_t>(cs + t) * p.Hv + h) * DV + wcol + lr;
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) u[16 * j] = Z[b][j][i];
+          }
+        }
+    }
     if constexpr (OUTW) {  // U as operands for the output wave
 #pragma unroll
       for (int kgi = 0; kgi < KGC; ++kgi) sUx[kgi * 64 + lane] = chain_frag<T>([&](int t) { return Z[t][0]; }, kgi);
@@ -845,7 +792,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
     return v;
   };
   auto cons_seg3 = [&](int c, int s) __attribute__((always_inline)) {
-    if constexpr (!OUTW) o_rows_out(c, s);
+    if constexpr (!OUTW && !SAVE) o_rows_out(c, s);
     const unsigned char* S = stage(s);
     const int olane = opaque_lane();
     const T* sK = reinterpret_cast<const T*>(S + L::sK);
@@ -1003,6 +950,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
         lds_barrier();
       }
       for (int c = 0; c < nch; ++c) {
+        if constexpr (SAVE) save_state(c);
         cons_seg1(c & 1);
         lds_barrier();
         cons_seg2(c, c & 1);
@@ -1015,6 +963,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
         lds_barrier();
         lds_barrier();
         lds_barrier();
+        if constexpr (SAVE) save_state(c);
         cons_seg1(0);
         lds_barrier();
         cons_seg2(c, 0);
@@ -1036,8 +985,8 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
   }
 }
 
-template <class T, int DK, int DV, int BV, int NSTAGE, int NCW, bool OUTW>
-hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
+template <class T, int DK, int DV, int BV, int NSTAGE, int NCW, bool OUTW, bool SAVE>
+hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
   using L = Layout<T, DK, BV, NSTAGE, NCW, OUTW>;
   static_assert(L::bytes <= 160 * 1024, "LDS budget of one gfx950 compute unit");
   Params p;
@@ -1050,6 +999,9 @@ hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   p.cu = a.cu_seqlens;
   p.o = a.o;
   p.hT = a.final_state;
+  p.save_state = a.save_state;
+  p.save_u = a.save_u;
+  p.chunk_base = a.chunk_base;
   p.T = a.seqlen;
   p.Hqk = a.Hqk;
   p.Hv = a.Hv;
@@ -1059,11 +1011,19 @@ hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   if (p.nunits == 0) return hipSuccess;
   const int units_pad = (p.nunits + 7) / 8 * 8;
   const dim3 grid(units_pad * p.nslices);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<T, DK, DV, BV, NSTAGE, NCW, OUTW>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(L::bytes));
+  hipError_t e = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&prefill_kernel<T, DK, DV, BV, NSTAGE, NCW, OUTW, SAVE>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(L::bytes));
   if (e != hipSuccess) return e;
-  prefill_kernel<T, DK, DV, BV, NSTAGE, NCW, OUTW><<<grid, dim3(64 * (NP + NCW * (OUTW ? 2 : 1))), L::bytes, stream>>>(p);
+  prefill_kernel<T, DK, DV, BV, NSTAGE, NCW, OUTW, SAVE>
+      <<<grid, dim3(64 * (NP + NCW * (OUTW ? 2 : 1))), L::bytes, stream>>>(p);
   return hipGetLastError();
+}
+
+template <class T, int DK, int DV, int BV, int NSTAGE, int NCW, bool OUTW>
+hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
+  return a.save_state ? launch_cfg<T, DK, DV, BV, NSTAGE, NCW, OUTW, true>(a, stream)
+                      : launch_cfg<T, DK, DV, BV, NSTAGE, NCW, OUTW, false>(a, stream);
 }
 
 // dv-slice width and consumer wavefronts.  Every (sequence, head) unit walks

@@ -39,7 +39,8 @@ class Dims(ctypes.Structure):
 DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1}
 
 EXPORTED = ("gdn_fwd_chunked_workspace_size", "gdn_fwd_chunked", "gdn_decode_step", "gdn_decode_verify",
-            "gdn_output_norm_gate", "gdn_short_conv", "gdn_status_string")
+            "gdn_output_norm_gate", "gdn_short_conv", "gdn_bwd_chunked_workspace_size", "gdn_bwd_chunked",
+            "gdn_status_string")
 
 
 def _load():
@@ -62,6 +63,11 @@ def _load():
     i32 = ctypes.c_int32
     lib.gdn_short_conv.argtypes = [i32, i32, i32, vp, i32, i32, i32, ctypes.c_float, ctypes.c_int, vp, fp, vp, vp]
     lib.gdn_short_conv.restype = ctypes.c_int
+    lib.gdn_bwd_chunked_workspace_size.argtypes = [ctypes.POINTER(Dims)]
+    lib.gdn_bwd_chunked_workspace_size.restype = sz
+    lib.gdn_bwd_chunked.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, fp, fp, fp, vp, vp, fp, fp, fp, fp, fp, fp, fp,
+                                    vp, sz, vp]
+    lib.gdn_bwd_chunked.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     return lib
@@ -318,3 +324,64 @@ def short_conv(x, weight, *, cu_seqlens=None, l2norm=False, eps=1e-6, out=None):
                                   DTYPE_CODE[x.dtype], _ptr(x), _ptr(weight), _ptr(out), _stream(dev))
     _check(code)
     return out
+
+
+def bwd_chunked_workspace_size(dims: Dims) -> int:
+    return int(lib.gdn_bwd_chunked_workspace_size(ctypes.byref(dims)))
+
+
+def bwd_chunked(q, k, v, g, beta, d_o, *, initial_state=None, d_final_state=None, cu_seqlens=None, chunk_size=64,
+                scale=1.0, want_d_initial_state=True, workspace=None):
+    """Backward of ``fwd_chunked``: a dict of fp32 gradients dq, dk [B, T, Hqk, dk], dv [B, T, Hv, dv],
+    dg, dbeta [B, T, Hv] and d_initial_state [N, Hv, dk, dv] (None unless ``want_d_initial_state``).
+
+    The inputs are those of the forward pass; ``d_o`` [B, T, Hv, dv] has q's dtype and
+    ``d_final_state`` is fp32 [N, Hv, dk, dv] or None.  ``workspace`` may be a uint8 device tensor of
+    at least ``bwd_chunked_workspace_size`` bytes to reuse; otherwise one is allocated.
+    """
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    _need(q, "q", q.dtype, dev, 4)
+    if q.dtype not in DTYPE_CODE:
+        raise TypeError("q, k, v must be float32 or bfloat16")
+    B, T, Hqk, dk = q.shape
+    _need(k, "k", q.dtype, dev, 4)
+    _need(v, "v", q.dtype, dev, 4)
+    _need(d_o, "d_o", q.dtype, dev, 4)
+    Hv, dv = v.shape[2], v.shape[3]
+    if k.shape != q.shape or v.shape[:2] != (B, T) or d_o.shape != v.shape:
+        raise ValueError("q, k, v, d_o shapes disagree")
+    _need(g, "g", torch.float32, dev, 3)
+    _need(beta, "beta", torch.float32, dev, 3)
+    if g.shape != (B, T, Hv) or beta.shape != (B, T, Hv):
+        raise ValueError("g and beta must be [B, T, Hv]")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev, 1)
+        N = cu_seqlens.shape[0] - 1
+    else:
+        N = B
+    for name, st in (("initial_state", initial_state), ("d_final_state", d_final_state)):
+        if st is not None:
+            _need(st, name, torch.float32, dev, 4)
+            if st.shape != (N, Hv, dk, dv):
+                raise ValueError(f"{name} must be [N, Hv, dk, dv]")
+    f32 = dict(dtype=torch.float32, device=dev)
+    grads = {"dq": torch.empty((B, T, Hqk, dk), **f32), "dk": torch.empty((B, T, Hqk, dk), **f32),
+             "dv": torch.empty((B, T, Hv, dv), **f32), "dg": torch.empty((B, T, Hv), **f32),
+             "dbeta": torch.empty((B, T, Hv), **f32),
+             "d_initial_state": torch.empty((N, Hv, dk, dv), **f32) if want_d_initial_state else None}
+    dims = make_dims(B, T, N, Hqk, Hv, dk, dv, chunk_size, scale, q.dtype)
+    ws_bytes = bwd_chunked_workspace_size(dims)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    else:
+        _need(workspace, "workspace", torch.uint8, dev, 1)
+    with torch.cuda.device(dev):
+        code = lib.gdn_bwd_chunked(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                   _ptr(initial_state), _ptr(cu_seqlens), _ptr(d_o), _ptr(d_final_state),
+                                   _ptr(grads["dq"]), _ptr(grads["dk"]), _ptr(grads["dv"]), _ptr(grads["dg"]),
+                                   _ptr(grads["dbeta"]), _ptr(grads["d_initial_state"]), _ptr(workspace),
+                                   ctypes.c_size_t(workspace.numel()), _stream(dev))
+    _check(code)
+    return grads

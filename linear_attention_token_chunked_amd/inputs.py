@@ -180,6 +180,16 @@ def make_conv(B, T, heads, head_dim, dtype="bf16", seed=0, num_packed=0):
     return out
 
 
+def make_cotangents(B, T, Hv, dv, N, dk, dtype="bf16", seed=0, final=True):
+    """Draw the incoming gradients of a prefill's backward pass: d_o [B, T, Hv, dv] ~ N(0, 1)
+    in the activations' dtype, and d_final [N, Hv, dk, dv] ~ 0.1 N(0, 1) fp32 (or None)."""
+    rng = np.random.default_rng(seed + 7919)
+    return {
+        "d_o": _cast(rng.standard_normal((B, T, Hv, dv)), dtype),
+        "d_final": _cast(0.1 * rng.standard_normal((N, Hv, dk, dv)), "fp32") if final else None,
+    }
+
+
 def make_workload(w: Workload, seed=0, gate_scale=0.1):
     """Inputs for one named workload (see WORKLOADS)."""
     if w.kind == "verify":

@@ -20,10 +20,11 @@ def declared_functions():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gdn_\w+)\s*\(", text, flags=re.M)))
 
 
-def test_header_declares_the_seven_entry_points():
+def test_header_declares_the_nine_entry_points():
     assert declared_functions() == sorted(
-        ["gdn_decode_step", "gdn_decode_verify", "gdn_fwd_chunked", "gdn_fwd_chunked_workspace_size",
-         "gdn_output_norm_gate", "gdn_short_conv", "gdn_status_string"])
+        ["gdn_bwd_chunked", "gdn_bwd_chunked_workspace_size", "gdn_decode_step", "gdn_decode_verify",
+         "gdn_fwd_chunked", "gdn_fwd_chunked_workspace_size", "gdn_output_norm_gate", "gdn_short_conv",
+         "gdn_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -72,7 +73,17 @@ def call_ver(gdn, d, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s_in=FAKE, s_out
                                      P(0))
 
 
-INVALID, NOT_SUPPORTED, MISALIGNED = 1, 2, 3
+def call_bwd(gdn, d, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=0, cu=0, do=FAKE, dhT=0, dq=FAKE, dk=FAKE,
+             dv=FAKE, dg=FAKE, dbeta=FAKE, dh0=0, ws=FAKE, ws_bytes=None):
+    P = ctypes.c_void_p
+    if ws_bytes is None:
+        ws_bytes = gdn.bwd_chunked_workspace_size(d)
+    return gdn.lib.gdn_bwd_chunked(ctypes.byref(d), P(q), P(k), P(v), P(g), P(beta), P(h0), P(cu), P(do), P(dhT),
+                                   P(dq), P(dk), P(dv), P(dg), P(dbeta), P(dh0), P(ws), ctypes.c_size_t(ws_bytes),
+                                   P(0))
+
+
+INVALID, NOT_SUPPORTED, MISALIGNED, WORKSPACE_TOO_SMALL = 1, 2, 3, 4
 
 
 def test_status_strings(gdn):
@@ -189,3 +200,39 @@ def test_short_conv_invalid(gdn):
     assert f(y=FAKE) == INVALID                         # y must not be x
     assert f(w=FAKE + 4) == MISALIGNED
     assert f(T=0) == 0                                  # nothing to do
+
+
+def bwd_ws_bytes(tokens, N, Hv, dk, dv):
+    al = lambda x: (x + 255) // 256 * 256
+    chunks = tokens // 64 + N
+    return al(4 * (N + 1)) + 2 * al(4 * chunks * Hv * dk * dv) + 2 * al(4 * tokens * Hv * dv)
+
+
+def test_bwd_workspace_size(gdn):
+    # chunk offsets, two states per value head and chunk, two fp32 values per token, head and channel
+    assert gdn.bwd_chunked_workspace_size(dims(gdn, B=1, T=128, N=1)) == bwd_ws_bytes(128, 1, 4, 128, 128)
+    assert gdn.bwd_chunked_workspace_size(dims(gdn, B=3, T=100, N=3)) == bwd_ws_bytes(300, 3, 4, 128, 128)
+    assert gdn.lib.gdn_bwd_chunked_workspace_size(None) == 0
+    # floor(total / 64) + N bounds the chunks of any split into N sequences
+    for lens in ([1] * 7, [63, 65, 1], [64, 64], [0, 200, 0, 5]):
+        chunks = sum(-(-n // 64) for n in lens)
+        assert chunks <= sum(lens) // 64 + len(lens)
+
+
+def test_bwd_invalid(gdn):
+    assert call_bwd(gdn, dims(gdn, Hv=3)) == INVALID
+    assert call_bwd(gdn, dims(gdn, N=2)) == INVALID                 # N != B without cu_seqlens
+    assert call_bwd(gdn, dims(gdn, B=2, N=3), cu=FAKE) == INVALID   # packed input needs B == 1
+    assert call_bwd(gdn, dims(gdn, dk=128, dv=64)) == NOT_SUPPORTED
+    assert call_bwd(gdn, dims(gdn, chunk_size=32)) == NOT_SUPPORTED
+    assert call_bwd(gdn, dims(gdn, dtype=0)) == NOT_SUPPORTED       # fp32 is built for dk = 64
+    assert call_bwd(gdn, dims(gdn, dtype=7)) == INVALID
+    assert call_bwd(gdn, dims(gdn), do=0) == INVALID
+    assert call_bwd(gdn, dims(gdn), dg=0) == INVALID
+    assert call_bwd(gdn, dims(gdn), dq=FAKE + 4) == MISALIGNED
+    assert call_bwd(gdn, dims(gdn), dh0=FAKE + 8) == MISALIGNED
+    assert call_bwd(gdn, dims(gdn), ws=FAKE + 64) == MISALIGNED
+    d = dims(gdn)
+    assert call_bwd(gdn, d, ws_bytes=gdn.bwd_chunked_workspace_size(d) - 1) == WORKSPACE_TOO_SMALL
+    assert call_bwd(gdn, d, ws=0) == INVALID
+    assert call_bwd(gdn, dims(gdn, B=0, N=0)) == 0                  # nothing to do
