@@ -203,12 +203,14 @@ gdn_status_t gdn_short_conv(int32_t batch, int32_t seqlen, int32_t num_seqs, con
 
 /*
  * Bytes of device workspace gdn_bwd_chunked needs for these dims, each part
- * rounded up to 256 bytes: (N + 1) int32 chunk offsets; two fp32 states
- * (dk x dv) per value head and chunk, the state entering the chunk and the
- * gradient of the state leaving it, for (floor(B * T / 64) + N) chunks (a bound
- * on the chunks of any split of the tokens into N sequences); and two fp32
- * values per token, value head and value channel (the chunk form's corrected
- * values U and their gradient).  0 for dims with negative sizes.
+ * rounded up to 256 bytes: (N + 1) int32 chunk offsets; two states (dk x dv)
+ * per value head and chunk, the state entering the chunk and the gradient of
+ * the state leaving it, for (floor(B * T / 64) + N) chunks (a bound on the
+ * chunks of any split of the tokens into N sequences); and two values per
+ * token, value head and value channel (the chunk form's corrected values U and
+ * their gradient).  Values are stored in dtype (bf16 inputs: bf16, the
+ * precision in which the matrix cores consume them).  0 for dims with
+ * negative sizes.
  */
 size_t gdn_bwd_chunked_workspace_size(const gdn_dims_t* d);
 

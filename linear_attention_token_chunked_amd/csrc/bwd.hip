@@ -21,15 +21,18 @@
 // and dG from every place G enters (gam, kf, gam_C and the two decay masks),
 // summed into dg by a reverse cumsum inside the chunk.  Three kernels:
 //   1. the forward prefill in its saving variant keeps each chunk's starting
-//      state and U (fp32 workspace);
+//      state and U (in the input's element type: the operands the products use);
 //   2. dstate_kernel walks each (sequence, value head, 32-column slice of dv)
 //      backwards over its chunks, holding dM in registers: it keeps dM' and dZ
 //      per chunk and leaves dM of the first chunk as the initial state's gradient;
-//   3. dlocal_kernel forms every per-token gradient of one chunk and one
-//      query/key head (looping over the value heads that share it, so dq and
-//      dk are summed without atomics), all chunks in parallel.
+//   3. dlocal_kernel forms every per-token gradient of one chunk and one value
+//      head, all chunks in parallel (value heads that share a query/key head
+//      add their dq and dk with atomics).
 // Products run on the matrix cores over 16-wide k-steps with operands in LDS
 // (bf16 inputs: bf16 operands, fp32 accumulation; fp32 inputs: fp32 throughout).
+// Workgroup barriers order LDS only (lds_barrier): the stores to the workspace
+// and the outputs, which no thread of the same kernel reads, stay in flight
+// across them.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -48,8 +51,9 @@ __device__ __forceinline__ typename Vec4<T>::type row4(const T* X, int ld, int l
 // acc (16x16 accumulator tile) += sum_{k < K} opA(m, k) opB(n, k), K a multiple
 // of 16, where opA(m, k) = TA ? A[k][m] : A[m][k] and likewise for B (row
 // strides lda, ldb; A and B point at element (0, 0) of the operands).
-template <class T, bool TA, bool TB>
-__device__ __forceinline__ void tile_mm(floatx4& acc, const T* A, int lda, const T* B, int ldb, int K, int lane) {
+template <class T, bool TA, bool TB, int K>
+__device__ __forceinline__ void tile_mm(floatx4& acc, const T* A, int lda, const T* B, int ldb, int lane) {
+#pragma unroll
   for (int k0 = 0; k0 < K; k0 += 16) {
     const auto fa = TA ? lds_col4<T>(A + k0 * lda, lda, 0, 0, lane) : row4<T>(A + k0, lda, lane);
     const auto fb = TB ? lds_col4<T>(B + k0 * ldb, ldb, 0, 0, lane) : row4<T>(B + k0, ldb, lane);
@@ -57,13 +61,31 @@ __device__ __forceinline__ void tile_mm(floatx4& acc, const T* A, int lda, const
   }
 }
 
-__device__ __forceinline__ float sum16(float x) {  // over the 16 lanes of a row group
-  x += __shfl_xor(x, 1);
-  x += __shfl_xor(x, 2);
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 8);
+// Sum over the 16 lanes of a row group, in every lane of it (DPP row rotations:
+// no LDS round trips).
+// The same product when both operands are read along their rows (no
+// transposes): whole k-groups of the wide matrix-core instruction
+// (bf16: 16x16x32, 16-byte row reads), K a multiple of Mma<T>::KG.
+template <class T, int K>
+__device__ __forceinline__ void tile_mm_nn(floatx4& acc, const T* A, int lda, const T* B, int ldb, int lane) {
+  static_assert(K % Mma<T>::KG == 0, "whole k-groups");
+  const T* ar = A + (lane & 15) * lda;
+  const T* br = B + (lane & 15) * ldb;
+#pragma unroll
+  for (int kg = 0; kg < K / Mma<T>::KG; ++kg) Mma<T>::mma(acc, lds_frag<T>(ar, kg, lane), lds_frag<T>(br, kg, lane));
+}
+
+__device__ __forceinline__ float sum16(float x) {
+#define GDN_ROR_ADD(n) \
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + (n), 0xf, 0xf, false))
+  GDN_ROR_ADD(8);
+  GDN_ROR_ADD(4);
+  GDN_ROR_ADD(2);
+  GDN_ROR_ADD(1);
+#undef GDN_ROR_ADD
   return x;
 }
+__device__ __forceinline__ floatx4 vec4_at(const float* v) { return *reinterpret_cast<const floatx4*>(v); }
 __device__ __forceinline__ float rdlane(float x, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }
@@ -78,15 +100,45 @@ __device__ __forceinline__ void store4(D* p, const floatx4& v) {
   *reinterpret_cast<typename Vec4<D>::type*>(p) = pack4<D>(v[0], v[1], v[2], v[3]);
 }
 
-// Rows [0, C) of W columns from a token-major source (row stride ss elements)
-// into an LDS tile (row stride ld); rows >= L are zero.
-template <class S, class D, int W>
-__device__ __forceinline__ void stage_rows(D* dst, int ld, const S* src, size_t ss, int L, int tid, int nt) {
-  constexpr int PR = W / 4;
-  for (int i = tid; i < C * PR; i += nt) {
-    const int t = i / PR, e = (i - t * PR) * 4;
-    const floatx4 v = t < L ? load4(src + t * ss + e) : zero4();
-    store4<D>(dst + t * ld + e, v);
+// Rows of a row-major tile held in registers on their way to LDS, as raw
+// 4-element vectors: R rows of W columns, NT threads (rows >= L read as zero).
+template <class T, int W, int NT, int R = C>
+struct RowsInFlight {
+  static constexpr int PR = W / 4, N = R * PR, IT = (N + NT - 1) / NT;
+  typename Vec4<T>::type v[IT];
+  __device__ __forceinline__ void load(const T* src, size_t ss, int L, int tid) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int i = tid + it * NT, t = i / PR, e = (i - t * PR) * 4;
+      if (i < N && t < L) v[it] = *reinterpret_cast<const typename Vec4<T>::type*>(src + t * ss + e);
+      else v[it] = typename Vec4<T>::type{};
+    }
+  }
+  __device__ __forceinline__ void store(T* dst, int ld, int tid) const {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int i = tid + it * NT, t = i / PR, e = (i - t * PR) * 4;
+      if (i < N) *reinterpret_cast<typename Vec4<T>::type*>(dst + t * ld + e) = v[it];
+    }
+  }
+};
+
+// R rows of W columns from a row-major source (row stride ss elements) into an
+// LDS tile (row stride ld); rows >= L are zero.  Every load is issued before
+// the first store, so the workgroup waits for memory once.
+template <class S, class D, int W, int NT, int R = C>
+__device__ __forceinline__ void stage_rows(D* dst, int ld, const S* src, size_t ss, int L, int tid) {
+  constexpr int PR = W / 4, N = R * PR, IT = (N + NT - 1) / NT;
+  floatx4 v[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int i = tid + it * NT, t = i / PR, e = (i - t * PR) * 4;
+    v[it] = (i < N && t < L) ? load4(src + t * ss + e) : zero4();
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int i = tid + it * NT, t = i / PR, e = (i - t * PR) * 4;
+    if (i < N) store4<D>(dst + t * ld + e, v[it]);
   }
 }
 
@@ -120,8 +172,8 @@ struct BwdParams {
   const void *q, *k, *v, *dout;
   const float *g, *beta, *dhT;
   const int32_t *cu, *cpre;
-  const float *ck_state, *ck_u;  // chunk-start states, U (from the saving prefill)
-  float *dm, *dz;                // dM' per chunk, dZ per token (dstate_kernel)
+  const void *ck_state, *ck_u;  // chunk-start states, U (from the saving prefill), element type T
+  void *dm, *dz;                // dM' per chunk, dZ per token (dstate_kernel), element type T
   float *dq, *dk, *dv, *dg, *dbeta, *dh0;
   int T, N, Hqk, Hv, chunk_bound;
   float scale;
@@ -130,12 +182,15 @@ struct BwdParams {
 // ------------------------------------------------------- state gradient scan
 template <class T, int DK, int BV>
 struct DsLayout {
-  static constexpr int PAD = 32 / sizeof(T);  // 32-byte row padding
+  static constexpr int PAD = sizeof(T) == 2 ? 16 : 4;  // row padding: 32 bytes (bf16), 16 (fp32, to fit twice)
   static constexpr int LDK = DK + PAD, LDB = BV + PAD, LDC = C + PAD, LDD = 16 + PAD, LDF = BV + 4, LDT = 20;
-  static constexpr int oK = 0;
-  static constexpr int oQ = oK + C * LDK * sizeof(T);
-  static constexpr int odO = oQ + C * LDK * sizeof(T);
-  static constexpr int odOg = odO + C * LDB * sizeof(T);  // s gam dO
+  // a chunk's inputs, double-buffered: K, Q, the dO slice, the gate vectors
+  static constexpr int iK = 0;
+  static constexpr int iQ = iK + C * LDK * sizeof(T);
+  static constexpr int idO = iQ + C * LDK * sizeof(T);
+  static constexpr int iVec = idO + C * LDB * sizeof(T);
+  static constexpr int in_bytes = iVec + (V_N * C + 4) * 4;
+  static constexpr int odOg = 2 * in_bytes;  // s gam dO
   static constexpr int odZ = odOg + C * LDB * sizeof(T);
   static constexpr int odZb = odZ + C * LDB * sizeof(T);  // -beta gam dZ
   static constexpr int odMn = odZb + C * LDB * sizeof(T);
@@ -144,21 +199,22 @@ struct DsLayout {
   static constexpr int oTd = oA + C * LDC * sizeof(T);  // diagonal blocks of (I + A)^-1, row-major
   static constexpr int odU = oTd + 4 * 16 * LDD * sizeof(T);  // fp32
   static constexpr int oAt = odU + C * LDF * 4;               // fp32 diagonal blocks of A, transposed
-  static constexpr int oVec = oAt + 4 * 16 * LDT * 4;
-  static constexpr int bytes = oVec + (V_N * C + 4) * 4;
+  static constexpr int bytes = oAt + 4 * 16 * LDT * 4;
+  static_assert(in_bytes % 16 == 0, "aligned buffers");
 };
 
 template <class T, int DK, int DV, int BV>
-__global__ __launch_bounds__(256) void dstate_kernel(BwdParams p) {
+__global__ __launch_bounds__(512) void dstate_kernel(BwdParams p) {
   using L = DsLayout<T, DK, BV>;
   constexpr int LDK = L::LDK, LDB = L::LDB, LDC = L::LDC, LDD = L::LDD, LDF = L::LDF, LDT = L::LDT;
-  constexpr int NJ = BV / 16;              // column tiles of the slice
-  constexpr int NMT = (DK / 16) * NJ / 4;  // dM tiles per wavefront
-  static_assert((DK / 16) * NJ % 4 == 0 && 4 * NJ % 4 == 0, "tiles split over four wavefronts");
+  constexpr int NW = 8, NT = 64 * NW;       // wavefronts, threads
+  constexpr int NJ = BV / 16;               // column tiles of the slice (one solving wavefront each)
+  constexpr int NST = 64 * (NW - NJ);       // threads that stage the next chunk meanwhile
+  constexpr int NTL = (DK / 16) * NJ;       // dM tiles
+  constexpr int NMT = (NTL + NW - 1) / NW;  // dM tiles per wavefront (some idle when NTL < NW)
+  static_assert(NTL % NW == 0 || NTL < NW, "tiles split over the wavefronts");
+  static_assert(4 * NJ <= NW, "one wavefront per dU tile");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  T* sK = reinterpret_cast<T*>(smem + L::oK);
-  T* sQ = reinterpret_cast<T*>(smem + L::oQ);
-  T* sdO = reinterpret_cast<T*>(smem + L::odO);
   T* sdOg = reinterpret_cast<T*>(smem + L::odOg);
   T* sdZ = reinterpret_cast<T*>(smem + L::odZ);
   T* sdZb = reinterpret_cast<T*>(smem + L::odZb);
@@ -168,90 +224,120 @@ __global__ __launch_bounds__(256) void dstate_kernel(BwdParams p) {
   T* sTd = reinterpret_cast<T*>(smem + L::oTd);
   float* sdU = reinterpret_cast<float*>(smem + L::odU);
   float* sAt = reinterpret_cast<float*>(smem + L::oAt);
-  float* vec = reinterpret_cast<float*>(smem + L::oVec);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lr = lane & 15;
+  // workgroup -> (unit, slice); a unit's slices get ids 8 apart and so share one XCD's L2
   constexpr int NS = DV / BV;
-  const int unit = blockIdx.x / NS;
-  const int col0 = (blockIdx.x - unit * NS) * BV;
+  const int rest = blockIdx.x >> 3, slice = rest % NS;
+  const int unit = (blockIdx.x & 7) + 8 * (rest / NS);
+  if (unit >= p.N * p.Hv) return;
+  const int col0 = slice * BV;
   const int n = unit / p.Hv, h = unit - n * p.Hv, hq = h / (p.Hv / p.Hqk);
   const Seq sq = seq_of(p.cu, p.cpre, p.T, n);
   const int nch = (sq.eos - sq.bos + C - 1) / C;
   const size_t sbase = static_cast<size_t>(unit) * DK * DV;
-  const T* qg = static_cast<const T*>(p.q);
-  const T* kg = static_cast<const T*>(p.k);
-  const T* dog = static_cast<const T*>(p.dout);
   const size_t qk_tok = static_cast<size_t>(p.Hqk) * DK, v_tok = static_cast<size_t>(p.Hv) * DV;
 
-  // dM tiles of this wavefront: tile t = wave + 4i -> rows 16 (t / NJ), columns 16 (t % NJ)
-  floatx4 dM[NMT];
+  // chunk c's inputs into buffer c & 1, by threads [t0, t0 + NTH) (gates: the first of their wavefronts)
+  auto stage_in = [&](int c, int t0, auto nth) __attribute__((always_inline)) {
+    constexpr int NTH = decltype(nth)::value;
+    unsigned char* B = smem + (c & 1) * L::in_bytes;
+    const int cs = sq.bos + c * C, Lc = min(C, sq.eos - cs), t = tid - t0;
+    const size_t qo = static_cast<size_t>(cs) * qk_tok + static_cast<size_t>(hq) * DK;
+    RowsInFlight<T, DK, NTH> rk, rq;
+    RowsInFlight<T, BV, NTH> rdo;
+    rk.load(static_cast<const T*>(p.k) + qo, qk_tok, Lc, t);
+    rq.load(static_cast<const T*>(p.q) + qo, qk_tok, Lc, t);
+    rdo.load(static_cast<const T*>(p.dout) + static_cast<size_t>(cs) * v_tok + static_cast<size_t>(h) * DV + col0, v_tok,
+             Lc, t);
+    if (t < 64) {
+      const size_t gi = static_cast<size_t>(cs) * p.Hv + h;
+      gate_vectors(reinterpret_cast<float*>(B + L::iVec), p.g + gi, p.beta + gi, p.Hv, Lc, lane);
+    }
+    rk.store(reinterpret_cast<T*>(B + L::iK), LDK, t);
+    rq.store(reinterpret_cast<T*>(B + L::iQ), LDK, t);
+    rdo.store(reinterpret_cast<T*>(B + L::idO), LDB, t);
+  };
+  // dM' as matrix-core operands
+  floatx4 dM[NMT];  // tile t = wave + NW i -> rows 16 (t / NJ), columns 16 (t % NJ)
+  auto dm_to_lds = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NMT; ++i) {
+      const int t = wave + NW * i, a = t / NJ, jc = t % NJ;
+      if (t >= NTL) break;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sdMn[(16 * a + 4 * lg + r) * LDB + 16 * jc + lr] = from_float<T>(dM[i][r]);
+    }
+  };
+
 #pragma unroll
   for (int i = 0; i < NMT; ++i) {
-    const int t = wave + 4 * i, a = t / NJ, jc = t % NJ;
+    const int t = wave + NW * i, a = t / NJ, jc = t % NJ;
+    if (t >= NTL) break;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       dM[i][r] = p.dhT ? p.dhT[sbase + static_cast<size_t>(16 * a + 4 * lg + r) * DV + col0 + 16 * jc + lr] : 0.f;
   }
+  if (nch > 0) stage_in(nch - 1, 0, std::integral_constant<int, NT>());
+  dm_to_lds();
+  lds_barrier();
 
   for (int c = nch - 1; c >= 0; --c) {
     const int cs = sq.bos + c * C, Lc = min(C, sq.eos - cs);
-    // -- stage: K, Q, dO slice, gates; dM' to LDS (operands) and to the workspace
-    stage_rows<T, T, DK>(sK, LDK, kg + static_cast<size_t>(cs) * qk_tok + static_cast<size_t>(hq) * DK, qk_tok, Lc,
-                         tid, 256);
-    stage_rows<T, T, DK>(sQ, LDK, qg + static_cast<size_t>(cs) * qk_tok + static_cast<size_t>(hq) * DK, qk_tok, Lc,
-                         tid, 256);
-    stage_rows<T, T, BV>(sdO, LDB, dog + static_cast<size_t>(cs) * v_tok + static_cast<size_t>(h) * DV + col0, v_tok,
-                         Lc, tid, 256);
-    if (wave == 0) {
-      const size_t gi = static_cast<size_t>(cs) * p.Hv + h;
-      gate_vectors(vec, p.g + gi, p.beta + gi, p.Hv, Lc, lane);
-    }
+    const unsigned char* B = smem + (c & 1) * L::in_bytes;
+    const T* sK = reinterpret_cast<const T*>(B + L::iK);
+    const T* sQ = reinterpret_cast<const T*>(B + L::iQ);
+    const T* sdO = reinterpret_cast<const T*>(B + L::idO);
+    const float* vec = reinterpret_cast<const float*>(B + L::iVec);
+    // -- dM' of this chunk to the workspace; Gram tiles P and A (lower tiles), s gam dO
     {
-      float* dmw = p.dm + (static_cast<size_t>(sq.cbase + c) * p.Hv + h) * DK * DV;
+      T* dmw = static_cast<T*>(p.dm) + (static_cast<size_t>(sq.cbase + c) * p.Hv + h) * DK * DV;
 #pragma unroll
       for (int i = 0; i < NMT; ++i) {
-        const int t = wave + 4 * i, a = t / NJ, jc = t % NJ;
+        const int t = wave + NW * i, a = t / NJ, jc = t % NJ;
+        if (t >= NTL) break;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * a + 4 * lg + r, col = 16 * jc + lr;
-          sdMn[row * LDB + col] = from_float<T>(dM[i][r]);
-          dmw[static_cast<size_t>(row) * DV + col0 + col] = dM[i][r];
-        }
+        for (int r = 0; r < 4; ++r)
+          dmw[static_cast<size_t>(16 * a + 4 * lg + r) * DV + col0 + 16 * jc + lr] = from_float<T>(dM[i][r]);
       }
     }
-    __syncthreads();
-    // -- Gram tiles: P and A (lower tiles), s gam dO
     {
       const float s = p.scale;
-      for (int job = wave; job < 20; job += 4) {
+      for (int job = wave; job < 20; job += NW) {
         const int kind = job / 10, lt = job % 10;  // lower tile lt -> (ti, tj)
         const int ti = lt < 1 ? 0 : lt < 3 ? 1 : lt < 6 ? 2 : 3;
         const int tj = lt - ti * (ti + 1) / 2;
         floatx4 acc = zero4();
-        tile_mm<T, false, false>(acc, (kind ? sK : sQ) + 16 * ti * LDK, LDK, sK + 16 * tj * LDK, LDK, DK, lane);
-        const int j = 16 * tj + lr;
+        tile_mm_nn<T, DK>(acc, (kind ? sK : sQ) + 16 * ti * LDK, LDK, sK + 16 * tj * LDK, LDK, lane);
+        const int j = 16 * tj + lr, i0 = 16 * ti + 4 * lg;
+        const floatx4 Gi = vec4_at(vec + V_GL * C + i0), bi = vec4_at(vec + V_BETA * C + i0);
+        const float Gj = vec[V_GL * C + j];
+        float val[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * ti + 4 * lg + r;
-          const float dec = j <= i ? __builtin_amdgcn_exp2f(vec[V_GL * C + i] - vec[V_GL * C + j]) : 0.f;
-          if (kind == 0) {
-            sP[i * LDC + j] = from_float<T>(s * dec * acc[r]);
-          } else {
-            const float a = j < i ? vec[V_BETA * C + i] * dec * acc[r] : 0.f;
-            sA[i * LDC + j] = from_float<T>(a);
-            if (ti == tj) sAt[(ti * 16 + (j & 15)) * LDT + (i & 15)] = a;
-          }
+        for (int r = 0; r < 4; ++r) {  // branch-free: the masks are selects
+          const int i = i0 + r;
+          const float e = __builtin_amdgcn_exp2f(Gi[r] - Gj);
+          val[r] = kind == 0 ? (j <= i ? s * e * acc[r] : 0.f) : (j < i ? bi[r] * e * acc[r] : 0.f);
         }
+        T* dst = kind == 0 ? sP : sA;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[(i0 + r) * LDC + j] = from_float<T>(val[r]);
+        if (kind == 0 && ti != tj) {  // the tile above the diagonal is zero
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sP[j * LDC + i0 + r] = from_float<T>(0.f);
+        }
+        if (kind == 1 && ti == tj)
+          *reinterpret_cast<floatx4*>(sAt + (ti * 16 + lr) * LDT + 4 * lg) = floatx4{val[0], val[1], val[2], val[3]};
       }
-      for (int i = tid; i < C * BV; i += 256) {
+      for (int i = tid; i < C * BV; i += NT) {
         const int t = i / BV, cc = i - t * BV;
         sdOg[t * LDB + cc] = from_float<T>(s * vec[V_GAM * C + t] * to_float(sdO[t * LDB + cc]));
       }
     }
-    __syncthreads();
+    lds_barrier();
     // -- inverses of the diagonal blocks of I + A; dU = P^T dO + diag(kf) K dM'
-    {
+    if (wave < 4) {
       const int cc = lane >> 2, q = lane & 3;
       floatx4 x;
 #pragma unroll
@@ -260,60 +346,72 @@ __global__ __launch_bounds__(256) void dstate_kernel(BwdParams p) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) sTd[(wave * 16 + 4 * q + t) * LDD + cc] = from_float<T>(x[t]);
     }
-    for (int t = wave; t < 4 * NJ; t += 4) {
-      const int bt = t / NJ, jc = t % NJ;
+    if (wave < 4 * NJ) {
+      const int bt = wave / NJ, jc = wave % NJ;
       floatx4 acc = zero4(), acc2 = zero4();
-      tile_mm<T, true, true>(acc, sP + 16 * bt * LDC + 16 * bt, LDC, sdO + 16 * bt * LDB + 16 * jc, LDB, C - 16 * bt,
-                             lane);
-      tile_mm<T, false, true>(acc2, sK + 16 * bt * LDK, LDK, sdMn + 16 * jc, LDB, DK, lane);
+      tile_mm<T, true, true, C>(acc, sP + 16 * bt, LDC, sdO + 16 * jc, LDB, lane);
+      tile_mm<T, false, true, DK>(acc2, sK + 16 * bt * LDK, LDK, sdMn + 16 * jc, LDB, lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 16 * bt + 4 * lg + r;
         sdU[row * LDF + 16 * jc + lr] = acc[r] + vec[V_KF * C + row] * acc2[r];
       }
     }
-    __syncthreads();
-    // -- dZ = (I + A)^-T dU by blocks, last block first; one wavefront per column tile
+    lds_barrier();
+    // -- dZ = (I + A)^-T dU by blocks, last block first, one wavefront per column tile;
+    //    the other wavefronts stage the next chunk meanwhile
     if (wave < NJ) {
       const int jc = wave;
-      float* dzw = p.dz + (static_cast<size_t>(cs) * p.Hv + h) * DV + col0 + 16 * jc + lr;
+      const size_t o0 = (static_cast<size_t>(cs) * p.Hv + h) * DV + col0 + 16 * jc + lr;
+      T* dzw = static_cast<T*>(p.dz) + o0;
+      float* dvw = p.dv + o0;
 #pragma unroll
       for (int b = 3; b >= 0; --b) {
         floatx4 w, sub = zero4();
 #pragma unroll
         for (int r = 0; r < 4; ++r) w[r] = sdU[(16 * b + 4 * lg + r) * LDF + 16 * jc + lr];
         for (int m = b + 1; m < 4; ++m)
-          tile_mm<T, true, true>(sub, sA + 16 * m * LDC + 16 * b, LDC, sdZ + 16 * m * LDB + 16 * jc, LDB, 16, lane);
+          tile_mm<T, true, true, 16>(sub, sA + 16 * m * LDC + 16 * b, LDC, sdZ + 16 * m * LDB + 16 * jc, LDB, lane);
         w -= sub;
         floatx4 u = zero4();
         Mma16<T>::mma(u, lds_col4<T>(sTd + b * 16 * LDD, LDD, 0, 0, lane), Mma16<T>::chain(w));
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * b + 4 * lg + r;
-          sdZ[row * LDB + 16 * jc + lr] = from_float<T>(u[r]);
-          sdZb[row * LDB + 16 * jc + lr] = from_float<T>(-vec[V_BETA * C + row] * vec[V_GAM * C + row] * u[r]);
-          if (row < Lc) dzw[static_cast<size_t>(row) * v_tok] = u[r];
+          const T zt = from_float<T>(u[r]);
+          const float bt = vec[V_BETA * C + row];
+          sdZ[row * LDB + 16 * jc + lr] = zt;
+          sdZb[row * LDB + 16 * jc + lr] = from_float<T>(-bt * vec[V_GAM * C + row] * u[r]);
+          if (row < Lc) {
+            dzw[static_cast<size_t>(row) * v_tok] = zt;
+            dvw[static_cast<size_t>(row) * v_tok] = bt * u[r];
+          }
         }
       }
+    } else if (c > 0) {
+      stage_in(c - 1, 64 * NJ, std::integral_constant<int, NST>());
     }
-    __syncthreads();
-    // -- dM = gam_C dM' + s Q^T diag(gam) dO - K^T diag(beta gam) dZ
+    lds_barrier();
+    // -- dM = gam_C dM' + s Q^T diag(gam) dO - K^T diag(beta gam) dZ, then its operand copy
     {
       const float gC = vec[V_N * C];
 #pragma unroll
       for (int i = 0; i < NMT; ++i) {
-        const int t = wave + 4 * i, a = t / NJ, jc = t % NJ;
+        const int t = wave + NW * i, a = t / NJ, jc = t % NJ;
+        if (t >= NTL) break;
         dM[i] *= gC;
-        tile_mm<T, true, true>(dM[i], sQ + 16 * a, LDK, sdOg + 16 * jc, LDB, C, lane);
-        tile_mm<T, true, true>(dM[i], sK + 16 * a, LDK, sdZb + 16 * jc, LDB, C, lane);
+        tile_mm<T, true, true, C>(dM[i], sQ + 16 * a, LDK, sdOg + 16 * jc, LDB, lane);
+        tile_mm<T, true, true, C>(dM[i], sK + 16 * a, LDK, sdZb + 16 * jc, LDB, lane);
       }
+      dm_to_lds();  // (dU, the only reader, is done: the barrier above)
     }
-    __syncthreads();
+    lds_barrier();
   }
   if (p.dh0) {
 #pragma unroll
     for (int i = 0; i < NMT; ++i) {
-      const int t = wave + 4 * i, a = t / NJ, jc = t % NJ;
+      const int t = wave + NW * i, a = t / NJ, jc = t % NJ;
+      if (t >= NTL) break;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         p.dh0[sbase + static_cast<size_t>(16 * a + 4 * lg + r) * DV + col0 + 16 * jc + lr] = dM[i][r];
@@ -361,7 +459,7 @@ __global__ __launch_bounds__(512) void dlocal_kernel(BwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lr = lane & 15;
-  const int gc = blockIdx.x / p.Hqk, hq = blockIdx.x - (blockIdx.x / p.Hqk) * p.Hqk;
+  const int gc = blockIdx.x / p.Hv, h = blockIdx.x - (blockIdx.x / p.Hv) * p.Hv;
   // the chunk's sequence: the last n with chunk base <= gc
   int n, c;
   if (p.cu) {
@@ -382,194 +480,221 @@ __global__ __launch_bounds__(512) void dlocal_kernel(BwdParams p) {
   }
   const Seq sq = seq_of(p.cu, p.cpre, p.T, n);
   const int cs = sq.bos + c * C, Lc = min(C, sq.eos - cs);
-  const int rep = p.Hv / p.Hqk;
+  const int rep = p.Hv / p.Hqk, hq = h / rep;
   const size_t qk_tok = static_cast<size_t>(p.Hqk) * DK, v_tok = static_cast<size_t>(p.Hv) * DV;
-  const T* qg = static_cast<const T*>(p.q);
-  const T* kg = static_cast<const T*>(p.k);
   const T* vg = static_cast<const T*>(p.v);
-  const T* dog = static_cast<const T*>(p.dout);
   const float s = p.scale;
+  const size_t ck = (static_cast<size_t>(sq.cbase + c) * p.Hv + h) * DK * DV;
+  const size_t qo = static_cast<size_t>(cs) * qk_tok + static_cast<size_t>(hq) * DK;
+  const size_t vo = static_cast<size_t>(cs) * v_tok + static_cast<size_t>(h) * DV;
+  // dq, dk: value heads that share a query/key head add into the same rows
+  auto put = [&](float* dst, size_t off, float x) {
+    if (rep == 1) dst[off] = x;
+    else atomicAdd(dst + off, x);
+  };
 
-  stage_rows<T, T, DK>(sQ, LDK, qg + static_cast<size_t>(cs) * qk_tok + static_cast<size_t>(hq) * DK, qk_tok, Lc,
-                       tid, NT);
-  stage_rows<T, T, DK>(sK, LDK, kg + static_cast<size_t>(cs) * qk_tok + static_cast<size_t>(hq) * DK, qk_tok, Lc,
-                       tid, NT);
+  // -- stage: Q, K, dO, U, dZ, M; gates
   if (tid < C) {
     sdG[tid] = 0.f;
     sdB[tid] = 0.f;
   }
-  __syncthreads();  // (the staging below adds into sdB)
-  // output tiles of this wavefront: tile t = wave + 8i -> rows 16 (t / KTL), key columns 16 (t % KTL)
-  floatx4 dqa[NOT], dka[NOT];
-#pragma unroll
-  for (int i = 0; i < NOT; ++i) dqa[i] = dka[i] = zero4();
-
-  for (int hh = 0; hh < rep; ++hh) {
-    const int h = hq * rep + hh;
-    const size_t ck = (static_cast<size_t>(sq.cbase + c) * p.Hv + h) * DK * DV;
-    // -- stage: dO, U, dZ, M; gates; dv = beta dZ and the dZ . v part of dbeta
-    stage_rows<T, T, DV>(sdO, LDV, dog + static_cast<size_t>(cs) * v_tok + static_cast<size_t>(h) * DV, v_tok, Lc,
-                         tid, NT);
-    stage_rows<float, T, DV>(sU, LDV, p.ck_u + static_cast<size_t>(cs) * v_tok + static_cast<size_t>(h) * DV, v_tok,
-                             Lc, tid, NT);
-    for (int i = tid; i < DK * DV / 4; i += NT) {
-      const int r = i / (DV / 4), e = (i - r * (DV / 4)) * 4;
-      store4<T>(sM + r * LDV + e, load4(p.ck_state + ck + static_cast<size_t>(r) * DV + e));
-    }
+  {
+    RowsInFlight<T, DK, NT> rq, rk;
+    RowsInFlight<T, DV, NT> rdo, ru, rdz;
+    RowsInFlight<T, DV, NT, DK> rm;
+    rq.load(static_cast<const T*>(p.q) + qo, qk_tok, Lc, tid);
+    rk.load(static_cast<const T*>(p.k) + qo, qk_tok, Lc, tid);
+    rdo.load(static_cast<const T*>(p.dout) + vo, v_tok, Lc, tid);
+    ru.load(static_cast<const T*>(p.ck_u) + vo, v_tok, Lc, tid);
+    rdz.load(static_cast<const T*>(p.dz) + vo, v_tok, Lc, tid);
+    rm.load(static_cast<const T*>(p.ck_state) + ck, DV, DK, tid);
     if (wave == 0) {
       const size_t gi = static_cast<size_t>(cs) * p.Hv + h;
       gate_vectors(vec, p.g + gi, p.beta + gi, p.Hv, Lc, lane);
     }
-    for (int i = tid; i < C * (DV / 4); i += NT) {  // 16 lanes per row when DV = 64, 32 when DV = 128
-      const int t = i / (DV / 4), e = (i - t * (DV / 4)) * 4;
-      floatx4 z = zero4(), vv = zero4();
-      if (t < Lc) {
-        const size_t off = static_cast<size_t>(cs + t) * v_tok + static_cast<size_t>(h) * DV + e;
-        z = load4(p.dz + off);
-        vv = load4(vg + off);
-        const float bt = p.beta[static_cast<size_t>(cs + t) * p.Hv + h];
-        *reinterpret_cast<floatx4*>(p.dv + off) = z * bt;
-      }
-      store4<T>(sdZ + t * LDV + e, z);
-      float part = z[0] * vv[0] + z[1] * vv[1] + z[2] * vv[2] + z[3] * vv[3];
+    rq.store(sQ, LDK, tid);
+    rk.store(sK, LDK, tid);
+    rdo.store(sdO, LDV, tid);
+    ru.store(sU, LDV, tid);
+    rdz.store(sdZ, LDV, tid);
+    rm.store(sM, LDV, tid);
+  }
+  lds_barrier();
+  {  // the dZ . v part of dbeta (dZ from LDS, v from memory)
+    constexpr int PR = DV / 4, IT = C * PR / NT;
+    static_assert(C * PR % NT == 0 && NT % PR == 0, "whole rows per pass");
+    floatx4 vv[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int i = tid + it * NT, t = i / PR, e = (i - t * PR) * 4;
+      vv[it] = t < Lc ? load4(vg + vo + static_cast<size_t>(t) * v_tok + e) : zero4();
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int i = tid + it * NT, t = i / PR, e = (i - t * PR) * 4;
+      float part = 0.f;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) part += to_float(sdZ[t * LDV + e + x]) * vv[it][x];
       if (t < Lc) atomicAdd(&sdB[t], part);
     }
-    __syncthreads();
-    // -- C x C tiles: dP (masked, times s exp(G_i - G_j)) and D + D^T; the M products
-    for (int job = wave; job < 20; job += 8) {
-      const int kind = job / 10, lt = job % 10;
-      const int ti = lt < 1 ? 0 : lt < 3 ? 1 : lt < 6 ? 2 : 3;
-      const int tj = lt - ti * (ti + 1) / 2;
-      floatx4 gr = zero4(), d = zero4();
-      tile_mm<T, false, false>(gr, (kind ? sK : sQ) + 16 * ti * LDK, LDK, sK + 16 * tj * LDK, LDK, DK, lane);
-      tile_mm<T, false, false>(d, (kind ? sdZ : sdO) + 16 * ti * LDV, LDV, sU + 16 * tj * LDV, LDV, DV, lane);
-      const int j = 16 * tj + lr;
-      float colsum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * ti + 4 * lg + r;
-        const float dec = j <= i ? __builtin_amdgcn_exp2f(vec[V_GL * C + i] - vec[V_GL * C + j]) : 0.f;
-        float w, rowb = 0.f;
-        if (kind == 0) {  // P_ij = s dec (QK^T)_ij, dP_ij = (dO U^T)_ij, j <= i
-          const bool on = j <= i;
-          const float dp = on ? d[r] : 0.f;
-          w = dp * s * dec * gr[r];
-          sdP[i * LDC + j] = from_float<T>(dp * s * dec);
-        } else {  // A_ij = beta_i dec (KK^T)_ij, dA_ij = -(dZ U^T)_ij, j < i
-          const bool on = j < i;
-          const float da = on ? -d[r] : 0.f;
-          const float bi = vec[V_BETA * C + i];
-          w = da * bi * dec * gr[r];
-          rowb = da * dec * gr[r];
-          const T dd = from_float<T>(da * bi * dec);
-          if (on) {
-            sS[i * LDC + j] = dd;
-            sS[j * LDC + i] = dd;
-          } else if (i == j) {
-            sS[i * LDC + j] = from_float<T>(0.f);
-          }
-        }
-        colsum += w;
-        const float rw = sum16(w), rb = sum16(rowb);
-        if (lr == 0) {
-          atomicAdd(&sdG[i], rw);
-          if (kind) atomicAdd(&sdB[i], rb);
-        }
-      }
-      colsum += __shfl_xor(colsum, 16);
-      colsum += __shfl_xor(colsum, 32);
-      if (lg == 0) atomicAdd(&sdG[j], -colsum);
-    }
-#pragma unroll
-    for (int i = 0; i < NOT; ++i) {
-      const int t = wave + 8 * i, it = t / KTL, kt = t % KTL;
-      floatx4 a = zero4(), b = zero4();
-      tile_mm<T, false, false>(a, sdO + 16 * it * LDV, LDV, sM + 16 * kt * LDV, LDV, DV, lane);  // dO M^T
-      tile_mm<T, false, false>(b, sdZ + 16 * it * LDV, LDV, sM + 16 * kt * LDV, LDV, DV, lane);  // dZ M^T
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * it + 4 * lg + r, key = 16 * kt + lr;
-        const float gam = vec[V_GAM * C + row], bt = vec[V_BETA * C + row];
-        dqa[i][r] += s * gam * a[r];
-        dka[i][r] -= bt * gam * b[r];
-        const float qa = sum16(to_float(sQ[row * LDK + key]) * a[r]);
-        const float kb = sum16(to_float(sK[row * LDK + key]) * b[r]);
-        if (lr == 0) {
-          atomicAdd(&sdG[row], s * gam * qa - bt * gam * kb);
-          atomicAdd(&sdB[row], -gam * kb);
-        }
-      }
-    }
-    __syncthreads();
-    // -- dM' replaces M in LDS; gam_C <dM', M> enters dG at the chunk's end
-    {
-      float part = 0.f;
-      const float* dmp = p.dm + ck;
-      for (int i = tid; i < DK * DV / 4; i += NT) {
-        const int r = i / (DV / 4), e = (i - r * (DV / 4)) * 4;
-        const floatx4 dmv = load4(dmp + static_cast<size_t>(r) * DV + e);
-        const floatx4 mv = load4(p.ck_state + ck + static_cast<size_t>(r) * DV + e);
-        part += dmv[0] * mv[0] + dmv[1] * mv[1] + dmv[2] * mv[2] + dmv[3] * mv[3];
-        store4<T>(sM + r * LDV + e, dmv);
-      }
-      part = sum16(part);
-      part += __shfl_xor(part, 16);
-      part += __shfl_xor(part, 32);
-      if (lane == 0) atomicAdd(&sdG[C - 1], vec[V_N * C] * part);
-    }
-    __syncthreads();
-    // -- dq += (dP s dec) K;  dk += diag(kf) U dM'^T + (dP s dec)^T Q + (D + D^T) K
-#pragma unroll
-    for (int i = 0; i < NOT; ++i) {
-      const int t = wave + 8 * i, it = t / KTL, kt = t % KTL;
-      tile_mm<T, false, true>(dqa[i], sdP + 16 * it * LDC, LDC, sK + 16 * kt, LDK, 16 * (it + 1), lane);
-      floatx4 a = zero4();
-      tile_mm<T, false, false>(a, sU + 16 * it * LDV, LDV, sM + 16 * kt * LDV, LDV, DV, lane);  // U dM'^T
-      float ssum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * it + 4 * lg + r, key = 16 * kt + lr;
-        const float kf = vec[V_KF * C + row];
-        dka[i][r] += kf * a[r];
-        const float sj = kf * sum16(to_float(sK[row * LDK + key]) * a[r]);
-        if (lr == 0) atomicAdd(&sdG[row], -sj);
-        ssum += sj;
-      }
-      if (lr == 0) atomicAdd(&sdG[C - 1], ssum);
-      tile_mm<T, true, true>(dka[i], sdP + 16 * it * LDC + 16 * it, LDC, sQ + 16 * it * LDK + 16 * kt, LDK,
-                             C - 16 * it, lane);
-      tile_mm<T, false, true>(dka[i], sS + 16 * it * LDC, LDC, sK + 16 * kt, LDK, C, lane);
-    }
-    __syncthreads();
-    // -- dg = reverse cumsum of dG over the chunk; dbeta; clear the accumulators
-    if (wave == 0) {
-      const int t = C - 1 - lane;
-      const float dg = wave_inclusive_sum(sdG[t]);
-      const float db = sdB[t];
-      if (t < Lc) {
-        const size_t gi = static_cast<size_t>(cs + t) * p.Hv + h;
-        p.dg[gi] = dg;
-        p.dbeta[gi] = db;
-      }
-      sdG[t] = 0.f;
-      sdB[t] = 0.f;
-    }
-    __syncthreads();
   }
-  // dq, dk (summed over the value heads of this query/key head)
+  // -- C x C tiles: dP (masked, times s exp(G_i - G_j)) and D + D^T, with their dG and dbeta terms
+  for (int job = wave; job < 20; job += 8) {
+    const int kind = job / 10, lt = job % 10;
+    const int ti = lt < 1 ? 0 : lt < 3 ? 1 : lt < 6 ? 2 : 3;
+    const int tj = lt - ti * (ti + 1) / 2;
+    floatx4 gr = zero4(), d = zero4();
+    tile_mm_nn<T, DK>(gr, (kind ? sK : sQ) + 16 * ti * LDK, LDK, sK + 16 * tj * LDK, LDK, lane);
+    tile_mm_nn<T, DV>(d, (kind ? sdZ : sdO) + 16 * ti * LDV, LDV, sU + 16 * tj * LDV, LDV, lane);
+    const int j = 16 * tj + lr, i0 = 16 * ti + 4 * lg;
+    const floatx4 Gi = vec4_at(vec + V_GL * C + i0), bi = vec4_at(vec + V_BETA * C + i0);
+    const float Gj = vec[V_GL * C + j];
+    float colsum = 0.f;
+    floatx4 rw, rb;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {  // branch-free: the masks are selects
+      const int i = i0 + r;
+      const float e = __builtin_amdgcn_exp2f(Gi[r] - Gj);
+      float w, rowb = 0.f;
+      if (kind == 0) {  // P_ij = s dec (QK^T)_ij, dP_ij = (dO U^T)_ij, j <= i
+        const float dps = j <= i ? d[r] * s * e : 0.f;  // dP s dec
+        w = dps * gr[r];
+        sdP[i * LDC + j] = from_float<T>(dps);
+      } else {  // A_ij = beta_i dec (KK^T)_ij, dA_ij = -(dZ U^T)_ij, j < i
+        const float dae = j < i ? -d[r] * e : 0.f;  // dA dec
+        w = dae * bi[r] * gr[r];
+        rowb = dae * gr[r];
+        const T dd = from_float<T>(dae * bi[r]);
+        if (j < i) sS[j * LDC + i] = dd;
+        if (j <= i) sS[i * LDC + j] = dd;  // (zero on the diagonal)
+      }
+      colsum += w;
+      rw[r] = sum16(w);
+      rb[r] = sum16(rowb);
+    }
+    if (kind == 0 && ti != tj) {  // the tile above the diagonal is zero
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sdP[j * LDC + i0 + r] = from_float<T>(0.f);
+    }
+    if (lr == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        atomicAdd(&sdG[i0 + r], rw[r]);
+        if (kind) atomicAdd(&sdB[i0 + r], rb[r]);
+      }
+    }
+    colsum += __shfl_xor(colsum, 16);
+    colsum += __shfl_xor(colsum, 32);
+    if (lg == 0) atomicAdd(&sdG[j], -colsum);
+  }
+  lds_barrier();
+  // -- dq = s diag(gam) dO M^T + (dP s dec) K  (written out);
+  //    dk = -diag(beta gam) dZ M^T + (dP s dec)^T Q + (D + D^T) K  (kept; the dM' term follows)
+  floatx4 dka[NOT];
 #pragma unroll
   for (int i = 0; i < NOT; ++i) {
     const int t = wave + 8 * i, it = t / KTL, kt = t % KTL;
+    floatx4 a = zero4(), b = zero4();
+    tile_mm_nn<T, DV>(a, sdO + 16 * it * LDV, LDV, sM + 16 * kt * LDV, LDV, lane);  // dO M^T
+    tile_mm_nn<T, DV>(b, sdZ + 16 * it * LDV, LDV, sM + 16 * kt * LDV, LDV, lane);  // dZ M^T
+    floatx4 dq = zero4();
+    dka[i] = zero4();
+    {
+      const int r0 = 16 * it + 4 * lg, key = 16 * kt + lr;
+      const floatx4 gam = vec4_at(vec + V_GAM * C + r0), bt = vec4_at(vec + V_BETA * C + r0);
+      floatx4 gq, gk;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        dq[r] = s * gam[r] * a[r];
+        dka[i][r] = -bt[r] * gam[r] * b[r];
+        gq[r] = sum16(to_float(sQ[(r0 + r) * LDK + key]) * a[r]);
+        gk[r] = sum16(to_float(sK[(r0 + r) * LDK + key]) * b[r]);
+      }
+      if (lr == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          atomicAdd(&sdG[r0 + r], s * gam[r] * gq[r] - bt[r] * gam[r] * gk[r]);
+          atomicAdd(&sdB[r0 + r], -gam[r] * gk[r]);
+        }
+      }
+    }
+    tile_mm<T, false, true, C>(dq, sdP + 16 * it * LDC, LDC, sK + 16 * kt, LDK, lane);
+    tile_mm<T, true, true, C>(dka[i], sdP + 16 * it, LDC, sQ + 16 * kt, LDK, lane);
+    tile_mm<T, false, true, C>(dka[i], sS + 16 * it * LDC, LDC, sK + 16 * kt, LDK, lane);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * it + 4 * lg + r;
-      if (row < Lc) {
-        const size_t off = static_cast<size_t>(cs + row) * qk_tok + static_cast<size_t>(hq) * DK + 16 * kt + lr;
-        p.dq[off] = dqa[i][r];
-        p.dk[off] = dka[i][r];
-      }
+      if (row < Lc) put(p.dq, qo + static_cast<size_t>(row) * qk_tok + 16 * kt + lr, dq[r]);
     }
   }
+  // -- dM' replaces M in LDS; gam_C <dM', M> enters dG at the chunk's end
+  {
+    constexpr int PR = DV / 4, IT = DK * PR / NT;
+    static_assert(DK * PR % NT == 0, "whole passes");
+    const T* dmp = static_cast<const T*>(p.dm) + ck;
+    floatx4 dmv[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int i = tid + it * NT, r = i / PR, e = (i - r * PR) * 4;
+      dmv[it] = load4(dmp + static_cast<size_t>(r) * DV + e);
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int i = tid + it * NT, r = i / PR, e = (i - r * PR) * 4;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) part += dmv[it][x] * to_float(sM[r * LDV + e + x]);
+    }
+    part = sum16(part);
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+    if (lane == 0) atomicAdd(&sdG[C - 1], vec[V_N * C] * part);
+    lds_barrier();  // every M value is read before dM' replaces it
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int i = tid + it * NT, r = i / PR, e = (i - r * PR) * 4;
+      store4<T>(sM + r * LDV + e, dmv[it]);
+    }
+  }
+  lds_barrier();
+  // -- dk += diag(kf) U dM'^T, with its dG terms
+#pragma unroll
+  for (int i = 0; i < NOT; ++i) {
+    const int t = wave + 8 * i, it = t / KTL, kt = t % KTL;
+    floatx4 a = zero4();
+    tile_mm_nn<T, DV>(a, sU + 16 * it * LDV, LDV, sM + 16 * kt * LDV, LDV, lane);  // U dM'^T
+    const int r0 = 16 * it + 4 * lg, key = 16 * kt + lr;
+    const floatx4 kf = vec4_at(vec + V_KF * C + r0);
+    floatx4 sj;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      dka[i][r] += kf[r] * a[r];
+      sj[r] = kf[r] * sum16(to_float(sK[(r0 + r) * LDK + key]) * a[r]);
+      if (r0 + r < Lc) put(p.dk, qo + static_cast<size_t>(r0 + r) * qk_tok + key, dka[i][r]);
+    }
+    if (lr == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) atomicAdd(&sdG[r0 + r], -sj[r]);
+      atomicAdd(&sdG[C - 1], sj[0] + sj[1] + sj[2] + sj[3]);
+    }
+  }
+  lds_barrier();
+  // -- dg = reverse cumsum of dG over the chunk; dbeta
+  if (wave == 0) {
+    const int t = C - 1 - lane;
+    const float dg = wave_inclusive_sum(sdG[t]);
+    if (t < Lc) {
+      const size_t gi = static_cast<size_t>(cs + t) * p.Hv + h;
+      p.dg[gi] = dg;
+      p.dbeta[gi] = sdB[t];
+    }
+  }
+}
+
+// Zeroes n floats.
+__global__ void zero_kernel(float* x, size_t n) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) x[i] = 0.f;
 }
 
 // Exclusive prefix sum of the chunk counts of the packed sequences: out[n] is
@@ -599,16 +724,16 @@ __global__ __launch_bounds__(1024) void chunk_prefix_kernel(const int32_t* cu, i
 struct WsParts {
   size_t cpre, state, dm, u, dz, total;
 };
-WsParts ws_parts(int64_t tokens, int N, int Hv, int dk, int dv) {
+WsParts ws_parts(int64_t tokens, int N, int Hv, int dk, int dv, int esize) {
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t chunks = static_cast<size_t>(tokens / C + N);
   WsParts w;
   w.cpre = 0;
   w.state = al(static_cast<size_t>(N + 1) * 4);
-  w.dm = w.state + al(chunks * Hv * dk * dv * 4);
-  w.u = w.dm + al(chunks * Hv * dk * dv * 4);
-  w.dz = w.u + al(static_cast<size_t>(tokens) * Hv * dv * 4);
-  w.total = w.dz + al(static_cast<size_t>(tokens) * Hv * dv * 4);
+  w.dm = w.state + al(chunks * Hv * dk * dv * esize);
+  w.u = w.dm + al(chunks * Hv * dk * dv * esize);
+  w.dz = w.u + al(static_cast<size_t>(tokens) * Hv * dv * esize);
+  w.total = w.dz + al(static_cast<size_t>(tokens) * Hv * dv * esize);
   return w;
 }
 
@@ -618,7 +743,7 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   using LL = DlLayout<T, DK, DV>;
   static_assert(LS::bytes <= 160 * 1024 && LL::bytes <= 160 * 1024, "LDS budget of one gfx950 compute unit");
   const int64_t tokens = static_cast<int64_t>(a.batch) * a.seqlen;
-  const WsParts w = ws_parts(tokens, a.num_seqs, a.Hv, DK, DV);
+  const WsParts w = ws_parts(tokens, a.num_seqs, a.Hv, DK, DV, sizeof(T));
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);  // 256-byte aligned
   int32_t* cpre = a.cu_seqlens ? reinterpret_cast<int32_t*>(ws + w.cpre) : nullptr;
   if (cpre) chunk_prefix_kernel<<<dim3(1), dim3(1024), 0, stream>>>(a.cu_seqlens, a.num_seqs, cpre);
@@ -643,8 +768,8 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   f.chunk = C;
   f.scale = a.scale;
   f.bf16 = sizeof(T) == 2;
-  f.save_state = reinterpret_cast<float*>(ws + w.state);
-  f.save_u = reinterpret_cast<float*>(ws + w.u);
+  f.save_state = ws + w.state;
+  f.save_u = ws + w.u;
   f.chunk_base = cpre;
   hipError_t e = launch_prefill(f, stream);
   if (e != hipSuccess) return e;
@@ -661,8 +786,8 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   p.cpre = cpre;
   p.ck_state = f.save_state;
   p.ck_u = f.save_u;
-  p.dm = reinterpret_cast<float*>(ws + w.dm);
-  p.dz = reinterpret_cast<float*>(ws + w.dz);
+  p.dm = ws + w.dm;
+  p.dz = ws + w.dz;
   p.dq = a.dq;
   p.dk = a.dk;
   p.dv = a.dv;
@@ -680,18 +805,24 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dstate_kernel<T, DK, DV, BV>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, LS::bytes);
   if (e != hipSuccess) return e;
-  dstate_kernel<T, DK, DV, BV><<<dim3(units * (DV / BV)), dim3(256), LS::bytes, stream>>>(p);
+  dstate_kernel<T, DK, DV, BV><<<dim3((units + 7) / 8 * 8 * (DV / BV)), dim3(512), LS::bytes, stream>>>(p);
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dlocal_kernel<T, DK, DV>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, LL::bytes);
   if (e != hipSuccess) return e;
-  dlocal_kernel<T, DK, DV><<<dim3(p.chunk_bound * a.Hqk), dim3(512), LL::bytes, stream>>>(p);
+  if (a.Hv != a.Hqk) {  // value heads that share a query/key head add their dq, dk
+    const size_t nqk = static_cast<size_t>(tokens) * a.Hqk * DK;
+    const dim3 zg(static_cast<unsigned>((nqk + 255) / 256));
+    zero_kernel<<<zg, dim3(256), 0, stream>>>(a.dq, nqk);
+    zero_kernel<<<zg, dim3(256), 0, stream>>>(a.dk, nqk);
+  }
+  dlocal_kernel<T, DK, DV><<<dim3(p.chunk_bound * a.Hv), dim3(512), LL::bytes, stream>>>(p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int64_t tokens, int num_seqs, int Hv, int dk, int dv) {
-  return ws_parts(tokens, num_seqs, Hv, dk, dv).total;
+size_t bwd_workspace_bytes(int64_t tokens, int num_seqs, int Hv, int dk, int dv, bool bf16) {
+  return ws_parts(tokens, num_seqs, Hv, dk, dv, bf16 ? 2 : 4).total;
 }
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
@@ -699,7 +830,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     if (a.head_dim_k == 128 && a.head_dim_v == 128) return launch<bf16, 128, 128, 32>(a, stream);
     if (a.head_dim_k == 64 && a.head_dim_v == 64) return launch<bf16, 64, 64, 32>(a, stream);
   } else {
-    if (a.head_dim_k == 64 && a.head_dim_v == 64) return launch<float, 64, 64, 32>(a, stream);
+    if (a.head_dim_k == 64 && a.head_dim_v == 64) return launch<float, 64, 64, 16>(a, stream);
   }
   return hipErrorInvalidValue;
 }

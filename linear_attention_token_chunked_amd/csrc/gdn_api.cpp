@@ -213,7 +213,7 @@ size_t gdn_bwd_chunked_workspace_size(const gdn_dims_t* d) {
       d->head_dim_v < 1)
     return 0;
   return gdn::bwd_workspace_bytes(static_cast<int64_t>(d->batch) * d->seqlen, d->num_seqs, d->num_v_heads,
-                                  d->head_dim_k, d->head_dim_v);
+                                  d->head_dim_k, d->head_dim_v, d->dtype == GDN_DTYPE_BFLOAT16);
 }
 
 gdn_status_t gdn_bwd_chunked(const gdn_dims_t* d, const void* q, const void* k, const void* v, const float* g,

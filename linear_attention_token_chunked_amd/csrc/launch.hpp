@@ -30,9 +30,10 @@ struct PrefillArgs {
   bool bf16;
   // Set by the backward pass only: keep every chunk's starting state
   // ([chunk][Hv][dk][dv], chunk = chunk_base[n] + local index) and U (the
-  // chunk form's corrected values, [token][Hv][dv]) in fp32, and skip o.
-  float* save_state = nullptr;
-  float* save_u = nullptr;
+  // chunk form's corrected values, [token][Hv][dv]) in the element type of
+  // q, k, v, and skip o.
+  void* save_state = nullptr;
+  void* save_u = nullptr;
   const int32_t* chunk_base = nullptr;  // [N + 1] with cu_seqlens, else null (n * ceil(T / C))
 };
 
@@ -89,7 +90,7 @@ struct BwdArgs {
   float scale;
   bool bf16;
 };
-size_t bwd_workspace_bytes(int64_t tokens, int num_seqs, int Hv, int dk, int dv);
+size_t bwd_workspace_bytes(int64_t tokens, int num_seqs, int Hv, int dk, int dv, bool bf16);
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);

@@ -226,7 +226,7 @@ struct Params {
   const int32_t* cu;
   void* o;
   float* hT;
-  float *save_state, *save_u;
+  void *save_state, *save_u;  // element type T
   const int32_t* chunk_base;
   int T, Hqk, Hv, nunits, nslices;
   float scale;
@@ -336,7 +336,8 @@ template <> struct OutPTiles<0> { static constexpr int n = 4, ti[4] = {0, 1, 1, 
 template <> struct OutPTiles<1> { static constexpr int n = 4, ti[4] = {2, 2, 3, 3}, tj[4] = {1, 2, 1, 2}; };
 
 // SAVE: the variant a backward pass runs first; it keeps each chunk's starting
-// state and U (fp32) and writes no output.
+// state and U (as T, the precision of the products' operands) and writes no
+// output.
 template <class T, int DK, int DV, int BV, int NSTAGE, int NCW, bool OUTW, bool SAVE>
 __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kernel(Params p) {
   using L = Layout<T, DK, BV, NSTAGE, NCW, OUTW>;
@@ -563,13 +564,13 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
   // The state at the start of chunk c (SAVE).
   auto save_state = [&](int c) __attribute__((always_inline)) {
     const int cb = p.chunk_base ? p.chunk_base[n] : n * ((p.T + C - 1) / C);
-    float* d = p.save_state + (static_cast<size_t>(cb + c) * p.Hv + h) * DK * DV;
+    T* d = static_cast<T*>(p.save_state) + (static_cast<size_t>(cb + c) * p.Hv + h) * DK * DV;
 #pragma unroll
     for (int a = 0; a < KT; ++a)
 #pragma unroll
       for (int j = 0; j < NTW; ++j)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) d[slane + MM::state_row(a, 0, s) * DV + 16 * j] = Ms[a][j][s];
+        for (int s = 0; s < 4; ++s) d[slane + MM::state_row(a, 0, s) * DV + 16 * j] = from_float<T>(Ms[a][j][s]);
   };
 
   // seg 1: Y = K M; Z = beta (V - exp(G) Y).  With one state tile per wave the
@@ -766,9 +767,9 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
         for (int i = 0; i < 4; ++i) {
           const int t = 16 * b + 4 * lg + i;
           if (t < Lc) {
-            float* u = p.save_u + (static_cast<size_t>(cs + t) * p.Hv + h) * DV + wcol + lr;
+            T* u = static_cast<T*>(p.save_u) + (static_cast<size_t>(cs + t) * p.Hv + h) * DV + wcol + lr;
 #pragma unroll
-            for (int j = 0; j < NTW; ++j) u[16 * j] = Z[b][j][i];
+            for (int j = 0; j < NTW; ++j) u[16 * j] = from_float<T>(Z[b][j][i]);
           }
         }
     }

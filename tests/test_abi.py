@@ -202,16 +202,19 @@ def test_short_conv_invalid(gdn):
     assert f(T=0) == 0                                  # nothing to do
 
 
-def bwd_ws_bytes(tokens, N, Hv, dk, dv):
+def bwd_ws_bytes(tokens, N, Hv, dk, dv, esize):
     al = lambda x: (x + 255) // 256 * 256
     chunks = tokens // 64 + N
-    return al(4 * (N + 1)) + 2 * al(4 * chunks * Hv * dk * dv) + 2 * al(4 * tokens * Hv * dv)
+    return al(4 * (N + 1)) + 2 * al(esize * chunks * Hv * dk * dv) + 2 * al(esize * tokens * Hv * dv)
 
 
 def test_bwd_workspace_size(gdn):
-    # chunk offsets, two states per value head and chunk, two fp32 values per token, head and channel
-    assert gdn.bwd_chunked_workspace_size(dims(gdn, B=1, T=128, N=1)) == bwd_ws_bytes(128, 1, 4, 128, 128)
-    assert gdn.bwd_chunked_workspace_size(dims(gdn, B=3, T=100, N=3)) == bwd_ws_bytes(300, 3, 4, 128, 128)
+    # chunk offsets, two states per value head and chunk, two values per token, head and channel,
+    # in the element type of q, k, v
+    assert gdn.bwd_chunked_workspace_size(dims(gdn, B=1, T=128, N=1)) == bwd_ws_bytes(128, 1, 4, 128, 128, 2)
+    assert gdn.bwd_chunked_workspace_size(dims(gdn, B=3, T=100, N=3)) == bwd_ws_bytes(300, 3, 4, 128, 128, 2)
+    assert gdn.bwd_chunked_workspace_size(dims(gdn, B=1, T=130, N=1, dk=64, dv=64, dtype=0)) == \
+        bwd_ws_bytes(130, 1, 4, 64, 64, 4)
     assert gdn.lib.gdn_bwd_chunked_workspace_size(None) == 0
     # floor(total / 64) + N bounds the chunks of any split into N sequences
     for lens in ([1] * 7, [63, 65, 1], [64, 64], [0, 200, 0, 5]):
