@@ -146,11 +146,7 @@ __device__ __forceinline__ void stage_rows(D* dst, int ld, const S* src, size_t 
 // inclusive cumsum Gl, exp(G), exp(G_C - G), beta (tokens >= L act as g = 0,
 // beta = 0), and exp(G_C) in vec[4C].
 enum { V_GL, V_GAM, V_KF, V_BETA, V_N };
-__device__ __forceinline__ void gate_vectors(float* vec, const float* g, const float* beta, size_t stride, int L,
-                                             int lane) {
-  const bool live = lane < L;
-  const float gt = live ? g[lane * stride] : 0.f;
-  const float bt = live ? beta[lane * stride] : 0.f;
+__device__ __forceinline__ void gate_vectors_from(float* vec, float gt, float bt, int lane) {
   const float Gl = wave_inclusive_sum(gt) * kLog2e;
   const float GlC = rdlane(Gl, 63);
   vec[V_GL * C + lane] = Gl;
@@ -158,6 +154,11 @@ __device__ __forceinline__ void gate_vectors(float* vec, const float* g, const f
   vec[V_KF * C + lane] = __builtin_amdgcn_exp2f(GlC - Gl);
   vec[V_BETA * C + lane] = bt;
   if (lane == 0) vec[V_N * C] = __builtin_amdgcn_exp2f(GlC);
+}
+__device__ __forceinline__ void gate_vectors(float* vec, const float* g, const float* beta, size_t stride, int L,
+                                             int lane) {
+  const bool live = lane < L;
+  gate_vectors_from(vec, live ? g[lane * stride] : 0.f, live ? beta[lane * stride] : 0.f, lane);
 }
 
 struct Seq {
@@ -482,7 +483,6 @@ __global__ __launch_bounds__(512) void dlocal_kernel(BwdParams p) {
   const int cs = sq.bos + c * C, Lc = min(C, sq.eos - cs);
   const int rep = p.Hv / p.Hqk, hq = h / rep;
   const size_t qk_tok = static_cast<size_t>(p.Hqk) * DK, v_tok = static_cast<size_t>(p.Hv) * DV;
-  const T* vg = static_cast<const T*>(p.v);
   const float s = p.scale;
   const size_t ck = (static_cast<size_t>(sq.cbase + c) * p.Hv + h) * DK * DV;
   const size_t qo = static_cast<size_t>(cs) * qk_tok + static_cast<size_t>(hq) * DK;
@@ -498,6 +498,10 @@ __global__ __launch_bounds__(512) void dlocal_kernel(BwdParams p) {
     sdG[tid] = 0.f;
     sdB[tid] = 0.f;
   }
+  // every global operand is requested here, so the workgroup waits for memory once;
+  // v and dM' stay in registers until they are used
+  RowsInFlight<T, DV, NT> rv;
+  RowsInFlight<T, DV, NT, DK> rdm;
   {
     RowsInFlight<T, DK, NT> rq, rk;
     RowsInFlight<T, DV, NT> rdo, ru, rdz;
@@ -508,6 +512,8 @@ __global__ __launch_bounds__(512) void dlocal_kernel(BwdParams p) {
     ru.load(static_cast<const T*>(p.ck_u) + vo, v_tok, Lc, tid);
     rdz.load(static_cast<const T*>(p.dz) + vo, v_tok, Lc, tid);
     rm.load(static_cast<const T*>(p.ck_state) + ck, DV, DK, tid);
+    rv.load(static_cast<const T*>(p.v) + vo, v_tok, Lc, tid);
+    rdm.load(static_cast<const T*>(p.dm) + ck, DV, DK, tid);
     if (wave == 0) {
       const size_t gi = static_cast<size_t>(cs) * p.Hv + h;
       gate_vectors(vec, p.g + gi, p.beta + gi, p.Hv, Lc, lane);
@@ -520,21 +526,15 @@ __global__ __launch_bounds__(512) void dlocal_kernel(BwdParams p) {
     rm.store(sM, LDV, tid);
   }
   lds_barrier();
-  {  // the dZ . v part of dbeta (dZ from LDS, v from memory)
+  {  // the dZ . v part of dbeta
     constexpr int PR = DV / 4, IT = C * PR / NT;
-    static_assert(C * PR % NT == 0 && NT % PR == 0, "whole rows per pass");
-    floatx4 vv[IT];
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const int i = tid + it * NT, t = i / PR, e = (i - t * PR) * 4;
-      vv[it] = t < Lc ? load4(vg + vo + static_cast<size_t>(t) * v_tok + e) : zero4();
-    }
+    static_assert(C * PR % NT == 0 && NT % PR == 0 && IT == decltype(rv)::IT, "whole rows per pass");
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int i = tid + it * NT, t = i / PR, e = (i - t * PR) * 4;
       float part = 0.f;
 #pragma unroll
-      for (int x = 0; x < 4; ++x) part += to_float(sdZ[t * LDV + e + x]) * vv[it][x];
+      for (int x = 0; x < 4; ++x) part += to_float(sdZ[t * LDV + e + x]) * to_float(rv.v[it][x]);
       if (t < Lc) atomicAdd(&sdB[t], part);
     }
   }
@@ -630,31 +630,20 @@ __global__ __launch_bounds__(512) void dlocal_kernel(BwdParams p) {
   // -- dM' replaces M in LDS; gam_C <dM', M> enters dG at the chunk's end
   {
     constexpr int PR = DV / 4, IT = DK * PR / NT;
-    static_assert(DK * PR % NT == 0, "whole passes");
-    const T* dmp = static_cast<const T*>(p.dm) + ck;
-    floatx4 dmv[IT];
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const int i = tid + it * NT, r = i / PR, e = (i - r * PR) * 4;
-      dmv[it] = load4(dmp + static_cast<size_t>(r) * DV + e);
-    }
+    static_assert(DK * PR % NT == 0 && IT == decltype(rdm)::IT, "whole passes");
     float part = 0.f;
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int i = tid + it * NT, r = i / PR, e = (i - r * PR) * 4;
 #pragma unroll
-      for (int x = 0; x < 4; ++x) part += dmv[it][x] * to_float(sM[r * LDV + e + x]);
+      for (int x = 0; x < 4; ++x) part += to_float(rdm.v[it][x]) * to_float(sM[r * LDV + e + x]);
     }
     part = sum16(part);
     part += __shfl_xor(part, 16);
     part += __shfl_xor(part, 32);
     if (lane == 0) atomicAdd(&sdG[C - 1], vec[V_N * C] * part);
     lds_barrier();  // every M value is read before dM' replaces it
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const int i = tid + it * NT, r = i / PR, e = (i - r * PR) * 4;
-      store4<T>(sM + r * LDV + e, dmv[it]);
-    }
+    rdm.store(sM, LDV, tid);
   }
   lds_barrier();
   // -- dk += diag(kf) U dM'^T, with its dG terms
