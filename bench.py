@@ -15,9 +15,9 @@ The same JSON line also carries
                 kind of live state: algorithmic GB/s against 8 TB/s;
   epilogue      gdn_output_norm_gate over the prefill output: GB/s against 8 TB/s;
   short_conv    gdn_short_conv with L2 norm over the prefill's q: GB/s against 8 TB/s;
-  bwd           gdn_bwd_chunked (all gradients) over the prefill's inputs: the
-                recurrence's algorithmic fp32 TFLOP/s against the 157.3 TFLOP/s
-                fp32 vector peak;
+  bwd           gdn_bwd_chunked (all gradients) over the prefill's inputs:
+                algorithmic GB/s against 8 TB/s (its 197 flops per algorithmic
+                byte sit below the chip's ridge), and its dense-tile TFLOP/s;
   cpu_baseline  the fp64 oracle on the host cores over the same workload.
 Inputs are seeded synthetic tensors (linear_attention_token_chunked_amd.inputs).
 Every timed loop starts after W untimed steps and at least --warm-seconds of
@@ -45,6 +45,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "prefill": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "prefill.hip"),
     "decode": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "decode.hip"),
+    "prefill_save": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "prefill.hip"),
+    "bwd_dstate": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "bwd.hip"),
+    "bwd_dlocal": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "bwd.hip"),
 }
 
 
@@ -72,11 +75,20 @@ def verify_bytes(N, Tv, Hqk, Hv, dk, dv, s_in):
     return N * Hv * dk * dv * 4 * 2 + Tv * (N * (2 * Hqk * dk + 2 * Hv * dv) * s_in + N * Hv * 8)
 
 
-def bwd_flops_per_token_head(dk, dv):
-    """fp32 flops of one token's recompute (Mt = a M, r = Mt^T k, M' = Mt + k u^T, o = M'^T q: 7 per
-    state element) and adjoint (dM += q do^T, dq, du, dk's two products, dMt, dg: 2 each; dM = a dMt: 1;
-    15 per element) for one value head."""
-    return 22 * dk * dv
+def bwd_flops_per_token(Hqk, Hv, dk, dv, C):
+    """Dense-tile flops per token of the chunked backward, each product counted once: the forward
+    recompute (prefill_flops_per_token), Q K^T and K K^T per query/key head, and per value head
+    P^T dO, dO U^T, dZ U^T (2 C^2 dv each), (I + A)^-T dU (C^2 dv), K dM', Q^T dO, K^T dZ, dO M^T,
+    dZ M^T, U dM'^T (2 C dk dv each), (dP)K, (dP)^T Q, (D + D^T) K (2 C^2 dk each)."""
+    return (prefill_flops_per_token(Hqk, Hv, dk, dv, C) + Hqk * (4 * C * dk)
+            + Hv * (7 * C * dv + 6 * C * dk + 12 * dk * dv))
+
+
+def bwd_bytes(tokens, N, Hqk, Hv, dk, dv, s_in):
+    """q, k, v, dO, g, beta read; dq, dk, dv (fp32), dg, dbeta written; the initial state and the final
+    state's gradient read and the initial state's gradient written (fp32)."""
+    per_tok = 2 * Hqk * dk * s_in + 2 * Hv * dv * s_in + 8 * Hv + 2 * Hqk * dk * 4 + Hv * dv * 4 + 8 * Hv
+    return tokens * per_tok + 3 * N * Hv * dk * dv * 4
 
 
 def source_hash(path):
@@ -331,13 +343,20 @@ def bench_bwd(gdn, torch, steps=10):
 
     wall, mean_ms, per = time_launches(step, steps, 2, torch)
     tokens = w.B * w.T
-    flops = bwd_flops_per_token_head(w.dk, w.dv) * tokens * w.Hv
+    flops = bwd_flops_per_token(w.Hqk, w.Hv, w.dk, w.dv, w.chunk) * tokens
+    nbytes = bwd_bytes(tokens, w.B, w.Hqk, w.Hv, w.dk, w.dv, dev["q"].element_size())
     tflops = flops / (mean_ms * 1e-3) / 1e12
+    gbps = nbytes / (mean_ms * 1e-3) / 1e9
+    parts = [measured_traffic(k, w.name) for k in ("prefill_save", "bwd_dstate", "bwd_dlocal")]
+    # 198 flops per algorithmic byte, below the chip's 312 (2.5 PFLOP/s over 8 TB/s): the HBM roof is the lower one
     return {
         "workload": w.name, "tokens": tokens, "ms_per_call_mean": mean_ms, "ms_per_call_median": per[len(per) // 2],
         "Mtok_s": tokens / (mean_ms * 1e-3) / 1e6, "flops_per_call": flops, "tflops": tflops,
-        "roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_FP32_TFLOPS, 4), "traffic": None},
+        "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4), "bytes_per_call": nbytes,
+        "kernels": "saving prefill, state-gradient scan, local gradients (one call = all three)",
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": sum(parts) if all(x is not None for x in parts) else None},
     }
 
 

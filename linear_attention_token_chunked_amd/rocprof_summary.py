@@ -26,6 +26,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SOURCES = {
     "prefill": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "prefill.hip"),
     "decode": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "decode.hip"),
+    "prefill_save": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "prefill.hip"),
+    "bwd_dstate": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "bwd.hip"),
+    "bwd_dlocal": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "bwd.hip"),
 }
 
 
@@ -37,8 +40,12 @@ def _find(d, suffix):
 
 
 def _kind(name):
-    if "prefill_kernel" in name:
-        return "prefill"
+    if "prefill_kernel" in name:  # the last template flag marks the saving variant a backward pass runs
+        return "prefill" if name.endswith("Lb0EEEvNS0_6ParamsE") else "prefill_save"
+    if "dstate_kernel" in name:
+        return "bwd_dstate"
+    if "dlocal_kernel" in name:
+        return "bwd_dlocal"
     if "decode_kernel" in name:
         return "decode"
     if "verify_kernel" in name:
@@ -86,7 +93,7 @@ def traffic(fetch_dir, write_dir, calib_mib, out_json, out_txt, cmd, workloads):
     lines = ["# HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB), scaled by the",
              f"# factor that makes a plain {calib_mib} MiB device copy read and write {calib_mib} MiB.",
              f"# command: {cmd}", f"# fetch factor {f_fetch:.4f}, write factor {f_write:.4f}", ""]
-    for k in ("prefill", "decode"):
+    for k in ("prefill", "decode", "prefill_save", "bwd_dstate", "bwd_dlocal"):
         if k not in fetch or k not in write:
             continue
         fr = sum(v for _, _, v in fetch[k]) / len(fetch[k]) * 1024 * f_fetch
@@ -94,7 +101,7 @@ def traffic(fetch_dir, write_dir, calib_mib, out_json, out_txt, cmd, workloads):
         res[k] = {"workload": workloads[k], "source_sha256_16": hashlib.sha256(open(SOURCES[k], "rb").read())
                   .hexdigest()[:16], "read_bytes_per_launch": fr, "write_bytes_per_launch": wr,
                   "bytes_per_launch": fr + wr, "dispatches": len(fetch[k])}
-        lines.append(f"{k:8s} {workloads[k]:20s} read {fr / 1e6:10.2f} MB  write {wr / 1e6:10.2f} MB  "
+        lines.append(f"{k:12s} {workloads[k]:20s} read {fr / 1e6:10.2f} MB  write {wr / 1e6:10.2f} MB  "
                      f"total {(fr + wr) / 1e6:10.2f} MB per launch  ({len(fetch[k])} dispatches)")
     json.dump(res, open(out_json, "w"), indent=1)
     open(out_txt, "w").write("\n".join(lines) + "\n")
@@ -122,7 +129,8 @@ def main():
         stats(a.trace_dir, a.out, a.cmd)
     else:
         traffic(a.fetch_dir, a.write_dir, a.calib_mib, a.out_json, a.out_txt, a.cmd,
-                {"prefill": a.prefill_workload, "decode": a.decode_workload})
+                {"prefill": a.prefill_workload, "decode": a.decode_workload, "prefill_save": a.prefill_workload,
+                 "bwd_dstate": a.prefill_workload, "bwd_dlocal": a.prefill_workload})
 
 
 if __name__ == "__main__":
