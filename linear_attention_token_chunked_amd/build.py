@@ -23,7 +23,8 @@ LIB = os.path.join(PKG, "libgdn.so")
 SOURCES = ["gdn_api.cpp", "decode.hip", "verify.hip", "epilogue.hip", "conv.hip", "bwd.hip", "prefill.hip"]
 ARCH = "gfx950"
 
-# Packed fp32 VALU ops are switched off for every device compile.
+# Packed fp32 VALU ops are switched off for every device compile: the kernels rely on plain
+# per-lane fp32 arithmetic only.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC, "-Wall",
           "-Wno-unused-function"]

@@ -27,8 +27,8 @@ The second line is the transcript's order of operations (decay, read under the
 key, write the error); the first is the same map as a product of a transition
 matrix and an input term.
 
-Readings taken where the pages are silent (each listed again in the design doc)
----------------------------------------------------------------------------
+Readings taken where the pages are silent (the HIP path takes the same ones)
+----------------------------------------------------------------------------
 R1  States are stored as M = S^T with shape (dk, dv): M[i, j] = S[j, i].  The
     update in this layout is M <- alpha (I - beta k k^T) M + beta k v^T and the
     output is o = M^T q.  Initial and final states use the same layout.
