@@ -75,6 +75,40 @@ __device__ __forceinline__ void tile_mm_nn(floatx4& acc, const T* A, int lda, co
   for (int kg = 0; kg < K / Mma<T>::KG; ++kg) Mma<T>::mma(acc, lds_frag<T>(ar, kg, lane), lds_frag<T>(br, kg, lane));
 }
 
+// A B operand read once and used for several output tiles: the k-groups of
+// rows (lane & 15) of B (row reads), or the 16-wide k-steps of columns
+// (lane & 15) of B (column reads).
+template <class T, int K>
+struct RowFrags {
+  typename Mma<T>::frag f[K / Mma<T>::KG];
+  __device__ __forceinline__ RowFrags(const T* B, int ldb, int lane) {
+#pragma unroll
+    for (int kg = 0; kg < K / Mma<T>::KG; ++kg) f[kg] = lds_frag<T>(B + (lane & 15) * ldb, kg, lane);
+  }
+};
+template <class T, int K>
+struct ColFrags {
+  typename Vec4<T>::type f[K / 16];
+  __device__ __forceinline__ ColFrags(const T* B, int ldb, int lane) {
+#pragma unroll
+    for (int k = 0; k < K / 16; ++k) f[k] = lds_col4<T>(B + 16 * k * ldb, ldb, 0, 0, lane);
+  }
+};
+template <class T, int K>
+__device__ __forceinline__ void tile_mm_nn(floatx4& acc, const T* A, int lda, const RowFrags<T, K>& b, int lane) {
+  const T* ar = A + (lane & 15) * lda;
+#pragma unroll
+  for (int kg = 0; kg < K / Mma<T>::KG; ++kg) Mma<T>::mma(acc, lds_frag<T>(ar, kg, lane), b.f[kg]);
+}
+template <class T, bool TA, int K>
+__device__ __forceinline__ void tile_mm(floatx4& acc, const T* A, int lda, const ColFrags<T, K>& b, int lane) {
+#pragma unroll
+  for (int k = 0; k < K / 16; ++k) {
+    const auto fa = TA ? lds_col4<T>(A + 16 * k * lda, lda, 0, 0, lane) : row4<T>(A + 16 * k, lda, lane);
+    Mma16<T>::mma(acc, fa, b.f[k]);
+  }
+}
+
 __device__ __forceinline__ float sum16(float x) {
 #define GDN_ROR_ADD(n) \
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + (n), 0xf, 0xf, false))
@@ -396,13 +430,16 @@ __global__ __launch_bounds__(512) void dstate_kernel(BwdParams p) {
     // -- dM = gam_C dM' + s Q^T diag(gam) dO - K^T diag(beta gam) dZ, then its operand copy
     {
       const float gC = vec[V_N * C];
+      static_assert(NW % NJ == 0, "a wavefront's tiles share one column block");
+      const int jc = wave % NJ;
+      const ColFrags<T, C> og(sdOg + 16 * jc, LDB, lane), zb(sdZb + 16 * jc, LDB, lane);
 #pragma unroll
       for (int i = 0; i < NMT; ++i) {
-        const int t = wave + NW * i, a = t / NJ, jc = t % NJ;
+        const int t = wave + NW * i, a = t / NJ;
         if (t >= NTL) break;
         dM[i] *= gC;
-        tile_mm<T, true, true, C>(dM[i], sQ + 16 * a, LDK, sdOg + 16 * jc, LDB, lane);
-        tile_mm<T, true, true, C>(dM[i], sK + 16 * a, LDK, sdZb + 16 * jc, LDB, lane);
+        tile_mm<T, true, C>(dM[i], sQ + 16 * a, LDK, og, lane);
+        tile_mm<T, true, C>(dM[i], sK + 16 * a, LDK, zb, lane);
       }
       dm_to_lds();  // (dU, the only reader, is done: the barrier above)
     }
@@ -529,13 +566,16 @@ __global__ __launch_bounds__(512) void dlocal_kernel(BwdParams p) {
   {  // the dZ . v part of dbeta
     constexpr int PR = DV / 4, IT = C * PR / NT;
     static_assert(C * PR % NT == 0 && NT % PR == 0 && IT == decltype(rv)::IT, "whole rows per pass");
+    static_assert(PR == 16 || PR == 32, "a row is one or two 16-lane groups");
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int i = tid + it * NT, t = i / PR, e = (i - t * PR) * 4;
       float part = 0.f;
 #pragma unroll
       for (int x = 0; x < 4; ++x) part += to_float(sdZ[t * LDV + e + x]) * to_float(rv.v[it][x]);
-      if (t < Lc) atomicAdd(&sdB[t], part);
+      part = sum16(part);  // the row's lanes first, then one atomic per row
+      if constexpr (PR == 32) part += __shfl_xor(part, 16);
+      if ((lane & (PR - 1)) == 0 && t < Lc) atomicAdd(&sdB[t], part);
     }
   }
   // -- C x C tiles: dP (masked, times s exp(G_i - G_j)) and D + D^T, with their dG and dbeta terms
@@ -590,13 +630,20 @@ __global__ __launch_bounds__(512) void dlocal_kernel(BwdParams p) {
   lds_barrier();
   // -- dq = s diag(gam) dO M^T + (dP s dec) K  (written out);
   //    dk = -diag(beta gam) dZ M^T + (dP s dec)^T Q + (D + D^T) K  (kept; the dM' term follows)
+  // A wavefront's tiles share one 16-column block kt of dq and dk (tile t = wave + 8i, kt = t % KTL),
+  // so the B operands are read once for all of them.
+  static_assert(8 % KTL == 0 || KTL % 8 == 0, "one key block per wavefront");
+  const int kt = wave % KTL;
   floatx4 dka[NOT];
+  {
+    const RowFrags<T, DV> mf(sM + 16 * kt * LDV, LDV, lane);  // M rows of the block
+    const ColFrags<T, C> kcol(sK + 16 * kt, LDK, lane), qcol(sQ + 16 * kt, LDK, lane);
 #pragma unroll
   for (int i = 0; i < NOT; ++i) {
-    const int t = wave + 8 * i, it = t / KTL, kt = t % KTL;
+    const int t = wave + 8 * i, it = t / KTL;
     floatx4 a = zero4(), b = zero4();
-    tile_mm_nn<T, DV>(a, sdO + 16 * it * LDV, LDV, sM + 16 * kt * LDV, LDV, lane);  // dO M^T
-    tile_mm_nn<T, DV>(b, sdZ + 16 * it * LDV, LDV, sM + 16 * kt * LDV, LDV, lane);  // dZ M^T
+    tile_mm_nn<T, DV>(a, sdO + 16 * it * LDV, LDV, mf, lane);  // dO M^T
+    tile_mm_nn<T, DV>(b, sdZ + 16 * it * LDV, LDV, mf, lane);  // dZ M^T
     floatx4 dq = zero4();
     dka[i] = zero4();
     {
@@ -618,14 +665,15 @@ __global__ __launch_bounds__(512) void dlocal_kernel(BwdParams p) {
         }
       }
     }
-    tile_mm<T, false, true, C>(dq, sdP + 16 * it * LDC, LDC, sK + 16 * kt, LDK, lane);
-    tile_mm<T, true, true, C>(dka[i], sdP + 16 * it, LDC, sQ + 16 * kt, LDK, lane);
-    tile_mm<T, false, true, C>(dka[i], sS + 16 * it * LDC, LDC, sK + 16 * kt, LDK, lane);
+    tile_mm<T, false, C>(dq, sdP + 16 * it * LDC, LDC, kcol, lane);
+    tile_mm<T, true, C>(dka[i], sdP + 16 * it, LDC, qcol, lane);
+    tile_mm<T, false, C>(dka[i], sS + 16 * it * LDC, LDC, kcol, lane);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * it + 4 * lg + r;
       if (row < Lc) put(p.dq, qo + static_cast<size_t>(row) * qk_tok + 16 * kt + lr, dq[r]);
     }
+  }
   }
   // -- dM' replaces M in LDS; gam_C <dM', M> enters dG at the chunk's end
   {
@@ -647,11 +695,12 @@ __global__ __launch_bounds__(512) void dlocal_kernel(BwdParams p) {
   }
   lds_barrier();
   // -- dk += diag(kf) U dM'^T, with its dG terms
+  const RowFrags<T, DV> dmf(sM + 16 * kt * LDV, LDV, lane);  // dM' rows of the block
 #pragma unroll
   for (int i = 0; i < NOT; ++i) {
-    const int t = wave + 8 * i, it = t / KTL, kt = t % KTL;
+    const int t = wave + 8 * i, it = t / KTL;
     floatx4 a = zero4();
-    tile_mm_nn<T, DV>(a, sU + 16 * it * LDV, LDV, sM + 16 * kt * LDV, LDV, lane);  // U dM'^T
+    tile_mm_nn<T, DV>(a, sU + 16 * it * LDV, LDV, dmf, lane);  // U dM'^T
     const int r0 = 16 * it + 4 * lg, key = 16 * kt + lr;
     const floatx4 kf = vec4_at(vec + V_KF * C + r0);
     floatx4 sj;
