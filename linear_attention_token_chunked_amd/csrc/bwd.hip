@@ -140,11 +140,16 @@ template <class T, int W, int NT, int R = C>
 struct RowsInFlight {
   static constexpr int PR = W / 4, N = R * PR, IT = (N + NT - 1) / NT;
   typename Vec4<T>::type v[IT];
+  // src is the same for every lane; the per-lane part is a 32-bit byte offset
+  // (at most 64 rows of at most 1 MB)
   __device__ __forceinline__ void load(const T* src, size_t ss, int L, int tid) {
+    const char* base = reinterpret_cast<const char*>(src);
+    const unsigned stride = static_cast<unsigned>(ss * sizeof(T));
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int i = tid + it * NT, t = i / PR, e = (i - t * PR) * 4;
-      if (i < N && t < L) v[it] = *reinterpret_cast<const typename Vec4<T>::type*>(src + t * ss + e);
+      const unsigned off = static_cast<unsigned>(t) * stride + static_cast<unsigned>(e * sizeof(T));
+      if (i < N && t < L) v[it] = *reinterpret_cast<const typename Vec4<T>::type*>(base + off);
       else v[it] = typename Vec4<T>::type{};
     }
   }
