@@ -61,8 +61,6 @@ __device__ __forceinline__ void tile_mm(floatx4& acc, const T* A, int lda, const
   }
 }
 
-// Sum over the 16 lanes of a row group, in every lane of it (DPP row rotations:
-// no LDS round trips).
 // The same product when both operands are read along their rows (no
 // transposes): whole k-groups of the wide matrix-core instruction
 // (bf16: 16x16x32, 16-byte row reads), K a multiple of Mma<T>::KG.
@@ -109,6 +107,8 @@ __device__ __forceinline__ void tile_mm(floatx4& acc, const T* A, int lda, const
   }
 }
 
+// Sum over the 16 lanes of a row group, in every lane of it (DPP row rotations:
+// no LDS round trips).
 __device__ __forceinline__ float sum16(float x) {
 #define GDN_ROR_ADD(n) \
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + (n), 0xf, 0xf, false))
@@ -122,16 +122,6 @@ __device__ __forceinline__ float sum16(float x) {
 __device__ __forceinline__ floatx4 vec4_at(const float* v) { return *reinterpret_cast<const floatx4*>(v); }
 __device__ __forceinline__ float rdlane(float x, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
-}
-
-__device__ __forceinline__ floatx4 load4(const float* p) { return *reinterpret_cast<const floatx4*>(p); }
-__device__ __forceinline__ floatx4 load4(const bf16* p) {
-  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
-  return floatx4{to_float(v[0]), to_float(v[1]), to_float(v[2]), to_float(v[3])};
-}
-template <class D>
-__device__ __forceinline__ void store4(D* p, const floatx4& v) {
-  *reinterpret_cast<typename Vec4<D>::type*>(p) = pack4<D>(v[0], v[1], v[2], v[3]);
 }
 
 // Rows of a row-major tile held in registers on their way to LDS, as raw
@@ -161,25 +151,6 @@ struct RowsInFlight {
     }
   }
 };
-
-// R rows of W columns from a row-major source (row stride ss elements) into an
-// LDS tile (row stride ld); rows >= L are zero.  Every load is issued before
-// the first store, so the workgroup waits for memory once.
-template <class S, class D, int W, int NT, int R = C>
-__device__ __forceinline__ void stage_rows(D* dst, int ld, const S* src, size_t ss, int L, int tid) {
-  constexpr int PR = W / 4, N = R * PR, IT = (N + NT - 1) / NT;
-  floatx4 v[IT];
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int i = tid + it * NT, t = i / PR, e = (i - t * PR) * 4;
-    v[it] = (i < N && t < L) ? load4(src + t * ss + e) : zero4();
-  }
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int i = tid + it * NT, t = i / PR, e = (i - t * PR) * 4;
-    if (i < N) store4<D>(dst + t * ld + e, v[it]);
-  }
-}
 
 // Per-chunk gate vectors, formed by one wavefront (lane = token): log2-scaled
 // inclusive cumsum Gl, exp(G), exp(G_C - G), beta (tokens >= L act as g = 0,
