@@ -70,6 +70,17 @@ typedef struct {
 /*
  * Bytes of device workspace gdn_fwd_chunked needs for these dims (0 when none).
  * Returns 0 as well for dims that gdn_fwd_chunked would reject.
+ *
+ * Only a row that is long for its number of heads needs one: bf16, dk = dv =
+ * 128, no cu_seqlens, B * Hv <= 51 and T >= 3072.  Such a row is cut into S
+ * segments run side by side, which relies on the recurrence being affine in the
+ * state: the state leaving a segment is Phi M + F, where M is the state
+ * entering it, F the state the segment leaves when started from zero and Phi
+ * the product of its tokens' transitions exp(g_t) (I - beta_t k_t k_t^T), and
+ * each output is its zero-start value plus (scale Phi_t^T q_t)^T M, Phi_t the
+ * product up to token t.  The workspace holds scale Phi_t^T q_t per token and
+ * value head in bf16 (B * T * Hv * dk * 2 bytes) plus a few fp32 states per
+ * segment and value head: 562 MB at B = 1, T = 65536, Hv = 32.
  */
 size_t gdn_fwd_chunked_workspace_size(const gdn_dims_t* d);
 

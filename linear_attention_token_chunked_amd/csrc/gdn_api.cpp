@@ -33,8 +33,13 @@ gdn_status_t from_hip(hipError_t e) { return e == hipSuccess ? GDN_STATUS_SUCCES
 extern "C" {
 
 size_t gdn_fwd_chunked_workspace_size(const gdn_dims_t* d) {
-  (void)d;
-  return 0;  // the fused prefill keeps every intermediate in LDS and registers
+  // The fused prefill keeps every intermediate in LDS and registers; only a few
+  // long bf16 rows (dk = dv = 128, no cu_seqlens) run as segments side by side,
+  // with a workspace for the segments' transitions and corrections.
+  if (!d || d->batch < 1 || d->seqlen < 1 || d->num_v_heads < 1 || d->num_seqs != d->batch) return 0;
+  if (d->dtype != GDN_DTYPE_BFLOAT16 || d->head_dim_k != 128 || d->head_dim_v != 128 || d->chunk_size != 64)
+    return 0;
+  return gdn::seg_workspace_bytes(d->batch, d->seqlen, d->num_v_heads);
 }
 
 gdn_status_t gdn_fwd_chunked(const gdn_dims_t* d, const void* q, const void* k, const void* v, const float* g,
@@ -82,6 +87,8 @@ gdn_status_t gdn_fwd_chunked(const gdn_dims_t* d, const void* q, const void* k, 
   a.chunk = d->chunk_size;
   a.scale = d->scale;
   a.bf16 = d->dtype == GDN_DTYPE_BFLOAT16;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
   return from_hip(gdn::launch_prefill(a, stream));
 }
 

@@ -35,7 +35,27 @@ struct PrefillArgs {
   void* save_state = nullptr;
   void* save_u = nullptr;
   const int32_t* chunk_base = nullptr;  // [N + 1] with cu_seqlens, else null (n * ceil(T / C))
+  // Caller's workspace (segmented prefill of long rows; see seg_plan).
+  void* workspace = nullptr;
+  size_t workspace_bytes = 0;
 };
+
+// Segmented prefill of a few long batch rows (bf16, dk = dv = 128, no cu_seqlens):
+// every row is cut into nseg segments of seg_len tokens that run side by side.
+struct SegPlan {
+  int nseg = 0, seg_len = 0;
+  void* qt = nullptr;       // [B, T, Hv, dk] bf16: the transition runs' outputs
+  float* fin = nullptr;     // [nseg][B][Hv][dk][dv] fp32: end states from the zero state (segment 0: the row's)
+  float* phi = nullptr;     // [nseg][B][Hv][dk][dk] fp32: transitions of the segments
+  void* mstart = nullptr;   // [nseg][B][Hv][dv][dk] bf16: start states of the segments, transposed
+  float* mbuf = nullptr;    // two [B][Hv][dk][dv] fp32 buffers for the scan
+  size_t mbuf_stride = 0;   // floats between them
+};
+// Whether (and how) rows of T tokens are segmented for batch * Hv units.
+bool seg_plan(int batch, int T, int Hv, SegPlan* sp);
+size_t seg_workspace_bytes(int batch, int T, int Hv);  // 0 when not segmented
+void seg_carve(void* ws, int batch, int T, int Hv, SegPlan* sp);
+hipError_t launch_seg_finish(const PrefillArgs& a, const SegPlan& sp, hipStream_t stream);
 
 // Multi-token verify: Tv (<= kMaxVerifyTokens) consecutive steps per sequence.
 constexpr int kMaxVerifyTokens = 8;

@@ -228,6 +228,11 @@ struct Params {
   float* hT;
   void *save_state, *save_u;  // element type T
   const int32_t* chunk_base;
+  // SEG: segments of seg_len tokens (see seg.hip); qt receives the transition
+  // runs' outputs, seg_fin / seg_phi their end states [nseg][batch][Hv][DK][DV]
+  void* qt;
+  float *seg_fin, *seg_phi;
+  int seg_len, nseg, batch;
   int T, Hqk, Hv, nunits, nslices;
   float scale;
 };
@@ -265,7 +270,8 @@ struct ChunkRegs {
   // is at most 4096 heads x 128 x 4 bytes, checked on the host), so the
   // loads take a uniform 64-bit base plus one 24-bit multiply per row.
   __device__ __forceinline__ void load(const T* kb, const T* qb, const T* vb, uint32_t qk_row, uint32_t v_row,
-                                       const float* gb, const float* bb, uint32_t g_row, int Lc, int tid) {
+                                       const float* gb, const float* bb, uint32_t g_row, int Lc, int tid,
+                                       bool vzero = false) {
     const char* kc = reinterpret_cast<const char*>(kb);
     const char* qc = reinterpret_cast<const char*>(qb);
     const char* vc = reinterpret_cast<const char*>(vb);
@@ -275,10 +281,15 @@ struct ChunkRegs {
       k[it] = *reinterpret_cast<const frag*>(kc + off);
       q[it] = *reinterpret_cast<const frag*>(qc + off);
     }
+    if (vzero) {  // (a workgroup-uniform branch)
 #pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      const int t = min(tid + it * PTHREADS, C * VPR - 1);
-      v[it] = *reinterpret_cast<const frag*>(vc + __umul24(min(t / VPR, Lc - 1), v_row) + (t % VPR) * 16);
+      for (int it = 0; it < VIT; ++it) v[it] = frag{};
+    } else {
+#pragma unroll
+      for (int it = 0; it < VIT; ++it) {
+        const int t = min(tid + it * PTHREADS, C * VPR - 1);
+        v[it] = *reinterpret_cast<const frag*>(vc + __umul24(min(t / VPR, Lc - 1), v_row) + (t % VPR) * 16);
+      }
     }
     const int gl = tid - (PTHREADS - 64);  // the last producer wave owns the gates, one token per lane
     if (gl >= 0) {
@@ -337,8 +348,9 @@ template <> struct OutPTiles<1> { static constexpr int n = 4, ti[4] = {2, 2, 3, 
 
 // SAVE: the variant a backward pass runs first; it keeps each chunk's starting
 // state and U (as T, the precision of the products' operands) and writes no
-// output.
-template <class T, int DK, int DV, int BV, int NSTAGE, int NCW, bool OUTW, bool SAVE>
+// output.  SEG: the segmented variant (seg.hip): the units are virtual
+// sequences, a segment of a batch row each.
+template <class T, int DK, int DV, int BV, int NSTAGE, int NCW, bool OUTW, bool SAVE, bool SEG>
 __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kernel(Params p) {
   using L = Layout<T, DK, BV, NSTAGE, NCW, OUTW>;
   using MM = Mma<T>;
@@ -372,7 +384,21 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
   const int h = unit - n * p.Hv;
   const int hq = h / (p.Hv / p.Hqk);
   int bos, eos;
-  if (p.cu) {
+  int b = n, seg = 0;  // SEG: the batch row and segment of virtual sequence n
+  bool phi = false;    // SEG: a transition run (v = 0 from the identity state)
+  if constexpr (SEG) {
+    // virtual sequences: every row's first segment, then per row and later
+    // segment a run from the zero state and a transition run
+    if (n >= p.batch) {
+      const int idx = n - p.batch, per = 2 * (p.nseg - 1);
+      b = idx / per;
+      const int r = idx - b * per;
+      seg = 1 + (r >> 1);
+      phi = (r & 1) != 0;
+    }
+    bos = b * p.T + seg * p.seg_len;
+    eos = min(b * p.T + p.T, bos + p.seg_len);
+  } else if (p.cu) {
     bos = p.cu[n];
     eos = p.cu[n + 1];
   } else {
@@ -387,7 +413,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
   const T* qg = static_cast<const T*>(p.q);
   const T* kgp = static_cast<const T*>(p.k);
   const T* vg = static_cast<const T*>(p.v);
-  T* og = static_cast<T*>(p.o);
+  T* og = static_cast<T*>(SEG && phi ? p.qt : p.o);
   const size_t qk_tok = static_cast<size_t>(p.Hqk) * DK;
   const size_t v_tok = static_cast<size_t>(p.Hv) * DV;
 
@@ -402,7 +428,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
     const size_t tg = static_cast<size_t>(cs) * p.Hv + h;
     pre.load(kgp + tq, qg + tq, vg + tv, static_cast<uint32_t>(qk_tok * sizeof(T)),
              static_cast<uint32_t>(v_tok * sizeof(T)), p.g + tg, p.beta + tg, static_cast<uint32_t>(p.Hv * 4),
-             min(C, eos - cs), tid);
+             min(C, eos - cs), tid, SEG && phi);
   };
 
   // Stage the chunk's K, Q, V and gates; issue the next chunk's loads.  (The
@@ -552,13 +578,26 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
   const size_t sbase = static_cast<size_t>(unit) * DK * DV;
   const int slane = MM::state_row(0, lg, 0) * DV + wcol + lr;
   if (consumer) {
-    const float* h0 = p.h0 + sbase;
+    if constexpr (SEG) {  // the row's initial state, the zero state, or (transition runs) the identity
+      const float* h0 = seg == 0 && p.h0 ? p.h0 + (static_cast<size_t>(b) * p.Hv + h) * DK * DV : nullptr;
 #pragma unroll
-    for (int a = 0; a < KT; ++a)
+      for (int a = 0; a < KT; ++a)
 #pragma unroll
-      for (int j = 0; j < NTW; ++j)
+        for (int j = 0; j < NTW; ++j)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) Ms[a][j][s] = p.h0 ? h0[slane + MM::state_row(a, 0, s) * DV + 16 * j] : 0.f;
+          for (int s = 0; s < 4; ++s) {
+            const int row = MM::state_row(a, lg, s), col = wcol + 16 * j + lr;
+            Ms[a][j][s] = h0 ? h0[row * DV + col] : (phi && row == col ? 1.f : 0.f);
+          }
+    } else {
+      const float* h0 = p.h0 + sbase;
+#pragma unroll
+      for (int a = 0; a < KT; ++a)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) Ms[a][j][s] = p.h0 ? h0[slane + MM::state_row(a, 0, s) * DV + 16 * j] : 0.f;
+    }
   }
 
   // The state at the start of chunk c (SAVE).
@@ -975,7 +1014,17 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
     }
   }
 
-  if (consumer && p.hT) {
+  if constexpr (SEG) {  // every run's end state, for the scan over segments
+    if (consumer) {
+      float* e = (phi ? p.seg_phi : p.seg_fin) + ((static_cast<size_t>(seg) * p.batch + b) * p.Hv + h) * DK * DV;
+#pragma unroll
+      for (int a = 0; a < KT; ++a)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) e[slane + MM::state_row(a, 0, s) * DV + 16 * j] = Ms[a][j][s];
+    }
+  } else if (consumer && p.hT) {
     float* hT = p.hT + sbase;
 #pragma unroll
     for (int a = 0; a < KT; ++a)
@@ -986,8 +1035,8 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
   }
 }
 
-template <class T, int DK, int DV, int BV, int NSTAGE, int NCW, bool OUTW, bool SAVE>
-hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
+template <class T, int DK, int DV, int BV, int NSTAGE, int NCW, bool OUTW, bool SAVE, bool SEG = false>
+hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream, const SegPlan* sp = nullptr) {
   using L = Layout<T, DK, BV, NSTAGE, NCW, OUTW>;
   static_assert(L::bytes <= 160 * 1024, "LDS budget of one gfx950 compute unit");
   Params p;
@@ -1009,14 +1058,26 @@ hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
   p.nunits = a.num_seqs * a.Hv;
   p.nslices = DV / BV;
   p.scale = a.scale;
+  p.qt = nullptr;
+  p.seg_fin = p.seg_phi = nullptr;
+  p.seg_len = p.nseg = 0;
+  p.batch = a.batch;
+  if constexpr (SEG) {  // virtual sequences: every row's segments, later ones twice
+    p.qt = sp->qt;
+    p.seg_fin = sp->fin;
+    p.seg_phi = sp->phi;
+    p.seg_len = sp->seg_len;
+    p.nseg = sp->nseg;
+    p.nunits = a.batch * (2 * sp->nseg - 1) * a.Hv;
+  }
   if (p.nunits == 0) return hipSuccess;
   const int units_pad = (p.nunits + 7) / 8 * 8;
   const dim3 grid(units_pad * p.nslices);
   hipError_t e = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&prefill_kernel<T, DK, DV, BV, NSTAGE, NCW, OUTW, SAVE>),
+      reinterpret_cast<const void*>(&prefill_kernel<T, DK, DV, BV, NSTAGE, NCW, OUTW, SAVE, SEG>),
       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(L::bytes));
   if (e != hipSuccess) return e;
-  prefill_kernel<T, DK, DV, BV, NSTAGE, NCW, OUTW, SAVE>
+  prefill_kernel<T, DK, DV, BV, NSTAGE, NCW, OUTW, SAVE, SEG>
       <<<grid, dim3(64 * (NP + NCW * (OUTW ? 2 : 1))), L::bytes, stream>>>(p);
   return hipGetLastError();
 }
@@ -1046,6 +1107,17 @@ int slice_config(int units, int dv) {
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (a.chunk != C) return hipErrorInvalidValue;
   const int units = a.num_seqs * a.Hv;
+  // A few long rows: segments side by side, finished by a scan and a correction.
+  if (a.bf16 && a.dk == 128 && a.dv == 128 && !a.cu_seqlens && !a.save_state && a.workspace) {
+    SegPlan sp;
+    if (seg_plan(a.batch, a.seqlen, a.Hv, &sp) &&
+        a.workspace_bytes >= seg_workspace_bytes(a.batch, a.seqlen, a.Hv)) {
+      seg_carve(a.workspace, a.batch, a.seqlen, a.Hv, &sp);
+      const hipError_t e = launch_cfg<bf16, 128, 128, 128, 2, 4, false, false, true>(a, stream, &sp);
+      if (e != hipSuccess) return e;
+      return launch_seg_finish(a, sp, stream);
+    }
+  }
   if (a.bf16) {
     if (a.dk == 128 && a.dv == 128) {
       switch (slice_config(units, 128)) {

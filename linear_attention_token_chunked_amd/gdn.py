@@ -115,12 +115,14 @@ def fwd_chunked_workspace_size(dims: Dims) -> int:
 
 
 def fwd_chunked(q, k, v, g, beta, *, initial_state=None, cu_seqlens=None, chunk_size=64, scale=1.0,
-                output_final_state=True, out=None, final_state=None):
+                output_final_state=True, out=None, final_state=None, workspace=None):
     """Chunked prefill: (o, final_state) for q, k [B, T, Hqk, dk], v [B, T, Hv, dv], g, beta [B, T, Hv].
 
     initial_state / final_state are fp32 [N, Hv, dk, dv]; cu_seqlens is int32 [N + 1] on the device
     (then B must be 1).  ``out`` and ``final_state`` may be given to reuse buffers; final_state may be
-    the initial_state tensor itself for an in-place update.
+    the initial_state tensor itself for an in-place update.  ``workspace`` may be a uint8 device tensor
+    of at least ``fwd_chunked_workspace_size`` bytes to reuse (long rows with few heads need one);
+    otherwise one is allocated when needed.
     """
     dev = q.device
     if dev.type != "cuda":
@@ -161,7 +163,12 @@ def fwd_chunked(q, k, v, g, beta, *, initial_state=None, cu_seqlens=None, chunk_
             raise ValueError("final_state must be [N, Hv, dk, dv]")
     dims = make_dims(B, T, N, Hqk, Hv, dk, dv, chunk_size, scale, q.dtype)
     ws_bytes = fwd_chunked_workspace_size(dims)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    ws = workspace
+    if ws is None:
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    else:
+        _need(ws, "workspace", torch.uint8, dev, 1)
+        ws_bytes = ws.numel()
     with torch.cuda.device(dev):
         code = lib.gdn_fwd_chunked(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                    _ptr(initial_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state), _ptr(ws),

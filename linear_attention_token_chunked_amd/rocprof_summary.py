@@ -40,8 +40,14 @@ def _find(d, suffix):
 
 
 def _kind(name):
-    if "prefill_kernel" in name:  # the last template flag marks the saving variant a backward pass runs
-        return "prefill" if name.endswith("Lb0EEEvNS0_6ParamsE") else "prefill_save"
+    if "prefill_kernel" in name:  # the last two template flags: the saving variant a backward pass
+        if name.endswith("Lb1ELb0EEEvNS0_6ParamsE"):  # runs, and the segmented variant of long rows
+            return "prefill_save"
+        return "prefill_seg" if name.endswith("Lb0ELb1EEEvNS0_6ParamsE") else "prefill"
+    if "seg_correct_kernel" in name:
+        return "seg_correct"
+    if "seg_scan_step_kernel" in name:
+        return "seg_scan"
     if "dstate_kernel" in name:
         return "bwd_dstate"
     if "dlocal_kernel" in name:

@@ -155,6 +155,35 @@ def test_decode_invalid(gdn):
 
 def test_workspace_size_is_zero_for_the_fused_prefill(gdn):
     assert gdn.fwd_chunked_workspace_size(dims(gdn)) == 0
+    # rows that fill the chip with their own units, short rows, fp32 and d = 64 run fused
+    assert gdn.fwd_chunked_workspace_size(dims(gdn, B=4, T=4096, N=4, Hqk=16, Hv=16)) == 0
+    assert gdn.fwd_chunked_workspace_size(dims(gdn, B=1, T=65536, N=1, Hqk=16, Hv=52)) == 0
+    assert gdn.fwd_chunked_workspace_size(dims(gdn, T=3071, Hv=1, Hqk=1)) == 0
+    assert gdn.fwd_chunked_workspace_size(dims(gdn, T=8192, dk=64, dv=64, dtype=0)) == 0
+    assert gdn.fwd_chunked_workspace_size(dims(gdn, T=8192, dk=64, dv=64)) == 0
+
+
+def seg_ws_bytes(B, T, Hv, nseg):
+    """Segmented prefill workspace: per-token bf16 vectors scale Phi_t^T q_t, then per segment and
+    value head the zero-start end state and the transition (fp32), the start state (bf16, for the
+    correction), and two fp32 states for the scan; each part padded to 256 bytes."""
+    al = lambda x: (x + 255) // 256 * 256
+    mat = 128 * 128
+    return (al(B * T * Hv * 128 * 2) + 2 * al(nseg * B * Hv * mat * 4) + al(nseg * B * Hv * mat * 2)
+            + 2 * al(B * Hv * mat * 4))
+
+
+def test_segmented_prefill_workspace(gdn):
+    # B = 1, T = 65536, 32 value heads: four segments (7 runs per head fill 224 of 256 compute units)
+    d = dims(gdn, B=1, T=65536, N=1, Hqk=16, Hv=32)
+    assert gdn.fwd_chunked_workspace_size(d) == seg_ws_bytes(1, 65536, 32, 4)
+    # one head: at most T / 1024 segments, and none of them empty
+    assert gdn.fwd_chunked_workspace_size(dims(gdn, T=3072, Hv=1, Hqk=1)) == seg_ws_bytes(1, 3072, 1, 3)
+    assert gdn.fwd_chunked_workspace_size(dims(gdn, T=5000, Hv=1, Hqk=1)) == seg_ws_bytes(1, 5000, 1, 4)
+    assert gdn.fwd_chunked_workspace_size(dims(gdn, B=1, T=65536, N=1, Hqk=1, Hv=51)) == seg_ws_bytes(1, 65536, 51, 3)
+    need = gdn.fwd_chunked_workspace_size(d)
+    assert call_fwd(gdn, d, ws_bytes=need - 1) == WORKSPACE_TOO_SMALL
+    assert call_fwd(gdn, d, ws=FAKE + 128, ws_bytes=need) == MISALIGNED
 
 
 def test_verify_invalid(gdn):
