@@ -200,10 +200,12 @@ def bench_prefill(name, gdn, torch, steps, warmup):
     N = B if dev["cu_seqlens"] is None else dev["cu_seqlens"].shape[0] - 1
     out = torch.empty((B, T, Hv, dv), dtype=dev["q"].dtype, device="cuda")
     fin = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device="cuda")
+    ws_bytes = gdn.fwd_chunked_workspace_size(gdn.make_dims(B, T, N, Hqk, Hv, dk, dv, w.chunk, 1.0, dev["q"].dtype))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes else None
 
     def step():
         gdn.fwd_chunked(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], initial_state=dev["initial_state"],
-                        cu_seqlens=dev["cu_seqlens"], chunk_size=w.chunk, out=out, final_state=fin)
+                        cu_seqlens=dev["cu_seqlens"], chunk_size=w.chunk, out=out, final_state=fin, workspace=ws)
 
     torch.cuda.synchronize()
     c0 = time.perf_counter()
