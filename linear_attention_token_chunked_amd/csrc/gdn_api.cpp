@@ -33,10 +33,14 @@ gdn_status_t from_hip(hipError_t e) { return e == hipSuccess ? GDN_STATUS_SUCCES
 extern "C" {
 
 size_t gdn_fwd_chunked_workspace_size(const gdn_dims_t* d) {
-  // The fused prefill keeps every intermediate in LDS and registers; only a few
-  // long bf16 rows (dk = dv = 128, no cu_seqlens) run as segments side by side,
-  // with a workspace for the segments' transitions and corrections.
-  if (!d || d->batch < 1 || d->seqlen < 1 || d->num_v_heads < 1 || d->num_seqs != d->batch) return 0;
+  // The fused prefill keeps every intermediate in LDS and registers.  Packed
+  // sequences (cu_seqlens, so batch 1 and num_seqs > 1) take a few bytes for
+  // their longest-first order; a few long bf16 rows (dk = dv = 128, no
+  // cu_seqlens) run as segments side by side, with a workspace for the
+  // segments' transitions and corrections.
+  if (!d || d->batch < 1 || d->seqlen < 0 || d->num_v_heads < 1 || d->chunk_size != 64) return 0;
+  if (d->num_seqs != d->batch) return d->batch == 1 ? gdn::order_workspace_bytes(d->num_seqs) : 0;
+  if (d->seqlen < 1) return 0;
   if (d->dtype != GDN_DTYPE_BFLOAT16 || d->head_dim_k != 128 || d->head_dim_v != 128 || d->chunk_size != 64)
     return 0;
   return gdn::seg_workspace_bytes(d->batch, d->seqlen, d->num_v_heads);

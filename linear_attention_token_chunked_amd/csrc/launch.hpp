@@ -35,10 +35,18 @@ struct PrefillArgs {
   void* save_state = nullptr;
   void* save_u = nullptr;
   const int32_t* chunk_base = nullptr;  // [N + 1] with cu_seqlens, else null (n * ceil(T / C))
-  // Caller's workspace (segmented prefill of long rows; see seg_plan).
+  // Caller's workspace (segmented prefill of long rows, see seg_plan; the
+  // longest-first order of packed sequences, see order_workspace_bytes).
   void* workspace = nullptr;
   size_t workspace_bytes = 0;
+  // Set by launch_prefill: the sequences in the order their workgroups are
+  // numbered ([N] int32 on the device), or null for the natural order.
+  const int32_t* order = nullptr;
 };
+
+// Workspace bytes for the longest-first order of num_seqs packed sequences
+// (0 where the natural order is kept).
+size_t order_workspace_bytes(int num_seqs);
 
 // Segmented prefill of a few long batch rows (bf16, dk = dv = 128, no cu_seqlens):
 // every row is cut into nseg segments of seg_len tokens that run side by side.

@@ -228,6 +228,7 @@ struct Params {
   float* hT;
   void *save_state, *save_u;  // element type T
   const int32_t* chunk_base;
+  const int32_t* order;  // packed sequences, longest first (null: natural order)
   // SEG: segments of seg_len tokens (see seg.hip); qt receives the transition
   // runs' outputs, seg_fin / seg_phi their end states [nseg][batch][Hv][DK][DV]
   void* qt;
@@ -380,8 +381,8 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
   const int slice = rest % p.nslices;
   const int unit = xcd + 8 * (rest / p.nslices);
   if (unit >= p.nunits) return;
-  const int n = unit / p.Hv;
-  const int h = unit - n * p.Hv;
+  const int h = unit % p.Hv;
+  const int n = !SEG && p.order ? p.order[unit / p.Hv] : unit / p.Hv;
   const int hq = h / (p.Hv / p.Hqk);
   int bos, eos;
   int b = n, seg = 0;  // SEG: the batch row and segment of virtual sequence n
@@ -575,7 +576,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
   frag mfr[KGK][NTW];  // the state as matrix-core operands (bf16-rounded for bf16 inputs), per chunk
   // the unit's state: uniform base, small per-lane offsets (keeps 64-bit
   // per-element addresses out of the registers)
-  const size_t sbase = static_cast<size_t>(unit) * DK * DV;
+  const size_t sbase = (static_cast<size_t>(n) * p.Hv + h) * DK * DV;
   const int slane = MM::state_row(0, lg, 0) * DV + wcol + lr;
   if (consumer) {
     if constexpr (SEG) {  // the row's initial state, the zero state, or (transition runs) the identity
@@ -1052,6 +1053,7 @@ hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream, const SegPlan* s
   p.save_state = a.save_state;
   p.save_u = a.save_u;
   p.chunk_base = a.chunk_base;
+  p.order = a.order;
   p.T = a.seqlen;
   p.Hqk = a.Hqk;
   p.Hv = a.Hv;
@@ -1102,11 +1104,52 @@ int slice_config(int units, int dv) {
   if (units >= 256) return 128;
   return units >= 128 ? 64 : 32;
 }
+
+// Longest-first order of packed sequences.  Each sequence's workgroups are
+// numbered by its place in this order, so the dispatcher starts the longest
+// sequences first and the short ones fill in at the end, instead of a long
+// sequence that happens to come late setting the end of the launch (with
+// lengths as uneven as a lognormal mix, that tail was a quarter of the time).
+// Rank of sequence i = the number of sequences longer than it, or as long and
+// before it: one thread per sequence, all lengths staged through LDS in turn.
+constexpr int kMaxOrdered = 4096;  // beyond this many sequences the natural order is kept
+
+__global__ __launch_bounds__(256) void order_kernel(const int32_t* cu, int N, int32_t* order) {
+  __shared__ int len[256];
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int li = i < N ? cu[i + 1] - cu[i] : 0;
+  int rank = 0;
+  for (int j0 = 0; j0 < N; j0 += 256) {
+    const int j = j0 + threadIdx.x;
+    __syncthreads();
+    len[threadIdx.x] = j < N ? cu[j + 1] - cu[j] : 0;
+    __syncthreads();
+    const int m = min(256, N - j0);
+    for (int u = 0; u < m; ++u) {
+      const int lj = len[u];
+      rank += (lj > li) | ((lj == li) & (j0 + u < i));
+    }
+  }
+  if (i < N) order[rank] = i;
+}
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
-  if (a.chunk != C) return hipErrorInvalidValue;
+size_t order_workspace_bytes(int num_seqs) {
+  return num_seqs >= 2 && num_seqs <= kMaxOrdered ? (static_cast<size_t>(num_seqs) * 4 + 255) / 256 * 256 : 0;
+}
+
+hipError_t launch_prefill(const PrefillArgs& args, hipStream_t stream) {
+  if (args.chunk != C) return hipErrorInvalidValue;
+  PrefillArgs a = args;
   const int units = a.num_seqs * a.Hv;
+  if (a.cu_seqlens && !a.save_state && a.workspace && order_workspace_bytes(a.num_seqs) &&
+      a.workspace_bytes >= order_workspace_bytes(a.num_seqs)) {
+    int32_t* order = static_cast<int32_t*>(a.workspace);
+    order_kernel<<<dim3((a.num_seqs + 255) / 256), dim3(256), 0, stream>>>(a.cu_seqlens, a.num_seqs, order);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.order = order;
+  }
   // A few long rows: segments side by side, finished by a scan and a correction.
   if (a.bf16 && a.dk == 128 && a.dv == 128 && !a.cu_seqlens && !a.save_state && a.workspace) {
     SegPlan sp;

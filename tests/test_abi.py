@@ -163,6 +163,18 @@ def test_workspace_size_is_zero_for_the_fused_prefill(gdn):
     assert gdn.fwd_chunked_workspace_size(dims(gdn, T=8192, dk=64, dv=64)) == 0
 
 
+def test_packed_sequences_workspace(gdn):
+    # packed sequences (batch 1, N > 1): N int32 for their longest-first order, up to 4096 sequences
+    assert gdn.fwd_chunked_workspace_size(dims(gdn, B=1, T=1000, N=2)) == 256
+    assert gdn.fwd_chunked_workspace_size(dims(gdn, B=1, T=1000, N=64)) == 256
+    assert gdn.fwd_chunked_workspace_size(dims(gdn, B=1, T=1000, N=65)) == 512
+    assert gdn.fwd_chunked_workspace_size(dims(gdn, B=1, T=0, N=4096)) == 16384
+    assert gdn.fwd_chunked_workspace_size(dims(gdn, B=1, T=1000, N=4097)) == 0
+    assert gdn.fwd_chunked_workspace_size(dims(gdn, B=1, T=1000, N=64, dk=64, dv=64, dtype=0)) == 256
+    d = dims(gdn, B=1, T=1000, N=64)
+    assert call_fwd(gdn, d, cu=FAKE, ws_bytes=255) == WORKSPACE_TOO_SMALL
+
+
 def seg_ws_bytes(B, T, Hv, nseg):
     """Segmented prefill workspace: per-token bf16 vectors scale Phi_t^T q_t, then per segment and
     value head the zero-start end state and the transition (fp32), the start state (bf16, for the

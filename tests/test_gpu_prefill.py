@@ -104,6 +104,17 @@ def test_packed_ragged_lengths(gdn, dtype, d):
     np.testing.assert_array_equal(gf[8], s0[8])
 
 
+def test_many_packed_sequences_longest_first(gdn):
+    """300 packed sequences of random lengths with many ties: their workgroups run longest first
+    (an order formed on the device over more than one block of sequences); results are per sequence."""
+    rng = np.random.default_rng(11)
+    lens = [int(x) for x in rng.integers(0, 131, size=300)]
+    lens[7] = 700  # one long sequence among short ones
+    flush(f"prefill packed N={len(lens)} tokens={sum(lens)}")
+    inp = make_prefill(1, 0, 1, 2, 64, 64, "bf16", init_state=True, lengths=lens, seed=12)
+    check_against_oracle(gdn, inp, "bf16")
+
+
 def test_slow_decay_long_carry(gdn):
     """log(alpha) scaled by 0.001: the state carries across all chunks and the initial state stays visible."""
     flush("prefill slow decay")
