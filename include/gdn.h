@@ -71,8 +71,13 @@ typedef struct {
  * Bytes of device workspace gdn_fwd_chunked needs for these dims (0 when none).
  * Returns 0 as well for dims that gdn_fwd_chunked would reject.
  *
- * Only a row that is long for its number of heads needs one: bf16, dk = dv =
- * 128, no cu_seqlens, B * Hv <= 51 and T >= 3072.  Such a row is cut into S
+ * Packed sequences (batch 1, 2 <= num_seqs <= 4096) need 4 * num_seqs bytes
+ * (rounded up to 256): the sequences are ranked by length on the device and
+ * their workgroups numbered longest first, which shortens the launch's tail
+ * when lengths are uneven.  The order changes no arithmetic.
+ *
+ * Otherwise only a row that is long for its number of heads needs one: bf16,
+ * dk = dv = 128, no cu_seqlens, B * Hv <= 51 and T >= 3072.  Such a row is cut into S
  * segments run side by side, which relies on the recurrence being affine in the
  * state: the state leaving a segment is Phi M + F, where M is the state
  * entering it, F the state the segment leaves when started from zero and Phi
