@@ -48,7 +48,12 @@ KERNEL_SOURCES = {
     "prefill_save": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "prefill.hip"),
     "bwd_dstate": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "bwd.hip"),
     "bwd_dlocal": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "bwd.hip"),
+    "verify": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "verify.hip"),
+    "epilogue": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "epilogue.hip"),
+    "short_conv": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "conv.hip"),
 }
+EPILOGUE_WORKLOAD = "epilogue_b4_t4096"
+SHORT_CONV_WORKLOAD = "short_conv_q_b4_t4096"
 
 
 # ------------------------------------------------------------------ algorithmic work
@@ -277,7 +282,7 @@ def bench_verify(gdn, torch, steps=20):
         "us_per_call_mean": us, "us_per_call_median": per[len(per) // 2] * 1e3,
         "Mtok_s": w.N * w.steps / (us * 1e-6) / 1e6, "bytes_per_call": nbytes, "GBps": gbps,
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": measured_traffic("verify", w.name)},
     }
 
 
@@ -297,10 +302,11 @@ def bench_epilogue(gdn, torch, steps=50):
     nbytes = 3 * rows * dv * dev["o"].element_size() + dv * 4
     gbps = nbytes / (us * 1e-6) / 1e9
     return {
-        "workload": "prefill_b4_t4096 output (262144 rows x 128, bf16)", "rows": rows, "dv": dv,
-        "us_per_call_mean": us, "bytes_per_call": nbytes, "GBps": gbps,
+        "workload": EPILOGUE_WORKLOAD, "what": "prefill_b4_t4096 output (262144 rows x 128, bf16)", "rows": rows,
+        "dv": dv, "us_per_call_mean": us, "bytes_per_call": nbytes, "GBps": gbps,
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": measured_traffic("epilogue", EPILOGUE_WORKLOAD)},
     }
 
 
@@ -321,10 +327,12 @@ def bench_short_conv(gdn, torch, steps=50):
     nbytes = 2 * x.numel() * x.element_size() + w.numel() * 4
     gbps = nbytes / (us * 1e-6) / 1e9
     return {
-        "workload": "q of prefill_b4_t4096 (4 x 4096 tokens x 16 heads x 128, bf16), width 4, L2 norm",
+        "workload": SHORT_CONV_WORKLOAD,
+        "what": "q of prefill_b4_t4096 (4 x 4096 tokens x 16 heads x 128, bf16), width 4, L2 norm",
         "us_per_call_mean": us, "bytes_per_call": nbytes, "GBps": gbps,
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": measured_traffic("short_conv", SHORT_CONV_WORKLOAD)},
     }
 
 

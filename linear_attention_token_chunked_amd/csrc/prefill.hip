@@ -234,7 +234,8 @@ struct Params {
   void* qt;
   float *seg_fin, *seg_phi;
   int seg_len, nseg, batch;
-  int T, Hqk, Hv, nunits, nslices;
+  int T, Hqk, Hv, nslices;
+  int grp, ngroups;  // units per group sharing keys and queries, number of groups
   float scale;
 };
 
@@ -374,38 +375,44 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
   const int lg = lane >> 4;
   const int lr = lane & 15;
 
-  // Workgroup -> (unit, dv-slice); the slices of one unit get ids 8 apart and
-  // so run on the same XCD and share its L2.
+  // Workgroup -> (unit, dv-slice).  Units that read the same keys and queries
+  // (the value heads of one q/k head; in the segmented variant also the
+  // zero-state and transition runs of one segment) form a group of p.grp, and
+  // the members of a group and their slices get ids 8 apart, so they run on
+  // one XCD and share its L2.
   const int xcd = blockIdx.x & 7;
   const int rest = blockIdx.x >> 3;
   const int slice = rest % p.nslices;
-  const int unit = xcd + 8 * (rest / p.nslices);
-  if (unit >= p.nunits) return;
-  const int h = unit % p.Hv;
-  const int n = !SEG && p.order ? p.order[unit / p.Hv] : unit / p.Hv;
-  const int hq = h / (p.Hv / p.Hqk);
+  const int member = (rest / p.nslices) % p.grp;
+  const int grp = (rest / p.nslices / p.grp) * 8 + xcd;
+  if (grp >= p.ngroups) return;
+  const int hg = p.Hv / p.Hqk;  // value heads per q/k head
+  int n, h;
+  int b, seg = 0;    // SEG: the batch row and segment of the run
+  bool phi = false;  // SEG: a transition run (v = 0 from the identity state)
   int bos, eos;
-  int b = n, seg = 0;  // SEG: the batch row and segment of virtual sequence n
-  bool phi = false;    // SEG: a transition run (v = 0 from the identity state)
   if constexpr (SEG) {
-    // virtual sequences: every row's first segment, then per row and later
-    // segment a run from the zero state and a transition run
-    if (n >= p.batch) {
-      const int idx = n - p.batch, per = 2 * (p.nseg - 1);
-      b = idx / per;
-      const int r = idx - b * per;
-      seg = 1 + (r >> 1);
-      phi = (r & 1) != 0;
-    }
+    // group (row, segment, q/k head); member (run, value head): segment 0 has
+    // one run from the row's initial state, every later segment a run from the
+    // zero state and a transition run
+    const int bs = grp / p.Hqk, run = member / hg;
+    seg = bs % p.nseg;
+    b = bs / p.nseg;
+    if (seg == 0 && run > 0) return;
+    h = (grp % p.Hqk) * hg + member % hg;
+    phi = run == 1;
+    n = seg == 0 ? b : p.batch + b * 2 * (p.nseg - 1) + 2 * (seg - 1) + run;  // (virtual sequence)
     bos = b * p.T + seg * p.seg_len;
     eos = min(b * p.T + p.T, bos + p.seg_len);
-  } else if (p.cu) {
-    bos = p.cu[n];
-    eos = p.cu[n + 1];
   } else {
-    bos = n * p.T;
-    eos = bos + p.T;
+    const int unit = grp * p.grp + member;  // = sequence * Hv + h
+    h = unit % p.Hv;
+    n = p.order ? p.order[unit / p.Hv] : unit / p.Hv;
+    b = n;
+    bos = p.cu ? p.cu[n] : n * p.T;
+    eos = p.cu ? p.cu[n + 1] : bos + p.T;
   }
+  const int hq = h / hg;
   const int nch = (eos - bos + C - 1) / C;
   const int col0 = slice * BV;
   const int cw = producer ? 0 : (wave - NP) % NCW;  // consumer index (an output wave: its consumer's)
@@ -1057,8 +1064,9 @@ hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream, const SegPlan* s
   p.T = a.seqlen;
   p.Hqk = a.Hqk;
   p.Hv = a.Hv;
-  p.nunits = a.num_seqs * a.Hv;
   p.nslices = DV / BV;
+  p.grp = a.Hv / a.Hqk;
+  p.ngroups = a.num_seqs * a.Hqk;
   p.scale = a.scale;
   p.qt = nullptr;
   p.seg_fin = p.seg_phi = nullptr;
@@ -1070,11 +1078,12 @@ hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream, const SegPlan* s
     p.seg_phi = sp->phi;
     p.seg_len = sp->seg_len;
     p.nseg = sp->nseg;
-    p.nunits = a.batch * (2 * sp->nseg - 1) * a.Hv;
+    p.grp = 2 * (a.Hv / a.Hqk);  // (segment 0 uses half of its group)
+    p.ngroups = a.batch * sp->nseg * a.Hqk;
   }
-  if (p.nunits == 0) return hipSuccess;
-  const int units_pad = (p.nunits + 7) / 8 * 8;
-  const dim3 grid(units_pad * p.nslices);
+  if (p.ngroups == 0) return hipSuccess;
+  const int groups_pad = (p.ngroups + 7) / 8 * 8;
+  const dim3 grid(groups_pad * p.grp * p.nslices);
   hipError_t e = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&prefill_kernel<T, DK, DV, BV, NSTAGE, NCW, OUTW, SAVE, SEG>),
       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(L::bytes));

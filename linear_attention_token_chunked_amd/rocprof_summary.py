@@ -29,6 +29,9 @@ SOURCES = {
     "prefill_save": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "prefill.hip"),
     "bwd_dstate": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "bwd.hip"),
     "bwd_dlocal": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "bwd.hip"),
+    "verify": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "verify.hip"),
+    "epilogue": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "epilogue.hip"),
+    "short_conv": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "conv.hip"),
 }
 
 
@@ -56,6 +59,10 @@ def _kind(name):
         return "decode"
     if "verify_kernel" in name:
         return "verify"
+    if "norm_gate_kernel" in name:
+        return "epilogue"
+    if "conv_kernel" in name:
+        return "short_conv"
     if "copyBuffer" in name or "copy" in name.lower():
         return "copy"
     return None
@@ -99,7 +106,7 @@ def traffic(fetch_dir, write_dir, calib_mib, out_json, out_txt, cmd, workloads):
     lines = ["# HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB), scaled by the",
              f"# factor that makes a plain {calib_mib} MiB device copy read and write {calib_mib} MiB.",
              f"# command: {cmd}", f"# fetch factor {f_fetch:.4f}, write factor {f_write:.4f}", ""]
-    for k in ("prefill", "decode", "prefill_save", "bwd_dstate", "bwd_dlocal"):
+    for k in ("prefill", "decode", "prefill_save", "bwd_dstate", "bwd_dlocal", "verify", "epilogue", "short_conv"):
         if k not in fetch or k not in write:
             continue
         fr = sum(v for _, _, v in fetch[k]) / len(fetch[k]) * 1024 * f_fetch
@@ -107,7 +114,7 @@ def traffic(fetch_dir, write_dir, calib_mib, out_json, out_txt, cmd, workloads):
         res[k] = {"workload": workloads[k], "source_sha256_16": hashlib.sha256(open(SOURCES[k], "rb").read())
                   .hexdigest()[:16], "read_bytes_per_launch": fr, "write_bytes_per_launch": wr,
                   "bytes_per_launch": fr + wr, "dispatches": len(fetch[k])}
-        lines.append(f"{k:12s} {workloads[k]:20s} read {fr / 1e6:10.2f} MB  write {wr / 1e6:10.2f} MB  "
+        lines.append(f"{k:12s} {workloads[k]:22s} read {fr / 1e6:10.2f} MB  write {wr / 1e6:10.2f} MB  "
                      f"total {(fr + wr) / 1e6:10.2f} MB per launch  ({len(fetch[k])} dispatches)")
     json.dump(res, open(out_json, "w"), indent=1)
     open(out_txt, "w").write("\n".join(lines) + "\n")
@@ -130,13 +137,18 @@ def main():
     t.add_argument("--cmd", default="")
     t.add_argument("--prefill-workload", default="prefill_b4_t4096")
     t.add_argument("--decode-workload", default="decode_n256")
+    t.add_argument("--verify-workload", default="verify_n256_t4")
+    t.add_argument("--epilogue-workload", default="epilogue_b4_t4096")
+    t.add_argument("--short-conv-workload", default="short_conv_q_b4_t4096")
     a = ap.parse_args()
     if a.what == "stats":
         stats(a.trace_dir, a.out, a.cmd)
     else:
         traffic(a.fetch_dir, a.write_dir, a.calib_mib, a.out_json, a.out_txt, a.cmd,
                 {"prefill": a.prefill_workload, "decode": a.decode_workload, "prefill_save": a.prefill_workload,
-                 "bwd_dstate": a.prefill_workload, "bwd_dlocal": a.prefill_workload})
+                 "bwd_dstate": a.prefill_workload, "bwd_dlocal": a.prefill_workload,
+                 "verify": a.verify_workload, "epilogue": a.epilogue_workload,
+                 "short_conv": a.short_conv_workload})
 
 
 if __name__ == "__main__":
