@@ -4,7 +4,7 @@
       per-kernel call count and average / min / max duration from --kernel-trace output
   python -m linear_attention_token_chunked_amd.rocprof_summary traffic <fetch_dir> <write_dir> <calib_mib> \
         <out.json> <out.txt> --cmd "<command>"
-      HBM bytes per launch of the prefill and decode kernels from a FETCH_SIZE run and a
+      HBM bytes per launch of the measured kernels from a FETCH_SIZE run and a
       WRITE_SIZE run.  Each counter is scaled by the factor that makes it read the known
       size of a plain device copy in the same run (calib_mib MiB read and written once).
 
