@@ -115,6 +115,18 @@ def test_many_packed_sequences_longest_first(gdn):
     check_against_oracle(gdn, inp, "bf16")
 
 
+def test_packed_beyond_ordering_limit(gdn):
+    """More than 4096 packed sequences keep their natural order (no ordering workspace): still per sequence."""
+    rng = np.random.default_rng(13)
+    lens = [int(x) for x in rng.integers(0, 9, size=4200)]
+    lens[100] = 300
+    flush(f"prefill packed N={len(lens)} tokens={sum(lens)} (natural order)")
+    inp = make_prefill(1, 0, 1, 1, 64, 64, "bf16", init_state=True, lengths=lens, seed=14)
+    dims = gdn.make_dims(1, sum(lens), len(lens), 1, 1, 64, 64, 64, 1.0, torch.bfloat16)
+    assert gdn.fwd_chunked_workspace_size(dims) == 0
+    check_against_oracle(gdn, inp, "bf16")
+
+
 def test_slow_decay_long_carry(gdn):
     """log(alpha) scaled by 0.001: the state carries across all chunks and the initial state stays visible."""
     flush("prefill slow decay")

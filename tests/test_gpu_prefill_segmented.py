@@ -80,3 +80,22 @@ def test_segmented_equals_unsegmented_path(gdn):
     torch.cuda.synchronize()
     assert not segmented(gdn, 64, 4096, 2)
     assert rel_l2(f64(o1), f64(o2[:1])) <= 2e-2 and rel_l2(f64(f1), f64(f2[:1])) <= 2e-2
+
+
+def test_segmented_in_place_state_and_no_final_state(gdn):
+    """The final state may overwrite the initial state (the scan writes it after every run has read it), and
+    without a final state only the outputs are formed; both match the separate-buffer call bit for bit."""
+    flush("segmented in place / no final state")
+    inp = make_prefill(1, 4096, 1, 2, 128, 128, "bf16", init_state=True, seed=21)
+    dev = to_dev(inp)
+    o1, f1 = gdn.fwd_chunked(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], initial_state=dev["initial_state"])
+    state = dev["initial_state"].clone()
+    o2, f2 = gdn.fwd_chunked(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], initial_state=state,
+                             final_state=state)
+    o3, f3 = gdn.fwd_chunked(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], initial_state=dev["initial_state"],
+                             output_final_state=False)
+    torch.cuda.synchronize()
+    assert f2 is state and f3 is None
+    assert torch.equal(o1, o2) and torch.equal(f1, state) and torch.equal(o1, o3)
+    ro, rf = recurrent(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], initial_state=inp["initial_state"])
+    assert_close("final_state", f64(state), rf, TOL[torch.bfloat16])
