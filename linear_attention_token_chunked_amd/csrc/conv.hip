@@ -32,24 +32,29 @@ __device__ __forceinline__ float row16_sum(float x) {
 
 // A 16-lane group walks a run of kRun consecutive tokens of one head: it
 // loads the head's taps once and slides a window of the last W token rows
-// through registers, so every row is loaded once.
+// through registers.  A wavefront's four groups take four consecutive heads of
+// one run, and the workgroup's four wavefronts take four consecutive runs of
+// the same heads: a wavefront hands the last W - 1 rows of its run to the next
+// one through LDS, so only the first run of a workgroup loads the rows before
+// it from memory again (3 of every 32 rows instead of 3 of every 8).
 constexpr int kRun = 8;
+constexpr int kWaves = kConvThreads / 64;
 
 template <class T, int HD, bool L2>
 __global__ __launch_bounds__(kConvThreads) void conv_kernel(const T* __restrict__ x, const float* __restrict__ w,
                                                             T* __restrict__ y, const int32_t* __restrict__ cu,
                                                             int num_seqs, int seqlen, int heads, int tokens,
-                                                            int runs, float eps) {
+                                                            int head_blocks, float eps) {
   constexpr int EPL = HD / 16;  // channels per lane
   constexpr int W = kConvWidth;
   static_assert(W == 4, "one 16-byte load of taps per channel");
   typedef T lane_vec __attribute__((ext_vector_type(EPL)));
-  const int lane16 = threadIdx.x & 15;
-  const int grp = blockIdx.x * (kConvThreads / 16) + (threadIdx.x >> 4);  // run * heads + head
-  if (grp >= runs * heads) return;  // whole 16-lane groups leave together
-  const int run = grp / heads;
-  const int h = grp - run * heads;
-  const int t0 = run * kRun;
+  __shared__ lane_vec handoff[kWaves][W - 1][64];  // a wavefront's last W - 1 rows, lane by lane
+  const int lane = threadIdx.x & 63, lane16 = lane & 15, wave = threadIdx.x >> 6;
+  const int hb = blockIdx.x % head_blocks;
+  const int h = hb * 4 + (lane >> 4);
+  const bool active = h < heads;  // (inactive groups still take part in the barrier)
+  const int t0 = (blockIdx.x / head_blocks) * (kWaves * kRun) + wave * kRun;
   // the sequence of the run's first token, and where the next one starts
   int start, next;
   if (cu) {
@@ -59,28 +64,46 @@ __global__ __launch_bounds__(kConvThreads) void conv_kernel(const T* __restrict_
       if (cu[mid] <= t0) lo = mid; else hi = mid;
     }
     start = cu[lo];
-    next = cu[lo + 1];  // > t0: lo is the last sequence starting at or before t0
+    next = cu[lo + 1];  // > t0 unless t0 is past the last token
   } else {
     start = t0 - t0 % seqlen;
     next = start + seqlen;
   }
-  const int c0 = h * HD + lane16 * EPL;  // first channel of this lane
+  const int c0 = (active ? h : 0) * HD + lane16 * EPL;  // first channel of this lane
   floatx4 taps[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) taps[e] = *reinterpret_cast<const floatx4*>(w + (c0 + e) * W);
-  const T* xl = x + static_cast<size_t>(h) * HD + lane16 * EPL;  // this lane's channels of token 0
-  T* yl = y + static_cast<size_t>(h) * HD + lane16 * EPL;
+  const T* xl = x + c0;  // this lane's channels of token 0
+  T* yl = y + c0;
   const size_t tstride = static_cast<size_t>(heads) * HD;
+  // the run's rows (past the last token, the last row again: never used)
+  lane_vec rows[kRun];
+#pragma unroll
+  for (int r = 0; r < kRun; ++r)
+    rows[r] = *reinterpret_cast<const lane_vec*>(xl + static_cast<size_t>(min(t0 + r, tokens - 1)) * tstride);
+  // rows t0 - 3 .. t0 - 1: from the wavefront before (LDS) or, for the first, from memory
+  lane_vec prev[W - 1];
+  if (wave == 0) {
+#pragma unroll
+    for (int i = 0; i < W - 1; ++i)
+      prev[i] = *reinterpret_cast<const lane_vec*>(xl + static_cast<size_t>(max(t0 - (W - 1) + i, 0)) * tstride);
+  }
+#pragma unroll
+  for (int i = 0; i < W - 1; ++i) handoff[wave][i][lane] = rows[kRun - (W - 1) + i];
+  __syncthreads();
+  if (wave > 0) {
+#pragma unroll
+    for (int i = 0; i < W - 1; ++i) prev[i] = handoff[wave - 1][i][lane];
+  }
+  if (!active || t0 >= tokens) return;
   // window of the W - 1 rows before the current token (zero before the sequence start)
   float win[W - 1][EPL];
 #pragma unroll
   for (int i = 0; i < W - 1; ++i) {
     const int u = t0 - (W - 1) + i;
     const bool live = u >= start && u >= 0;
-    lane_vec v = {};
-    if (live) v = *reinterpret_cast<const lane_vec*>(xl + static_cast<size_t>(u) * tstride);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) win[i][e] = live ? to_float(v[e]) : 0.f;
+    for (int e = 0; e < EPL; ++e) win[i][e] = live ? to_float(prev[i][e]) : 0.f;
   }
 #pragma unroll
   for (int r = 0; r < kRun; ++r) {
@@ -103,7 +126,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_kernel(const T* __restrict_
 #pragma unroll
         for (int e = 0; e < EPL; ++e) win[i][e] = 0.f;
     }
-    const lane_vec v = *reinterpret_cast<const lane_vec*>(xl + static_cast<size_t>(t) * tstride);
+    const lane_vec v = rows[r];
     float cur[EPL], acc[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
@@ -134,17 +157,17 @@ __global__ __launch_bounds__(kConvThreads) void conv_kernel(const T* __restrict_
 template <class T, int HD>
 hipError_t launch(const ConvArgs& a, hipStream_t stream) {
   if (a.tokens == 0) return hipSuccess;
-  const int runs = (a.tokens + kRun - 1) / kRun;
-  const int64_t groups = static_cast<int64_t>(runs) * a.heads;
-  const dim3 grid(static_cast<unsigned>((groups + kConvThreads / 16 - 1) / (kConvThreads / 16)));
+  const int head_blocks = (a.heads + 3) / 4;
+  const int64_t blocks = static_cast<int64_t>((a.tokens + kWaves * kRun - 1) / (kWaves * kRun)) * head_blocks;
+  const dim3 grid(static_cast<unsigned>(blocks));
   if (a.l2norm)
     conv_kernel<T, HD, true><<<grid, dim3(kConvThreads), 0, stream>>>(
         static_cast<const T*>(a.x), a.weight, static_cast<T*>(a.y), a.cu_seqlens, a.num_seqs, a.seqlen, a.heads,
-        a.tokens, runs, a.eps);
+        a.tokens, head_blocks, a.eps);
   else
     conv_kernel<T, HD, false><<<grid, dim3(kConvThreads), 0, stream>>>(
         static_cast<const T*>(a.x), a.weight, static_cast<T*>(a.y), a.cu_seqlens, a.num_seqs, a.seqlen, a.heads,
-        a.tokens, runs, a.eps);
+        a.tokens, head_blocks, a.eps);
   return hipGetLastError();
 }
 
