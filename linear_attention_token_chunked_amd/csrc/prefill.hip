@@ -473,6 +473,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
   // (fp32, for the inverses); -A below the diagonal and P stay in registers
   // until prod_finish.
   constexpr bool PROD_P = !(OUTW && NCW == 2);  // two output waves form most of P themselves
+  constexpr bool PMASK = !(OUTW && SAVE);         // a saving run with output waves forms no P (no O)
   floatx4 pkeep[3], akeep[3];
   auto gram = [&](auto wtag, int s) __attribute__((always_inline)) {
     using GT = GramTiles<decltype(wtag)::value>;
@@ -493,7 +494,8 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
 #pragma unroll
       for (int t = 0; t < GT::n; ++t) {
         rowk[kgi][GT::ti[t]] = lds_frag(sK + (16 * GT::ti[t] + lr) * LDK, kgi, lane);
-        if (PROD_P || (GT::pmask >> t & 1)) rowq[kgi][GT::ti[t]] = lds_frag(sQ + (16 * GT::ti[t] + lr) * LDK, kgi, lane);
+        if (PROD_P || (PMASK && (GT::pmask >> t & 1)))
+          rowq[kgi][GT::ti[t]] = lds_frag(sQ + (16 * GT::ti[t] + lr) * LDK, kgi, lane);
         rowk[kgi][GT::tj[t]] = lds_frag(sK + (16 * GT::tj[t] + lr) * LDK, kgi, lane);
       }
 #pragma unroll
@@ -501,7 +503,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
 #pragma unroll
       for (int t = 0; t < GT::n; ++t) {
         MM::mma(kk[t], rowk[kgi][GT::tj[t]], rowk[kgi][GT::ti[t]]);
-        if (PROD_P || (GT::pmask >> t & 1)) MM::mma(qk[t], rowk[kgi][GT::tj[t]], rowq[kgi][GT::ti[t]]);
+        if (PROD_P || (PMASK && (GT::pmask >> t & 1))) MM::mma(qk[t], rowk[kgi][GT::tj[t]], rowq[kgi][GT::ti[t]]);
       }
     // lane holds X[i = 16ti + lr][j = 16tj + 4lg + s] of both products
 #pragma unroll
@@ -516,7 +518,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
           const int j = 16 * GT::tj[t] + 4 * lg + s4;
           const float d = dd[s4];
           akeep[t][s4] = j < i ? bi * d * kk[t][s4] : 0.f;
-          if (PROD_P || (GT::pmask >> t & 1)) pkeep[t][s4] = d * qk[t][s4];
+          if (PROD_P || (PMASK && (GT::pmask >> t & 1))) pkeep[t][s4] = d * qk[t][s4];
         }
         if (GT::ti[t] == GT::tj[t]) {
 #pragma unroll
@@ -542,7 +544,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
     T* sAnf = reinterpret_cast<T*>(smem + L::oAnf);
 #pragma unroll
     for (int t = 0; t < GT::n; ++t) {
-      if (PROD_P || (GT::pmask >> t & 1))
+      if (PROD_P || (PMASK && (GT::pmask >> t & 1)))
         *reinterpret_cast<V4*>(sPf + L::pf(GT::ti[t], GT::tj[t], lane)) =
             pack4<T>(pkeep[t][0], pkeep[t][1], pkeep[t][2], pkeep[t][3]);
       if (GT::ti[t] != GT::tj[t])
@@ -639,6 +641,39 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
       for (int kgi = 0; kgi < KGK; ++kgi) sMx[kgi * 64 + lane] = mfr[kgi][0];
     }
   };
+  // SAVE with output waves: the same state, from the bf16 operand copy its
+  // consumer wave leaves in LDS (element e of k-group kg of lane group g is key
+  // 32 kg + 8 g + e of the lane's column), and U from its copy (element e of
+  // k-group kg is token 32 kg + 16 (e / 4) + 4 g + e % 4): the stores leave the
+  // consumers' chain.
+  auto save_state_from_operands = [&](int c) __attribute__((always_inline)) {
+    const int cb = p.chunk_base ? p.chunk_base[n] : n * ((p.T + C - 1) / C);
+    T* d = static_cast<T*>(p.save_state) + (static_cast<size_t>(cb + c) * p.Hv + h) * DK * DV + wcol + lr;
+    if constexpr (MM::TPG == 2) {  // (output waves run with bf16 only)
+#pragma unroll
+      for (int kgi = 0; kgi < KGK; ++kgi) {
+        const frag f = sMx[kgi * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d[(32 * kgi + 8 * lg + e) * DV] = f[e];
+      }
+    }
+  };
+  auto save_u_from_operands = [&](int c) __attribute__((always_inline)) {
+    const int cs = bos + c * C, Lc = min(C, eos - cs);
+    T* u = static_cast<T*>(p.save_u) + (static_cast<size_t>(cs) * p.Hv + h) * DV + wcol + lr;
+    if constexpr (MM::TPG == 2) {
+#pragma unroll
+      for (int kgi = 0; kgi < KGC; ++kgi) {
+        const frag f = sUx[kgi * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int t = 32 * kgi + 16 * (e >> 2) + 4 * lg + (e & 3);
+          if (t < Lc) u[static_cast<size_t>(t) * v_tok] = f[e];
+        }
+      }
+    }
+  };
+
   floatx4 Ot[4][NTW];  // O^T by 16-token tile: lane holds O[16ct + lr][wcol + 16j + 4lg + s]
   auto q_times_state = [&](const T* sQ, const float* vec) __attribute__((always_inline)) {
 #pragma unroll
@@ -806,7 +841,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
         Z[b][j] = u;  // Z_b is not needed any more
       }
     }
-    if constexpr (SAVE) {  // U rows of the chunk's tokens
+    if constexpr (SAVE && !OUTW) {  // U rows of the chunk's tokens (with output waves: theirs to store)
       const int cs = bos + c * C, Lc = min(C, eos - cs);
 #pragma unroll
       for (int b = 0; b < 4; ++b)
@@ -978,15 +1013,25 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
         lds_barrier();
       }
       for (int c = 0; c < nch; ++c) {
-        outw_qm(c & 1);
-        lds_barrier();
-        if constexpr (NCW == 2) {
-          if (wave == NP + NCW) outw_p(std::integral_constant<int, 0>(), c & 1);
-          else outw_p(std::integral_constant<int, 1>(), c & 1);
+        if constexpr (SAVE) {
+          // a saving run writes no O: the output waves store the chunk's
+          // starting state and U instead, from the consumers' operand copies
+          save_state_from_operands(c);
+          lds_barrier();
+          lds_barrier();
+          save_u_from_operands(c);
+          lds_barrier();
+        } else {
+          outw_qm(c & 1);
+          lds_barrier();
+          if constexpr (NCW == 2) {
+            if (wave == NP + NCW) outw_p(std::integral_constant<int, 0>(), c & 1);
+            else outw_p(std::integral_constant<int, 1>(), c & 1);
+          }
+          lds_barrier();
+          out_pu(c, c & 1, sUx);
+          lds_barrier();
         }
-        lds_barrier();
-        out_pu(c, c & 1, sUx);
-        lds_barrier();
       }
     }
   } else {
@@ -998,7 +1043,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
         lds_barrier();
       }
       for (int c = 0; c < nch; ++c) {
-        if constexpr (SAVE) save_state(c);
+        if constexpr (SAVE && !OUTW) save_state(c);
         cons_seg1(c & 1);
         lds_barrier();
         cons_seg2(c, c & 1);
@@ -1011,7 +1056,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
         lds_barrier();
         lds_barrier();
         lds_barrier();
-        if constexpr (SAVE) save_state(c);
+        if constexpr (SAVE && !OUTW) save_state(c);
         cons_seg1(0);
         lds_barrier();
         cons_seg2(c, 0);

@@ -190,8 +190,16 @@ def test_composition_and_decode_continuity(gdn):
     assert rel_l2(f64(state), f64(f_all)) < 2e-2
 
 
-def test_deterministic(gdn):
-    inp = make_prefill(2, 300, 2, 4, 128, 128, "bf16", init_state=True, seed=12)
+@pytest.mark.parametrize("case", ["batch", "packed", "segmented"])
+def test_deterministic(gdn, case):
+    """Repeated calls are bit-identical: no atomics, and the orders (longest-first sequences, the
+    segments' scan) are fixed by the inputs."""
+    if case == "batch":
+        inp = make_prefill(2, 300, 2, 4, 128, 128, "bf16", init_state=True, seed=12)
+    elif case == "packed":
+        inp = make_prefill(1, 0, 2, 4, 128, 128, "bf16", init_state=True, lengths=[300, 7, 300, 0, 129, 64], seed=12)
+    else:
+        inp = make_prefill(1, 4096, 1, 2, 128, 128, "bf16", init_state=True, seed=12)
     o1, f1 = run_gpu(gdn, inp)
     o2, f2 = run_gpu(gdn, inp)
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
