@@ -301,16 +301,15 @@ __global__ __launch_bounds__(512) void dstate_kernel(BwdParams p) {
     const T* sQ = reinterpret_cast<const T*>(B + L::iQ);
     const T* sdO = reinterpret_cast<const T*>(B + L::idO);
     const float* vec = reinterpret_cast<const float*>(B + L::iVec);
-    // -- dM' of this chunk to the workspace; Gram tiles P and A (lower tiles), s gam dO
+    // -- dM' of this chunk to the workspace (from its operand copy, as whole 16-byte
+    //    pieces); Gram tiles P and A (lower tiles), s gam dO
     {
-      T* dmw = static_cast<T*>(p.dm) + (static_cast<size_t>(sq.cbase + c) * p.Hv + h) * DK * DV;
-#pragma unroll
-      for (int i = 0; i < NMT; ++i) {
-        const int t = wave + NW * i, a = t / NJ, jc = t % NJ;
-        if (t >= NTL) break;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          dmw[static_cast<size_t>(16 * a + 4 * lg + r) * DV + col0 + 16 * jc + lr] = from_float<T>(dM[i][r]);
+      T* dmw = static_cast<T*>(p.dm) + (static_cast<size_t>(sq.cbase + c) * p.Hv + h) * DK * DV + col0;
+      constexpr int EP = 16 / sizeof(T), PPR = BV / EP;  // elements per piece, pieces per row
+      for (int i = tid; i < DK * PPR; i += NT) {
+        const int r = i / PPR, e = (i - r * PPR) * EP;
+        *reinterpret_cast<uint4*>(dmw + static_cast<size_t>(r) * DV + e) =
+            *reinterpret_cast<const uint4*>(sdMn + r * LDB + e);
       }
     }
     {
@@ -373,9 +372,6 @@ __global__ __launch_bounds__(512) void dstate_kernel(BwdParams p) {
     //    the other wavefronts stage the next chunk meanwhile
     if (wave < NJ) {
       const int jc = wave;
-      const size_t o0 = (static_cast<size_t>(cs) * p.Hv + h) * DV + col0 + 16 * jc + lr;
-      T* dzw = static_cast<T*>(p.dz) + o0;
-      float* dvw = p.dv + o0;
 #pragma unroll
       for (int b = 3; b >= 0; --b) {
         floatx4 w, sub = zero4();
@@ -393,16 +389,25 @@ __global__ __launch_bounds__(512) void dstate_kernel(BwdParams p) {
           const float bt = vec[V_BETA * C + row];
           sdZ[row * LDB + 16 * jc + lr] = zt;
           sdZb[row * LDB + 16 * jc + lr] = from_float<T>(-bt * vec[V_GAM * C + row] * u[r]);
-          if (row < Lc) {
-            dzw[static_cast<size_t>(row) * v_tok] = zt;
-            dvw[static_cast<size_t>(row) * v_tok] = bt * u[r];
-          }
+          sdU[row * LDF + 16 * jc + lr] = u[r];  // (this block's dU is read) dZ, for the copy-out
         }
       }
     } else if (c > 0) {
       stage_in(c - 1, 64 * NJ, std::integral_constant<int, NST>());
     }
     lds_barrier();
+    // -- dZ (workspace, T) and dv = beta dZ out as whole 16-byte pieces, by every
+    //    wavefront (the solving ones only wrote LDS)
+    if (tid < C * BV / 4) {
+      const int row = tid / (BV / 4), c4 = (tid - row * (BV / 4)) * 4;
+      if (row < Lc) {
+        const floatx4 z = *reinterpret_cast<const floatx4*>(sdU + row * LDF + c4);
+        const float bt = vec[V_BETA * C + row];
+        const size_t o0 = (static_cast<size_t>(cs + row) * p.Hv + h) * DV + col0 + c4;
+        *reinterpret_cast<floatx4*>(p.dv + o0) = bt * z;
+        *reinterpret_cast<typename Vec4<T>::type*>(static_cast<T*>(p.dz) + o0) = pack4<T>(z[0], z[1], z[2], z[3]);
+      }
+    }
     // -- dM = gam_C dM' + s Q^T diag(gam) dO - K^T diag(beta gam) dZ, then its operand copy
     {
       const float gC = vec[V_N * C];
