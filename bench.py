@@ -2,34 +2,43 @@
 """GDN token-mixer benchmark on one MI355X.
 
 One step = one gdn_fwd_chunked call (chunk-local gates, UT transform, W/U,
-masked products, state scan, outputs and final states) over the batch
-B=4, T=4096, 16 heads, dk=dv=128, bf16 in, fp32 state ("prefill_b4_t4096").
-``value`` is that prefill's throughput in Mtok/s with inputs resident in HBM.
-The same JSON line also carries
-  roofline      the prefill kernel's achieved algorithmic TFLOP/s against the
+masked products, state scan, outputs and final states) over the largest
+prefill workload: 64 packed sequences of lognormal length (210,119 tokens at
+seed 0), 16 q/k heads shared by 32 value heads, dk = dv = 128, bf16 in, fp32
+states ("varlen_64").  ``value`` is that prefill's throughput in Mtok/s with
+inputs resident in HBM.  The same JSON line also carries
+  roofline      the prefill call's achieved algorithmic TFLOP/s against the
                 2.5 PFLOP/s dense bf16 matrix-core peak, timed with HIP events
                 on the launch stream around the K back-to-back launches;
+  prefill       the headline's details: cold first call, per-launch p10/p90,
+                the time with a 512 MB scratch write between launches (caches
+                flushed), and the spread over three repeats of the K launches;
+  prefill_other the two other bf16 prefill workloads (4 x 4096 tokens x 16
+                heads; one 65,536-token row with 16 q/k / 32 value heads),
+                each with its own roofline, measured the same way;
   decode        64 consecutive gdn_decode_step calls on 256 sequences x 32 value
                 heads (512 MiB fp32 state): algorithmic GB/s against 8 TB/s;
   verify        gdn_decode_verify, 4 drafted tokens per sequence from the same
                 kind of live state: algorithmic GB/s against 8 TB/s;
-  epilogue      gdn_output_norm_gate over the prefill output: GB/s against 8 TB/s;
-  short_conv    gdn_short_conv with L2 norm over the prefill's q: GB/s against 8 TB/s;
-  bwd           gdn_bwd_chunked (all gradients) over the prefill's inputs:
+  epilogue      gdn_output_norm_gate over a 4 x 4096 x 16-head output: GB/s against 8 TB/s;
+  short_conv    gdn_short_conv with L2 norm over that workload's q: GB/s against 8 TB/s;
+  bwd           gdn_bwd_chunked (all gradients) over the 4 x 4096 x 16-head prefill:
                 algorithmic GB/s against 8 TB/s (its 197 flops per algorithmic
                 byte sit below the chip's ridge), and its dense-tile TFLOP/s;
-  cpu_baseline  the fp64 oracle on the host cores over the same workload.
+  cpu_baseline  the fp64 oracle on the host cores over the whole headline
+                workload, and the relative L2 error of the GPU's o and final
+                states against it (rel_l2_o, rel_l2_state).
 Inputs are seeded synthetic tensors (linear_attention_token_chunked_amd.inputs).
 Every timed loop starts after W untimed steps and at least --warm-seconds of
 untimed load, so that it sees the GPU at its steady clocks.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--warm-seconds S] [--no-cpu-baseline] [--all]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--warm-seconds S] [--no-cpu-baseline]
+                       [--workload NAME] [--no-others] [--no-decode]
 """
 
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -42,16 +51,6 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = {
-    "prefill": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "prefill.hip"),
-    "decode": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "decode.hip"),
-    "prefill_save": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "prefill.hip"),
-    "bwd_dstate": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "bwd.hip"),
-    "bwd_dlocal": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "bwd.hip"),
-    "verify": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "verify.hip"),
-    "epilogue": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "epilogue.hip"),
-    "short_conv": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "conv.hip"),
-}
 EPILOGUE_WORKLOAD = "epilogue_b4_t4096"
 SHORT_CONV_WORKLOAD = "short_conv_q_b4_t4096"
 
@@ -96,68 +95,53 @@ def bwd_bytes(tokens, N, Hqk, Hv, dk, dv, s_in):
     return tokens * per_tok + 3 * N * Hv * dk * dv * 4
 
 
-def source_hash(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def measured_traffic(family, workload):
+    """HBM bytes per call from committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs, or None when they
+    are missing or were taken on different kernel sources."""
+    from linear_attention_token_chunked_amd.rocprof_summary import sources_hash
 
-
-def measured_traffic(kernel, workload):
-    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs, or None
-    when they are missing or were taken on a different kernel source."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))[kernel]
+        rec = json.load(open(TRAFFIC_FILE))[f"{family}@{workload}"]
     except (OSError, KeyError, ValueError):
         return None
-    if rec.get("workload") != workload or rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
+    if rec.get("sources_sha256_16") != sources_hash(family):
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get("bytes_per_call")
 
 
 # ------------------------------------------------------------------ CPU baseline
-def _oracle_unit(args):
-    """Worker: the fp64 oracle on one (sequence, value head) unit."""
-    from threadpoolctl import threadpool_limits
-
-    from oracle import recurrent
-
-    q, k, v, g, beta = args
-    with threadpool_limits(1):
-        recurrent(q, k, v, g, beta)
-    return q.shape[1]
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
-def cpu_baseline(inp, workers):
-    """Time the oracle over every (sequence, value head) unit of the batch on `workers` processes."""
-    import multiprocessing as mp
+def cpu_baseline(pool, workers, inp, o, fin):
+    """The fp64 oracle over every (sequence, query/key head) piece of the workload on `workers`
+    forked processes (created before this process touched the GPU), timed as a whole, and the
+    relative L2 error of the GPU result (o, fin) against it."""
+    from oracle.parallel import prefill_errors
 
-    import numpy as np
-
-    f = {k: inp[k].float().numpy().astype(np.float64) for k in ("q", "k", "v", "g", "beta")}
-    B, T, Hqk, _ = f["q"].shape
-    Hv = f["v"].shape[2]
-    rep = Hv // Hqk
-    units = []
-    for b in range(B):
-        for h in range(Hv):
-            hq = h // rep
-            units.append((f["q"][b:b + 1, :, hq:hq + 1], f["k"][b:b + 1, :, hq:hq + 1], f["v"][b:b + 1, :, h:h + 1],
-                          f["g"][b:b + 1, :, h:h + 1], f["beta"][b:b + 1, :, h:h + 1]))
-    ctx = mp.get_context("fork")  # forked before this process touches the GPU
-    t0 = time.perf_counter()
-    with ctx.Pool(workers) as pool:
-        pool.map(_oracle_unit, units, chunksize=1)
-    dt = time.perf_counter() - t0
-    tokens = B * T
-    return {"value": tokens / dt / 1e6, "unit": "Mtok/s", "cores": workers, "kind": "oracle",
-            "sample": f"whole workload: {B}x{T} tokens, all {B * Hv} (sequence, value head) units of the fp64 "
-                      f"token recurrence, {dt:.2f} s wall on {workers} processes",
-            "seconds": round(dt, 3)}
+    err, dt, tokens = prefill_errors(pool, inp, o, fin)
+    s = err.summary()
+    return {"value": round(tokens / dt / 1e6, 5), "unit": "Mtok/s", "cores": workers, "kind": "oracle",
+            "sample": f"whole workload: {tokens} tokens, all {s['units']} (sequence, value head) units of the fp64 "
+                      f"token recurrence, one piece per (sequence, q/k head), {dt:.1f} s wall on {workers} processes",
+            "seconds": round(dt, 2), "cpu_model": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "rel_l2_o": s["rel_l2_o"], "rel_l2_state": s["rel_l2_state"],
+            "worst_unit_rel_l2_o": s["worst_unit_o"][1], "worst_unit_rel_l2_state": s["worst_unit_state"][1],
+            "finite": s["finite"]}
 
 
 # ------------------------------------------------------------------ GPU timing
 WARM_SECONDS = 1.0  # set from --warm-seconds
 
 
-def time_launches(fn, steps, warmup, torch):
+def time_launches(fn, steps, warmup, torch, warm_seconds=None):
     """Run fn() warmup times, and on for at least WARM_SECONDS of wall time in all, then time
     exactly `steps` calls back to back: wall clock around the whole loop (synchronised on both
     sides) and one pair of HIP events on the launch stream around it.  Returns the wall time
@@ -167,9 +151,10 @@ def time_launches(fn, steps, warmup, torch):
     The GPU raises its clocks only after some hundreds of milliseconds of sustained load;
     without the timed warm-up the first launches of a fresh process run up to 15 % slower
     than the steady state."""
+    warm_seconds = WARM_SECONDS if warm_seconds is None else warm_seconds
     t0 = time.perf_counter()
     n = 0
-    while n < warmup or time.perf_counter() - t0 < WARM_SECONDS:
+    while n < warmup or time.perf_counter() - t0 < warm_seconds:
         fn()
         n += 1
         if n % 16 == 0:
@@ -194,7 +179,19 @@ def time_launches(fn, steps, warmup, torch):
     return wall, mean_ms, per
 
 
-def bench_prefill(name, gdn, torch, steps, warmup):
+def prefill_tri_flops_per_token(Hqk, Hv, dk, dv, C):
+    """Triangle-aware count: the products with a masked or triangular factor (K K^T, Q K^T, T [K|V],
+    P U) counted at half their dense-tile flops."""
+    return Hqk * (2 * C * dk) + Hv * (C * (dk + dv) + C * dv + 6 * dk * dv)
+
+
+FLUSH_BYTES = 512 << 20  # scratch written between launches for the cache-flushed time (L2s and the 256 MB MALL)
+
+
+def bench_prefill(name, gdn, torch, steps, warmup, keep=False, repeats=3, flushed=10):
+    """Time gdn_fwd_chunked on one prefill workload: a cold first call; `steps` back-to-back launches
+    after the warm-up (the official loop) and two more such loops for the run-to-run spread;
+    per-launch p10/p90; and `flushed` launches each after a 512 MB scratch write (median)."""
     from linear_attention_token_chunked_amd.inputs import WORKLOADS, make_workload
 
     w = WORKLOADS[name]
@@ -218,17 +215,49 @@ def bench_prefill(name, gdn, torch, steps, warmup):
     torch.cuda.synchronize()
     cold_ms = (time.perf_counter() - c0) * 1e3
     wall, kern_ms, per = time_launches(step, steps, warmup, torch)
+    spread = [kern_ms]
+    for _ in range(repeats - 1):
+        spread.append(time_launches(step, steps, 0, torch, warm_seconds=0.0)[1])
+    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    fl = []
+    for _ in range(flushed):
+        scratch.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        fl.append(e0.elapsed_time(e1))
+    del scratch
+    fl.sort()
     tokens = B * T
     flops = prefill_flops_per_token(Hqk, Hv, dk, dv, w.chunk) * tokens
+    flops_tri = prefill_tri_flops_per_token(Hqk, Hv, dk, dv, w.chunk) * tokens
     nbytes = prefill_bytes(tokens, N, Hqk, Hv, dk, dv, dev["q"].element_size(), dev["initial_state"] is not None,
                            True)
-    return {
+    tflops = flops / (kern_ms * 1e-3) / 1e12
+    res = {
         "workload": name, "tokens": tokens, "B": B, "T": T, "num_seqs": N, "Hqk": Hqk, "Hv": Hv, "dk": dk, "dv": dv,
         "chunk": w.chunk, "ms_per_step": wall / steps * 1e3, "kernel_ms_mean": kern_ms,
         "kernel_ms_p10": per[len(per) // 10], "kernel_ms_p90": per[(len(per) * 9) // 10], "cold_ms": cold_ms,
-        "Mtok_s": tokens / (wall / steps) / 1e6, "flops_per_launch": flops, "bytes_per_launch": nbytes,
-        "tflops": flops / (kern_ms * 1e-3) / 1e12, "hbm_gbps": nbytes / (kern_ms * 1e-3) / 1e9,
-    }, inp
+        "repeats_kernel_ms": [round(x, 4) for x in spread],
+        "repeat_spread_pct": round(100 * (max(spread) - min(spread)) / min(spread), 2),
+        "flushed_kernel_ms_median": fl[len(fl) // 2],
+        "Mtok_s": tokens / (wall / steps) / 1e6, "flops_per_launch": flops, "flops_tri_per_launch": flops_tri,
+        "bytes_per_launch": nbytes, "tflops": tflops, "tflops_tri": flops_tri / (kern_ms * 1e-3) / 1e12,
+        "pct_mfma_peak": 100 * tflops / PEAK_BF16_TFLOPS,
+        "hbm_gbps": nbytes / (kern_ms * 1e-3) / 1e9, "pct_hbm_peak": 100 * nbytes / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic("prefill", name)},
+    }
+    res = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in res.items()}
+    kept = None
+    if keep:
+        torch.cuda.synchronize()
+        kept = (inp, out.cpu(), fin.cpu())
+    del dev, out, fin, ws
+    torch.cuda.empty_cache()
+    return res, kept
 
 
 def bench_decode(gdn, torch, warmup_rounds=1):
@@ -357,7 +386,6 @@ def bench_bwd(gdn, torch, steps=10):
     nbytes = bwd_bytes(tokens, w.B, w.Hqk, w.Hv, w.dk, w.dv, dev["q"].element_size())
     tflops = flops / (mean_ms * 1e-3) / 1e12
     gbps = nbytes / (mean_ms * 1e-3) / 1e9
-    parts = [measured_traffic(k, w.name) for k in ("prefill_save", "bwd_dstate", "bwd_dlocal")]
     # 198 flops per algorithmic byte, below the chip's 312 (2.5 PFLOP/s over 8 TB/s): the HBM roof is the lower one
     return {
         "workload": w.name, "tokens": tokens, "ms_per_call_mean": mean_ms, "ms_per_call_median": per[len(per) // 2],
@@ -366,21 +394,25 @@ def bench_bwd(gdn, torch, steps=10):
         "kernels": "saving prefill, state-gradient scan, local gradients (one call = all three)",
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(gbps / PEAK_HBM_GBPS, 4),
-                     "traffic": sum(parts) if all(x is not None for x in parts) else None},
+                     "traffic": measured_traffic("bwd", w.name)},
     }
+
+
+OTHER_PREFILL = ("prefill_b4_t4096", "prefill_t65536_gqa")
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--warm-seconds", type=float, default=1.0,
                     help="keep warming up (untimed) for at least this long per workload")
-    ap.add_argument("--workload", default="prefill_b4_t4096")
+    ap.add_argument("--workload", default="varlen_64", help="the headline prefill workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--all", action="store_true", help="also time the other prefill workloads (extra field)")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode, verify, epilogue, convolution "
+                                                               "and backward legs")
+    ap.add_argument("--no-others", action="store_true", help="skip the other prefill workloads")
     ap.add_argument("--pmc-calib-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -394,38 +426,47 @@ def main():
 
     import torch
 
-    from linear_attention_token_chunked_amd.inputs import WORKLOADS, make_workload
-
-    cpu = None
+    pool = workers = None
     if not args.no_cpu_baseline:
-        # before any GPU call: the oracle runs in forked worker processes
-        workers = max(1, min(16, len(os.sched_getaffinity(0))))
-        cpu = cpu_baseline(make_workload(WORKLOADS[args.workload]), workers)
+        # forked before this process touches the GPU; the oracle runs on it after the GPU legs
+        from oracle.parallel import host_workers, make_pool
+
+        workers = host_workers()
+        pool = make_pool(workers)
 
     from linear_attention_token_chunked_amd import gdn
 
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
-    res, _ = bench_prefill(args.workload, gdn, torch, args.steps, args.warmup)
-    traffic = measured_traffic("prefill", args.workload)
-    dec = None if args.no_decode else bench_decode(gdn, torch)
-    ver = None if args.no_decode else bench_verify(gdn, torch)
-    epi = None if args.no_decode else bench_epilogue(gdn, torch)
-    conv = None if args.no_decode else bench_short_conv(gdn, torch)
-    bwd = None if args.no_decode else bench_bwd(gdn, torch)
-    extra = {}
-    if args.all:
-        for name in ("prefill_t65536_gqa", "varlen_64"):
-            r, _ = bench_prefill(name, gdn, torch, max(3, args.steps // 10), 2)
-            r["pct_mfma_peak"] = round(100 * r["tflops"] / PEAK_BF16_TFLOPS, 2)
-            extra[name] = r
+    print(f"bench: prefill {args.workload}", file=sys.stderr, flush=True)
+    res, kept = bench_prefill(args.workload, gdn, torch, args.steps, args.warmup, keep=pool is not None)
+    others = {}
+    if not args.no_others:
+        for name in OTHER_PREFILL:
+            if name == args.workload:
+                continue
+            print(f"bench: prefill {name}", file=sys.stderr, flush=True)
+            others[name], _ = bench_prefill(name, gdn, torch, args.steps, args.warmup)
+    legs = {}
+    if not args.no_decode:
+        for leg, fn in (("decode", bench_decode), ("verify", bench_verify), ("epilogue", bench_epilogue),
+                        ("short_conv", bench_short_conv), ("bwd", bench_bwd)):
+            print(f"bench: {leg}", file=sys.stderr, flush=True)
+            legs[leg] = fn(gdn, torch)
             torch.cuda.empty_cache()
     if args.pmc_calib_mib:
         src = torch.empty(args.pmc_calib_mib << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
+    cpu = None
+    if pool is not None:
+        print("bench: fp64 oracle on the host over the headline workload", file=sys.stderr, flush=True)
+        inp, o_host, fin_host = kept
+        cpu = cpu_baseline(pool, workers, inp, o_host, fin_host)
+        pool.terminate()
+        pool.join()
     line = {
         "metric": "GDN prefill Mtok/s + % MFMA peak; decode-step HBM GB/s vs peak (1 GPU)",
         "value": round(res["Mtok_s"], 3),
@@ -439,21 +480,17 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": res["workload"], "batch": res["B"], "seq_len": res["T"], "qk_heads": res["Hqk"],
-                   "v_heads": res["Hv"], "head_dim_k": res["dk"], "head_dim_v": res["dv"], "chunk": res["chunk"],
-                   "state_dtype": "fp32", "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": round(res["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(res["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
-        "prefill": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in res.items()},
-        "decode": dec,
-        "verify": ver,
-        "epilogue": epi,
-        "short_conv": conv,
-        "bwd": bwd,
+        "config": {"workload": res["workload"], "batch": res["B"], "seq_len": res["T"], "num_seqs": res["num_seqs"],
+                   "qk_heads": res["Hqk"], "v_heads": res["Hv"], "head_dim_k": res["dk"], "head_dim_v": res["dv"],
+                   "chunk": res["chunk"], "state_dtype": "fp32", "parallelism": "single GPU"},
+        "roofline": res["roofline"],
+        "rel_l2_o": cpu["rel_l2_o"] if cpu else None,
+        "rel_l2_state": cpu["rel_l2_state"] if cpu else None,
+        "prefill": {k: v for k, v in res.items() if k != "roofline"},
+        "prefill_other": others or None,
+        **{k: legs.get(k) for k in ("decode", "verify", "epilogue", "short_conv", "bwd")},
         "cpu_baseline": cpu,
     }
-    if extra:
-        line["extra"] = extra
     print(json.dumps(line), flush=True)
 
 

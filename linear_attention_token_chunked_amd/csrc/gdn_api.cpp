@@ -66,7 +66,9 @@ gdn_status_t gdn_fwd_chunked(const gdn_dims_t* d, const void* q, const void* k, 
       !aligned(beta, 4) || !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(cu_seqlens, 4) ||
       !aligned(workspace, 256))
     return GDN_STATUS_MISALIGNED;
-  if (workspace_bytes < gdn_fwd_chunked_workspace_size(d)) return GDN_STATUS_WORKSPACE_TOO_SMALL;
+  const size_t need = gdn_fwd_chunked_workspace_size(d);
+  if (workspace_bytes < need) return GDN_STATUS_WORKSPACE_TOO_SMALL;
+  if (need > 0 && !workspace) return GDN_STATUS_INVALID_VALUE;
   if (d->num_seqs == 0) return GDN_STATUS_SUCCESS;
   // Token indices are 32-bit inside the kernels.
   if (static_cast<int64_t>(d->batch) * d->seqlen >= (int64_t(1) << 31)) return GDN_STATUS_NOT_SUPPORTED;
@@ -78,7 +80,9 @@ gdn_status_t gdn_fwd_chunked(const gdn_dims_t* d, const void* q, const void* k, 
   a.g = g;
   a.beta = beta;
   a.initial_state = initial_state;
-  a.cu_seqlens = cu_seqlens;
+  // One packed sequence is, by the cu_seqlens contract (cu = {0, T}), the single batch row: it takes
+  // the batch-row path, which is what gdn_fwd_chunked_workspace_size sized the workspace for.
+  a.cu_seqlens = d->num_seqs == 1 ? nullptr : cu_seqlens;
   a.o = o;
   a.final_state = final_state;
   a.batch = d->batch;

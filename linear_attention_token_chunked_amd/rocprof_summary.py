@@ -2,14 +2,20 @@
 
   python -m linear_attention_token_chunked_amd.rocprof_summary stats <trace_dir> <out.txt> --cmd "<command>"
       per-kernel call count and average / min / max duration from --kernel-trace output
-  python -m linear_attention_token_chunked_amd.rocprof_summary traffic <fetch_dir> <write_dir> <calib_mib> \
-        <out.json> <out.txt> --cmd "<command>"
-      HBM bytes per launch of the measured kernels from a FETCH_SIZE run and a
-      WRITE_SIZE run.  Each counter is scaled by the factor that makes it read the known
-      size of a plain device copy in the same run (calib_mib MiB read and written once).
+  python -m linear_attention_token_chunked_amd.rocprof_summary traffic <fetch_dir> <write_dir> <calib_mib> \\
+        <traffic.json> <out.txt> --workload family=name [...] --cmd "<command>"
+      HBM bytes per call of every measured family of kernels from a FETCH_SIZE run and a
+      WRITE_SIZE run of the same command.  Each counter is scaled by the factor that makes
+      it read the known size of a plain device copy in the same run (calib_mib MiB read and
+      written once).  A call's bytes are those of all the family's dispatches divided by the
+      number of calls (dispatches of the family's main kernel).  Records are merged into
+      traffic.json under "family@workload".
+  python -m linear_attention_token_chunked_amd.rocprof_summary counters <dir> <out.txt> --kernel SUBSTR \\
+        --cmd "<command>"
+      per-dispatch averages of every counter collected for the kernels whose name holds SUBSTR
 
-The traffic JSON records a hash of each kernel's source file; bench.py reports the
-traffic only while the source still has that hash.
+Each traffic record holds a hash of the source files its family is built from; bench.py
+reports the traffic only while those files still have that hash.
 """
 
 from __future__ import annotations
@@ -23,16 +29,30 @@ import json
 import os
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc")
+
+# Source files of each family of kernels the bench measures.
 SOURCES = {
-    "prefill": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "prefill.hip"),
-    "decode": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "decode.hip"),
-    "prefill_save": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "prefill.hip"),
-    "bwd_dstate": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "bwd.hip"),
-    "bwd_dlocal": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "bwd.hip"),
-    "verify": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "verify.hip"),
-    "epilogue": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "epilogue.hip"),
-    "short_conv": os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc", "conv.hip"),
+    "prefill": ["prefill.hip", "seg.hip", "scan.hip", "device_common.hpp"],
+    "bwd": ["prefill.hip", "bwd.hip", "device_common.hpp"],
+    "decode": ["decode.hip"],
+    "verify": ["verify.hip"],
+    "epilogue": ["epilogue.hip"],
+    "short_conv": ["conv.hip"],
 }
+# The kernel whose dispatches count the family's calls.
+MAIN = {"prefill": ("prefill", "scan"), "bwd": ("bwd_dlocal",), "decode": ("decode",), "verify": ("verify",),
+        "epilogue": ("epilogue",), "short_conv": ("short_conv",)}
+
+
+def sources_hash(family):
+    h = hashlib.sha256()
+    for f in SOURCES[family]:
+        path = os.path.join(CSRC, f)
+        if os.path.exists(path):
+            h.update(f.encode())
+            h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def _find(d, suffix):
@@ -42,29 +62,23 @@ def _find(d, suffix):
     return files
 
 
-def _kind(name):
-    if "prefill_kernel" in name:  # the last two template flags: the saving variant a backward pass
+def kind(name):
+    """(family, kernel) of a dispatch, or None for kernels that are not measured."""
+    if "prefill_kernel" in name:  # the two last template flags: the saving variant a backward pass
         if name.endswith("Lb1ELb0EEEvNS0_6ParamsE"):  # runs, and the segmented variant of long rows
-            return "prefill_save"
-        return "prefill_seg" if name.endswith("Lb0ELb1EEEvNS0_6ParamsE") else "prefill"
-    if "seg_correct_kernel" in name:
-        return "seg_correct"
-    if "seg_scan_step_kernel" in name:
-        return "seg_scan"
-    if "dstate_kernel" in name:
-        return "bwd_dstate"
-    if "dlocal_kernel" in name:
-        return "bwd_dlocal"
-    if "decode_kernel" in name:
-        return "decode"
-    if "verify_kernel" in name:
-        return "verify"
-    if "norm_gate_kernel" in name:
-        return "epilogue"
-    if "conv_kernel" in name:
-        return "short_conv"
+            return ("bwd", "prefill_save")
+        return ("prefill", "prefill_seg" if name.endswith("Lb0ELb1EEEvNS0_6ParamsE") else "prefill")
+    for sub, fam, k in (("order_kernel", "prefill", "order"), ("seg_correct_kernel", "prefill", "seg_correct"),
+                        ("seg_scan_step_kernel", "prefill", "seg_scan"), ("prep_kernel", "prefill", "prep"),
+                        ("scan_kernel", "prefill", "scan"),
+                        ("dstate_kernel", "bwd", "bwd_dstate"), ("dlocal_kernel", "bwd", "bwd_dlocal"),
+                        ("chunk_prefix_kernel", "bwd", "bwd_prefix"), ("zero_kernel", "bwd", "bwd_zero"),
+                        ("decode_kernel", "decode", "decode"), ("verify_kernel", "verify", "verify"),
+                        ("norm_gate_kernel", "epilogue", "epilogue"), ("conv_kernel", "short_conv", "short_conv")):
+        if sub in name:
+            return (fam, k)
     if "copyBuffer" in name or "copy" in name.lower():
-        return "copy"
+        return ("copy", "copy")
     return None
 
 
@@ -75,7 +89,7 @@ def stats(trace_dir, out, cmd):
     per = collections.defaultdict(list)
     for r in rows:
         per[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    lines = [f"# rocprofv3 kernel trace summary", f"# command: {cmd}", "",
+    lines = ["# rocprofv3 kernel trace summary", f"# command: {cmd}", "",
              f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10}  kernel"]
     for name, d in sorted(per.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"{len(d):6d} {sum(d) / len(d):10.2f} {min(d):10.2f} {max(d):10.2f}  {name[:150]}")
@@ -83,41 +97,69 @@ def stats(trace_dir, out, cmd):
     print("\n".join(lines))
 
 
-def _counter_per_dispatch(d, counter):
-    out = collections.defaultdict(list)
+def _counter(d, counter):
+    out = collections.defaultdict(list)  # (family, kernel) -> per-dispatch values (KiB)
     for f in _find(d, "counter_collection.csv"):
         for r in csv.DictReader(open(f)):
             if r["Counter_Name"] != counter:
                 continue
-            k = _kind(r["Kernel_Name"])
+            k = kind(r["Kernel_Name"])
             if k:
-                out[k].append((r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"])))
+                out[k].append(float(r["Counter_Value"]))
     return out
 
 
 def traffic(fetch_dir, write_dir, calib_mib, out_json, out_txt, cmd, workloads):
     calib = calib_mib * 1024 * 1024
-    fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
-    write = _counter_per_dispatch(write_dir, "WRITE_SIZE")
-    big = lambda lst: max(v for _, _, v in lst)  # the calibration copy is the largest copy dispatch
-    f_fetch = calib / (big(fetch["copy"]) * 1024)
-    f_write = calib / (big(write["copy"]) * 1024)
-    res = {"calibration": {"copy_bytes": calib, "fetch_factor": f_fetch, "write_factor": f_write}}
-    lines = ["# HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB), scaled by the",
+    fetch = _counter(fetch_dir, "FETCH_SIZE")
+    write = _counter(write_dir, "WRITE_SIZE")
+    f_fetch = calib / (max(fetch[("copy", "copy")]) * 1024)  # the calibration copy is the largest copy
+    f_write = calib / (max(write[("copy", "copy")]) * 1024)
+    try:
+        res = json.load(open(out_json))
+    except (OSError, ValueError):
+        res = {}
+    res["calibration"] = {"copy_bytes": calib, "fetch_factor": f_fetch, "write_factor": f_write}
+    lines = ["# HBM traffic per call from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB), scaled by the",
              f"# factor that makes a plain {calib_mib} MiB device copy read and write {calib_mib} MiB.",
              f"# command: {cmd}", f"# fetch factor {f_fetch:.4f}, write factor {f_write:.4f}", ""]
-    for k in ("prefill", "decode", "prefill_save", "bwd_dstate", "bwd_dlocal", "verify", "epilogue", "short_conv"):
-        if k not in fetch or k not in write:
+    for fam, wl in workloads.items():
+        kernels = sorted(k for (f, k) in fetch if f == fam)
+        calls = sum(len(fetch[(fam, k)]) for k in kernels if k in MAIN[fam])
+        if not calls:
             continue
-        fr = sum(v for _, _, v in fetch[k]) / len(fetch[k]) * 1024 * f_fetch
-        wr = sum(v for _, _, v in write[k]) / len(write[k]) * 1024 * f_write
-        res[k] = {"workload": workloads[k], "source_sha256_16": hashlib.sha256(open(SOURCES[k], "rb").read())
-                  .hexdigest()[:16], "read_bytes_per_launch": fr, "write_bytes_per_launch": wr,
-                  "bytes_per_launch": fr + wr, "dispatches": len(fetch[k])}
-        lines.append(f"{k:12s} {workloads[k]:22s} read {fr / 1e6:10.2f} MB  write {wr / 1e6:10.2f} MB  "
-                     f"total {(fr + wr) / 1e6:10.2f} MB per launch  ({len(fetch[k])} dispatches)")
-    json.dump(res, open(out_json, "w"), indent=1)
+        rd = sum(sum(fetch[(fam, k)]) for k in kernels) * 1024 * f_fetch / calls
+        wr = sum(sum(write.get((fam, k), [])) for k in kernels) * 1024 * f_write / calls
+        res[f"{fam}@{wl}"] = {"family": fam, "workload": wl, "sources_sha256_16": sources_hash(fam),
+                              "read_bytes_per_call": rd, "write_bytes_per_call": wr, "bytes_per_call": rd + wr,
+                              "calls": calls}
+        lines.append(f"{fam:10s} {wl:22s} read {rd / 1e6:10.2f} MB  write {wr / 1e6:10.2f} MB  "
+                     f"total {(rd + wr) / 1e6:10.2f} MB per call  ({calls} calls)")
+        for k in kernels:
+            n = len(fetch[(fam, k)])
+            kr = sum(fetch[(fam, k)]) * 1024 * f_fetch / n
+            kw = sum(write.get((fam, k), [0.0])) * 1024 * f_write / max(1, len(write.get((fam, k), [])))
+            lines.append(f"    {k:14s} read {kr / 1e6:10.2f} MB  write {kw / 1e6:10.2f} MB per dispatch "
+                         f"({n} dispatches)")
+    json.dump(res, open(out_json, "w"), indent=1, sort_keys=True)
     open(out_txt, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def counters(d, out, substr, cmd):
+    per = collections.defaultdict(list)
+    grid = set()
+    for f in _find(d, "counter_collection.csv"):
+        for r in csv.DictReader(open(f)):
+            if substr in r["Kernel_Name"]:
+                per[r["Counter_Name"]].append(float(r["Counter_Value"]))
+                grid.add((r["Kernel_Name"][:120], r["Grid_Size"], r.get("Workgroup_Size", "")))
+    lines = [f"# rocprofv3 counters per dispatch (average) of kernels matching '{substr}'", f"# command: {cmd}"]
+    lines += [f"# kernel {k} grid {g} workgroup {w}" for k, g, w in sorted(grid)]
+    lines.append("")
+    for name, v in sorted(per.items()):
+        lines.append(f"{name:28s} {sum(v) / len(v):18,.0f}   ({len(v)} dispatches)")
+    open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
@@ -135,20 +177,20 @@ def main():
     t.add_argument("out_json")
     t.add_argument("out_txt")
     t.add_argument("--cmd", default="")
-    t.add_argument("--prefill-workload", default="prefill_b4_t4096")
-    t.add_argument("--decode-workload", default="decode_n256")
-    t.add_argument("--verify-workload", default="verify_n256_t4")
-    t.add_argument("--epilogue-workload", default="epilogue_b4_t4096")
-    t.add_argument("--short-conv-workload", default="short_conv_q_b4_t4096")
+    t.add_argument("--workload", action="append", default=[], help="family=workload measured in this run")
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
+    c.add_argument("out")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--cmd", default="")
     a = ap.parse_args()
     if a.what == "stats":
         stats(a.trace_dir, a.out, a.cmd)
-    else:
+    elif a.what == "traffic":
         traffic(a.fetch_dir, a.write_dir, a.calib_mib, a.out_json, a.out_txt, a.cmd,
-                {"prefill": a.prefill_workload, "decode": a.decode_workload, "prefill_save": a.prefill_workload,
-                 "bwd_dstate": a.prefill_workload, "bwd_dlocal": a.prefill_workload,
-                 "verify": a.verify_workload, "epilogue": a.epilogue_workload,
-                 "short_conv": a.short_conv_workload})
+                dict(x.split("=", 1) for x in a.workload))
+    else:
+        counters(a.dir, a.out, a.kernel, a.cmd)
 
 
 if __name__ == "__main__":

@@ -6,7 +6,40 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
+TESTS = os.path.dirname(os.path.abspath(__file__))
+if TESTS not in sys.path:
+    sys.path.insert(0, TESTS)
+
+
+def _gpu_tests_deselected(config):
+    expr = " ".join((config.getoption("markexpr", default="") or "").split())
+    return expr == "not gpu"
 
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    # Worker processes for the fp64 oracle over whole full-size workloads.  They are forked here,
+    # before any test touches the GPU (a process that has initialised HIP must not fork).
+    config._oracle_pool = None
+    if not _gpu_tests_deselected(config):
+        from oracle.parallel import make_pool
+
+        config._oracle_pool = make_pool()
+
+
+def pytest_unconfigure(config):
+    pool = getattr(config, "_oracle_pool", None)
+    if pool is not None:
+        pool.terminate()
+        pool.join()
+
+
+@pytest.fixture(scope="session")
+def oracle_pool(request):
+    pool = request.config._oracle_pool
+    if pool is None:
+        from oracle.parallel import make_pool
+
+        # only reached when the marker expression deselected the GPU tests: no GPU in this process
+        pool = request.config._oracle_pool = make_pool(2)
+    return pool

@@ -10,7 +10,6 @@ import sys
 import numpy as np
 import torch
 
-from oracle import recurrent
 
 TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
 
@@ -42,18 +41,17 @@ def assert_close(name, got, ref, tol):
     return err
 
 
-def unit_oracle(inp, n, h, cu=None, T=None):
-    """Oracle for one (sequence n, value head h) unit of a prefill batch: returns (o [L, dv], final [dk, dv])."""
-    q, k, v, g, beta = (inp[x] for x in ("q", "k", "v", "g", "beta"))
-    Hqk, Hv = q.shape[2], v.shape[2]
-    hq = h // (Hv // Hqk)
-    if cu is not None:
-        b, s, e = 0, int(cu[n]), int(cu[n + 1])
-    else:
-        b, s, e = n, 0, q.shape[1]
-    sl = lambda t, head: t[b:b + 1, s:e, head:head + 1]
-    S0 = inp.get("initial_state")
-    S0 = S0[n:n + 1, h:h + 1] if S0 is not None else None
-    o, fin = recurrent(sl(q, hq), sl(k, hq), sl(v, h), g[b:b + 1, s:e, h:h + 1], beta[b:b + 1, s:e, h:h + 1],
-                       initial_state=S0)
-    return o[0, :, 0], fin[0, 0]
+def whole_check(pool, inp, o, fin, tol, label, scale=1.0):
+    """Whole-workload parity of a prefill result (see oracle.parallel): relative L2 of o and of the final
+    states over the whole tensors, and the worst (sequence, value head) unit, all within tol."""
+    from oracle.parallel import prefill_errors
+
+    err, secs, _ = prefill_errors(pool, inp, o, fin, scale=scale)
+    s = err.summary()
+    flush(f"  {label}: rel-L2 o {s['rel_l2_o']:.3e} state {s['rel_l2_state']:.3e} over {s['units']} units; "
+          f"worst unit o {s['worst_unit_o'][0]} {s['worst_unit_o'][1]:.3e}, "
+          f"state {s['worst_unit_state'][0]} {s['worst_unit_state'][1]:.3e} (oracle {secs:.1f} s)")
+    assert s["finite"], f"{label}: non-finite values"
+    assert s["rel_l2_o"] <= tol and s["rel_l2_state"] <= tol, f"{label}: whole-tensor rel-L2 above {tol}"
+    assert s["worst_unit_o"][1] <= tol and s["worst_unit_state"][1] <= tol, f"{label}: a unit above {tol}"
+    return s

@@ -198,6 +198,26 @@ def test_segmented_prefill_workspace(gdn):
     assert call_fwd(gdn, d, ws=FAKE + 128, ws_bytes=need) == MISALIGNED
 
 
+def test_needed_workspace_must_be_given(gdn):
+    """A declared size is not a buffer: with a workspace needed, a NULL one is rejected, whatever
+    workspace_bytes says (no silent path without it)."""
+    for d, cu in ((dims(gdn, B=1, T=65536, N=1, Hqk=16, Hv=32), 0), (dims(gdn, B=1, T=1000, N=64), FAKE)):
+        need = gdn.fwd_chunked_workspace_size(d)
+        assert need > 0
+        assert call_fwd(gdn, d, cu=cu, ws=0, ws_bytes=need) == INVALID
+        assert call_fwd(gdn, d, cu=cu, ws=0, ws_bytes=1 << 40) == INVALID
+
+
+def test_one_packed_sequence_is_a_batch_row(gdn):
+    """cu_seqlens with N = 1 is, by its contract {0, T}, the single batch row: the size query (which cannot
+    see cu_seqlens) and the call agree on the same workspace, and that workspace is required."""
+    row = dims(gdn, B=1, T=65536, N=1, Hqk=16, Hv=32)
+    need = gdn.fwd_chunked_workspace_size(row)
+    assert need > 0
+    assert call_fwd(gdn, row, cu=FAKE, ws_bytes=need - 1) == WORKSPACE_TOO_SMALL
+    assert call_fwd(gdn, row, cu=FAKE, ws=0, ws_bytes=need) == INVALID
+
+
 def test_verify_invalid(gdn):
     assert call_ver(gdn, dims(gdn, T=0)) == INVALID              # at least one token
     assert call_ver(gdn, dims(gdn, T=9)) == NOT_SUPPORTED        # at most eight

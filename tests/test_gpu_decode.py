@@ -46,35 +46,31 @@ def test_decode_small_matches_oracle(gdn, dtype, dk, dv, Hqk, Hv):
     assert_close("state", f64(state), ref_state, tol)
 
 
-def test_decode_full_workload_sampled_units(gdn):
-    """256 sequences x 32 value heads, 64 steps in place; oracle on 24 sampled units, all 64 steps."""
+def test_decode_full_workload_whole_tensors(gdn, oracle_pool):
+    """256 sequences x 32 value heads, 64 separate decode calls updating the 512 MiB state in place: every
+    element of o at every step and of the state after step 64 against 64 oracle decode steps per sequence
+    (forked host processes, one sequence each), whole tensors and every (sequence, value head) unit."""
+    from oracle.parallel import decode_errors
+
     w = WORKLOADS["decode_n256"]
-    flush(f"decode full {w}")
+    flush(f"decode full {w.name}: drawing inputs")
     inp = make_decode(w.N, w.Hqk, w.Hv, w.dk, w.dv, w.steps, w.dtype, seed=0)
     dev = to_dev(inp)
     state = dev["state"].clone()
     outs = []
+    flush("  GPU: 64 steps")
     for t in range(w.steps):
         outs.append(gdn.decode_step(dev["q"][t], dev["k"][t], dev["v"][t], dev["g"][t], dev["beta"][t], state))
-    o_all = torch.stack(outs)
+    o_all = torch.stack(outs).cpu()
+    fin = state.cpu()
     torch.cuda.synchronize()
-    assert bool(torch.isfinite(o_all.float()).all()) and bool(torch.isfinite(state).all())
-    rng = np.random.default_rng(123)
-    units = [(0, 0), (w.N - 1, w.Hv - 1)] + [(int(a), int(b)) for a, b in
-                                             zip(rng.integers(0, w.N, 22), rng.integers(0, w.Hv, 22))]
-    rep = w.Hv // w.Hqk
-    got_o, ref_o, got_s, ref_s = [], [], [], []
-    for n, h in units:
-        hq = h // rep
-        s = f64(inp["state"][n:n + 1, h:h + 1])
-        for t in range(w.steps):
-            ro, s = oracle_decode(inp["q"][t][n:n + 1, hq:hq + 1], inp["k"][t][n:n + 1, hq:hq + 1],
-                                  inp["v"][t][n:n + 1, h:h + 1], inp["g"][t][n:n + 1, h:h + 1],
-                                  inp["beta"][t][n:n + 1, h:h + 1], s)
-            ref_o.append(ro[0, 0])
-            got_o.append(f64(o_all[t, n, h]))
-        ref_s.append(s[0, 0])
-        got_s.append(f64(state[n, h]))
-        assert_close(f"o unit {(n, h)}", np.stack(got_o[-w.steps:]), np.stack(ref_o[-w.steps:]), TOL[torch.bfloat16])
-    assert_close("o sampled", np.stack(got_o), np.stack(ref_o), TOL[torch.bfloat16])
-    assert_close("state sampled", np.stack(got_s), np.stack(ref_s), TOL[torch.bfloat16])
+    flush("  oracle on the host")
+    err, secs = decode_errors(oracle_pool, inp, o_all, fin)
+    s = err.summary()
+    tol = TOL[torch.bfloat16]
+    flush(f"  {w.name}: rel-L2 o {s['rel_l2_o']:.3e} (64 steps) state {s['rel_l2_state']:.3e} over {s['units']} "
+          f"units; worst unit o {s['worst_unit_o'][0]} {s['worst_unit_o'][1]:.3e}, state "
+          f"{s['worst_unit_state'][0]} {s['worst_unit_state'][1]:.3e} (oracle {secs:.1f} s)")
+    assert s["finite"] and s["units"] == w.N * w.Hv
+    assert s["rel_l2_o"] <= tol and s["rel_l2_state"] <= tol
+    assert s["worst_unit_o"][1] <= tol and s["worst_unit_state"][1] <= tol
