@@ -33,17 +33,17 @@ gdn_status_t from_hip(hipError_t e) { return e == hipSuccess ? GDN_STATUS_SUCCES
 extern "C" {
 
 size_t gdn_fwd_chunked_workspace_size(const gdn_dims_t* d) {
-  // Few (sequence, value head) units in bf16 with dk = dv = 128 run in two passes, the chunk-local
-  // operands going through the workspace; otherwise the fused prefill keeps everything on chip, and
-  // packed sequences (batch 1, num_seqs > 1) only take a few bytes for their longest-first order.
-  if (!d || d->batch < 1 || d->seqlen < 0 || d->num_seqs < 0 || d->num_v_heads < 1 || d->chunk_size != 64)
+  // The fused prefill keeps every intermediate in LDS and registers.  Packed
+  // sequences (cu_seqlens, so batch 1 and num_seqs > 1) take a few bytes for
+  // their longest-first order; a few long bf16 rows (dk = dv = 128, no
+  // cu_seqlens) run as segments side by side, with a workspace for the
+  // segments' transitions and corrections.
+  if (!d || d->batch < 1 || d->seqlen < 0 || d->num_v_heads < 1 || d->chunk_size != 64) return 0;
+  if (d->num_seqs != d->batch) return d->batch == 1 ? gdn::order_workspace_bytes(d->num_seqs) : 0;
+  if (d->seqlen < 1) return 0;
+  if (d->dtype != GDN_DTYPE_BFLOAT16 || d->head_dim_k != 128 || d->head_dim_v != 128 || d->chunk_size != 64)
     return 0;
-  const bool packed = d->num_seqs != d->batch;
-  if (packed && d->batch != 1) return 0;
-  if (gdn::two_pass_applies(d->dtype == GDN_DTYPE_BFLOAT16, d->head_dim_k, d->head_dim_v, d->num_seqs,
-                            d->num_v_heads, d->seqlen))
-    return gdn::two_pass_parts(d->batch, d->seqlen, d->num_seqs, packed, d->num_v_heads).total;
-  return packed ? gdn::order_workspace_bytes(d->num_seqs) : 0;
+  return gdn::seg_workspace_bytes(d->batch, d->seqlen, d->num_v_heads);
 }
 
 gdn_status_t gdn_fwd_chunked(const gdn_dims_t* d, const void* q, const void* k, const void* v, const float* g,
@@ -227,9 +227,8 @@ size_t gdn_bwd_chunked_workspace_size(const gdn_dims_t* d) {
   if (!d || d->batch < 0 || d->seqlen < 0 || d->num_seqs < 0 || d->num_v_heads < 1 || d->head_dim_k < 1 ||
       d->head_dim_v < 1)
     return 0;
-  return gdn::bwd_parts(static_cast<int64_t>(d->batch) * d->seqlen, d->num_seqs, d->num_v_heads, d->head_dim_k,
-                        d->head_dim_v, d->dtype == GDN_DTYPE_BFLOAT16)
-      .total;
+  return gdn::bwd_workspace_bytes(static_cast<int64_t>(d->batch) * d->seqlen, d->num_seqs, d->num_v_heads,
+                                  d->head_dim_k, d->head_dim_v, d->dtype == GDN_DTYPE_BFLOAT16);
 }
 
 gdn_status_t gdn_bwd_chunked(const gdn_dims_t* d, const void* q, const void* k, const void* v, const float* g,

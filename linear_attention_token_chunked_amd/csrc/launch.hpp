@@ -35,7 +35,7 @@ struct PrefillArgs {
   void* save_state = nullptr;
   void* save_u = nullptr;
   const int32_t* chunk_base = nullptr;  // [N + 1] with cu_seqlens, else null (n * ceil(T / C))
-  // Caller's workspace (two-pass prefill of few units, see two_pass_parts; the
+  // Caller's workspace (segmented prefill of long rows, see seg_plan; the
   // longest-first order of packed sequences, see order_workspace_bytes).
   void* workspace = nullptr;
   size_t workspace_bytes = 0;
@@ -45,27 +45,25 @@ struct PrefillArgs {
 };
 
 // Workspace bytes for the longest-first order of num_seqs packed sequences
-// (0 where the natural order is kept: fewer than 2 or more than 4096 sequences).
+// (0 where the natural order is kept).
 size_t order_workspace_bytes(int num_seqs);
-// Ranks packed sequences by length, longest first (order[rank] = sequence).
-hipError_t launch_order(const int32_t* cu, int num_seqs, int32_t* order, hipStream_t stream);
 
-// Two-pass prefill of few (sequence, value head) units (bf16, dk = dv = 128): a
-// chunk-parallel pass writes every (chunk, value head)'s T = (I + A)^-1, masked
-// Q K^T and gate vectors to the workspace, and a sequential pass per unit runs
-// only the recurrence and the outputs from them.
-constexpr int kTwoPassBlockBytes = 13312;  // per (chunk slot, value head)
-constexpr int kTwoPassMaxUnits = 128;      // (sequence, value head) units up to which it runs
-struct TwoPassParts {
-  int64_t slots = 0;  // chunk slots: B * ceil(T / 64), or T / 64 + N for packed sequences
-  size_t chunk_base = 0, order = 0, blocks = 0, total = 0;  // byte offsets in the workspace; total size
+// Segmented prefill of a few long batch rows (bf16, dk = dv = 128, no cu_seqlens):
+// every row is cut into nseg segments of seg_len tokens that run side by side.
+struct SegPlan {
+  int nseg = 0, seg_len = 0;
+  void* qt = nullptr;       // [B, T, Hv, dk] bf16: the transition runs' outputs
+  float* fin = nullptr;     // [nseg][B][Hv][dk][dv] fp32: end states from the zero state (segment 0: the row's)
+  float* phi = nullptr;     // [nseg][B][Hv][dk][dk] fp32: transitions of the segments
+  void* mstart = nullptr;   // [nseg][B][Hv][dv][dk] bf16: start states of the segments, transposed
+  float* mbuf = nullptr;    // two [B][Hv][dk][dv] fp32 buffers for the scan
+  size_t mbuf_stride = 0;   // floats between them
 };
-bool two_pass_applies(bool bf16, int dk, int dv, int num_seqs, int Hv, int seqlen);
-TwoPassParts two_pass_parts(int batch, int T, int N, bool packed, int Hv);
-hipError_t launch_two_pass(const PrefillArgs& a, hipStream_t stream);
-// Exclusive prefix sum of the packed sequences' chunk counts (ceil(L_n / 64)): chunk_base[n] is
-// sequence n's first chunk slot, chunk_base[N] the number of slots.
-hipError_t launch_chunk_base(const int32_t* cu, int num_seqs, int32_t* chunk_base, hipStream_t stream);
+// Whether (and how) rows of T tokens are segmented for batch * Hv units.
+bool seg_plan(int batch, int T, int Hv, SegPlan* sp);
+size_t seg_workspace_bytes(int batch, int T, int Hv);  // 0 when not segmented
+void seg_carve(void* ws, int batch, int T, int Hv, SegPlan* sp);
+hipError_t launch_seg_finish(const PrefillArgs& a, const SegPlan& sp, hipStream_t stream);
 
 // Multi-token verify: Tv (<= kMaxVerifyTokens) consecutive steps per sequence.
 constexpr int kMaxVerifyTokens = 8;
@@ -120,10 +118,7 @@ struct BwdArgs {
   float scale;
   bool bf16;
 };
-struct BwdParts {
-  size_t cpre = 0, state = 0, dm = 0, u = 0, dz = 0, total = 0;  // byte offsets in the workspace; total size
-};
-BwdParts bwd_parts(int64_t tokens, int num_seqs, int Hv, int dk, int dv, bool bf16);
+size_t bwd_workspace_bytes(int64_t tokens, int num_seqs, int Hv, int dk, int dv, bool bf16);
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);

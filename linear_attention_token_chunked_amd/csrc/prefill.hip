@@ -40,11 +40,114 @@
 #include <type_traits>
 #include <utility>
 
+#include "device_common.hpp"
 #include "launch.hpp"
-#include "prefill_common.hpp"
 
 namespace gdn {
 namespace {
+
+constexpr int C = 64;                    // chunk length
+constexpr int NP = 4;                    // producer wavefronts (consumer wavefronts: a template parameter)
+constexpr int PTHREADS = 64 * NP;
+// The bf16 V tile is read only down its columns; it stores the 16-column
+// blocks of a row at swizzled places: block b of row r sits at block
+// b ^ swz(r).  A transposing read covers four rows of one block per 16-lane
+// group and eight rows per 32 lanes; the swizzle puts those eight rows'
+// 32-byte runs on eight different bank windows (unswizzled, 256-byte rows
+// would put them all on the same one).
+template <int W>
+__device__ __forceinline__ int swz(int r) {
+  constexpr int NB = W / 16;                    // 16-column blocks per row
+  constexpr int RPW = W >= 128 ? 1 : 128 / W;   // rows per 256 bytes
+  return (r / RPW) & (NB - 1);
+}
+template <int W>
+__device__ __forceinline__ int swz_off(int r, int c) {  // element offset of column c of row r
+  return r * W + ((((c >> 4) ^ swz<W>(r)) << 4) | (c & 15));
+}
+// Transposing 8-byte LDS read (see lds_col4).
+__device__ __forceinline__ bf16x4 tr_read(const bf16* ptr) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) s4*>(reinterpret_cast<size_t>(ptr)));
+  return __builtin_bit_cast(bf16x4, v);
+}
+// lds_col4<bf16> for a swizzled tile of width W.
+template <int W>
+__device__ __forceinline__ bf16x4 swz_col4(const bf16* base, int r0, int c0, int lane) {
+  const int lg = lane >> 4, lr = lane & 15;
+  return tr_read(base + swz_off<W>(r0 + 4 * lg + (lr >> 2), c0 + 4 * (lr & 3)));
+}
+
+// The second, column-read copy of K (bf16, rows of DK keys).  The K^T operand
+// for state tile a (keys per state_row) takes from each token row the four
+// 8-byte runs of keys 32(a>>1) + 4(a&1) + 8m, m = 0..3, 16 bytes apart.  The
+// 8-byte units u of row r are stored at u ^ (8 kn_x(r) + kn_e(r)): kn_x
+// permutes pairs of 32-byte blocks and kn_e swaps the halves of each 16-byte
+// piece, so the eight rows one 32-lane half of a transposing read covers use
+// 32 distinct bank pairs.  kn_e is bit 2 of the row.
+template <int DK>
+__device__ __forceinline__ int kn_x(int r) { return (r / (128 / DK)) & (DK / 32 - 1); }
+__device__ __forceinline__ int kn_e(int r) { return (r >> 2) & 1; }
+// Element offset of the (unswapped) 16-byte piece pc of row r.
+template <int DK>
+__device__ __forceinline__ int kn_piece(int r, int pc) { return r * DK + 8 * (pc ^ (kn_x<DK>(r) << 2)); }
+// Read addresses, split into a per-lane part and a per-tile part: the rows a
+// transposing read covers start at multiples of 8, where the swizzle depends
+// on the lane only.
+template <int DK>
+struct KnCols {
+  const bf16* lane_base;
+  int x, e;
+  __device__ __forceinline__ KnCols(const bf16* base, int lane) {
+    const int rl = 4 * (lane >> 4) + ((lane & 15) >> 2);
+    x = kn_x<DK>(rl);
+    e = kn_e(rl);
+    lane_base = base + rl * DK + 8 * (lane & 3);
+  }
+  __device__ __forceinline__ const bf16* tile(int a) const {
+    return lane_base + 32 * ((a >> 1) ^ x) + 4 * ((a & 1) ^ e);
+  }
+};
+
+// Operand fragment of k-group kg built from accumulator tiles tile(kg*TPG + t).
+template <class T, class F>
+__device__ __forceinline__ typename Mma<T>::frag chain_frag(F tile, int kg) {
+  if constexpr (Mma<T>::TPG == 2) {
+    return Mma<T>::chain(tile(2 * kg), tile(2 * kg + 1));
+  } else {
+    return Mma<float>::chain(tile(kg));
+  }
+}
+
+// Per-token gate vectors of a chunk, C floats each, in this order.
+enum { VEC_EG, VEC_BETA, VEC_EGC_G, VEC_EGC, VEC_GL, VEC_E0, VEC_N = VEC_E0 + 3 };
+
+// Decay factors exp(G_i - G_j) (j <= i, else 0) of the 16x16 tile (ti, tj) of a
+// chunk, for the accumulator layout that gives the lane i = 16ti + lr and
+// j = 16tj + 4lg + s.  Below the diagonal blocks they are products of two
+// factors no larger than one that the gate scan stores, exp(G_i - G_r) and
+// exp(G_r - G_j) with r the last token of tile tj (G is non-increasing);
+// on a diagonal block they are formed directly.
+__device__ __forceinline__ floatx4 decay_tile(const float* vec, int ti, int tj, int lg, int lr) {
+  const int i = 16 * ti + lr;
+  floatx4 d;
+  if (ti > tj) {
+    const float* e = vec + (VEC_E0 + tj) * C;
+    const floatx4 ej = *reinterpret_cast<const floatx4*>(e + 16 * tj + 4 * lg);
+    d = ej * e[i];
+  } else {
+    const float* gl = vec + VEC_GL * C;
+    const float Gi = gl[i];
+    const floatx4 Gj = *reinterpret_cast<const floatx4*>(gl + 16 * tj + 4 * lg);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int j = 16 * tj + 4 * lg + s4;
+      d[s4] = __builtin_amdgcn_exp2f(j <= i ? Gi - Gj[s4] : -__builtin_inff());  // exp2(-inf) = 0
+    }
+  }
+  return d;
+}
 
 // LDS layout.  K and Q rows are padded against bank conflicts (see LDK).
 template <class T, int DK, int BV, int NSTAGE, int NCW, bool OUTW>
@@ -126,9 +229,102 @@ struct Params {
   void *save_state, *save_u;  // element type T
   const int32_t* chunk_base;
   const int32_t* order;  // packed sequences, longest first (null: natural order)
+  // SEG: segments of seg_len tokens (see seg.hip); qt receives the transition
+  // runs' outputs, seg_fin / seg_phi their end states [nseg][batch][Hv][DK][DV]
+  void* qt;
+  float *seg_fin, *seg_phi;
+  int seg_len, nseg, batch;
   int T, Hqk, Hv, nslices;
   int grp, ngroups;  // units per group sharing keys and queries, number of groups
   float scale;
+};
+
+// Producers' raw operands of one chunk (K rows, this slice's V rows, gates),
+// loaded one chunk ahead.
+template <class T, int DK, int BV>
+struct ChunkRegs {
+  typedef typename Mma<T>::frag frag;
+  static constexpr int EPB = 16 / sizeof(T);
+  static constexpr int KPR = DK / EPB;                  // 16-byte pieces per K / Q row
+  static constexpr int KIT = C * KPR / PTHREADS;        // K (and Q) pieces per producer thread
+  static constexpr int RPI = 64 / KPR;                  // K rows per wave-wide load
+  static constexpr int VPR = BV / EPB;                  // 16-byte pieces per V row (this slice)
+  static constexpr int VIT = (C * VPR + PTHREADS - 1) / PTHREADS;
+  static_assert(C * KPR % PTHREADS == 0 && KIT % 2 == 0 && RPI % 4 == 0, "K rows split evenly");
+  frag k[KIT], q[KIT], v[VIT];
+  float g, b;
+
+  // Row of the K / Q piece a producer thread holds in slot it (its column is
+  // piece lane % KPR).  Bit 2 of the row is bit 0 of it, so the half swap of
+  // the column-read K copy (kn_e) is known at compile time.
+  __device__ __forceinline__ static int kq_row(int it, int tid) {
+    const int rr = (tid & 63) / KPR, w = tid >> 6;
+    return (rr & 3) | ((it & 1) << 2) | (((rr >> 2) + (RPI / 4) * (w + NP * (it >> 1))) << 3);
+  }
+
+  // Every load is unconditional and reads a valid row (rows past the end of
+  // the sequence read its last token): a select on a loaded value would make
+  // the compiler wait for the load on the spot.  The padded rows are finite
+  // and harmless because their gates are masked to g = 0, beta = 0, which
+  // zeroes their rows of A, Z and U exactly.  Consecutive lanes read
+  // consecutive 16-byte pieces of a row.
+  // Offsets inside a chunk are 32-bit byte counts (a token row of q, k or v
+  // is at most 4096 heads x 128 x 4 bytes, checked on the host), so the
+  // loads take a uniform 64-bit base plus one 24-bit multiply per row.
+  __device__ __forceinline__ void load(const T* kb, const T* qb, const T* vb, uint32_t qk_row, uint32_t v_row,
+                                       const float* gb, const float* bb, uint32_t g_row, int Lc, int tid,
+                                       bool vzero = false) {
+    const char* kc = reinterpret_cast<const char*>(kb);
+    const char* qc = reinterpret_cast<const char*>(qb);
+    const char* vc = reinterpret_cast<const char*>(vb);
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+      const uint32_t off = __umul24(min(kq_row(it, tid), Lc - 1), qk_row) + (tid % KPR) * 16;
+      k[it] = *reinterpret_cast<const frag*>(kc + off);
+      q[it] = *reinterpret_cast<const frag*>(qc + off);
+    }
+    if (vzero) {  // (a workgroup-uniform branch)
+#pragma unroll
+      for (int it = 0; it < VIT; ++it) v[it] = frag{};
+    } else {
+#pragma unroll
+      for (int it = 0; it < VIT; ++it) {
+        const int t = min(tid + it * PTHREADS, C * VPR - 1);
+        v[it] = *reinterpret_cast<const frag*>(vc + __umul24(min(t / VPR, Lc - 1), v_row) + (t % VPR) * 16);
+      }
+    }
+    const int gl = tid - (PTHREADS - 64);  // the last producer wave owns the gates, one token per lane
+    if (gl >= 0) {
+      const uint32_t off = __umul24(min(gl, Lc - 1), g_row);
+      g = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(gb) + off);
+      b = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(bb) + off);
+    }
+  }
+
+  // K, Q -> padded rows in natural key order; V and (if sKn) the column-read
+  // copy of K -> swizzled rows.  Every store is one 16-byte piece.
+  __device__ __forceinline__ void store(T* sK, T* sQ, T* sV, T* sKn, int LDK, int LDV, int tid) const {
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+      const int r = kq_row(it, tid), pc = tid % KPR;
+      *reinterpret_cast<frag*>(sK + r * LDK + pc * EPB) = k[it];
+      *reinterpret_cast<frag*>(sQ + r * LDK + pc * EPB) = q[it];
+      if constexpr (sizeof(T) == 2) {
+        if (sKn) {
+          const frag x = (it & 1) ? __builtin_shufflevector(k[it], k[it], 4, 5, 6, 7, 0, 1, 2, 3) : k[it];
+          *reinterpret_cast<frag*>(sKn + kn_piece<DK>(r, pc)) = x;
+        }
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < VIT; ++it) {
+      const int t = tid + it * PTHREADS;
+      if (t < C * VPR) {
+        const int r = t / VPR, c = (t % VPR) * EPB;
+        *reinterpret_cast<frag*>(sV + (sizeof(T) == 2 ? swz_off<BV>(r, c) : r * LDV + c)) = v[it];
+      }
+    }
+  }
 };
 
 // Gram tiles (ti >= tj) of producer wave W, grouped by token-row tile so that
@@ -154,8 +350,9 @@ template <> struct OutPTiles<1> { static constexpr int n = 4, ti[4] = {2, 2, 3, 
 
 // SAVE: the variant a backward pass runs first; it keeps each chunk's starting
 // state and U (as T, the precision of the products' operands) and writes no
-// output.
-template <class T, int DK, int DV, int BV, int NSTAGE, int NCW, bool OUTW, bool SAVE>
+// output.  SEG: the segmented variant (seg.hip): the units are virtual
+// sequences, a segment of a batch row each.
+template <class T, int DK, int DV, int BV, int NSTAGE, int NCW, bool OUTW, bool SAVE, bool SEG>
 __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kernel(Params p) {
   using L = Layout<T, DK, BV, NSTAGE, NCW, OUTW>;
   using MM = Mma<T>;
@@ -179,9 +376,10 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
   const int lr = lane & 15;
 
   // Workgroup -> (unit, dv-slice).  Units that read the same keys and queries
-  // (the value heads of one q/k head) form a group of p.grp, and the members
-  // of a group and their slices get ids 8 apart, so they run on one XCD and
-  // share its L2.
+  // (the value heads of one q/k head; in the segmented variant also the
+  // zero-state and transition runs of one segment) form a group of p.grp, and
+  // the members of a group and their slices get ids 8 apart, so they run on
+  // one XCD and share its L2.
   const int xcd = blockIdx.x & 7;
   const int rest = blockIdx.x >> 3;
   const int slice = rest % p.nslices;
@@ -189,11 +387,31 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
   const int grp = (rest / p.nslices / p.grp) * 8 + xcd;
   if (grp >= p.ngroups) return;
   const int hg = p.Hv / p.Hqk;  // value heads per q/k head
-  const int unit = grp * p.grp + member;  // = sequence * Hv + h
-  const int h = unit % p.Hv;
-  const int n = p.order ? p.order[unit / p.Hv] : unit / p.Hv;
-  const int bos = p.cu ? p.cu[n] : n * p.T;
-  const int eos = p.cu ? p.cu[n + 1] : bos + p.T;
+  int n, h;
+  int b, seg = 0;    // SEG: the batch row and segment of the run
+  bool phi = false;  // SEG: a transition run (v = 0 from the identity state)
+  int bos, eos;
+  if constexpr (SEG) {
+    // group (row, segment, q/k head); member (run, value head): segment 0 has
+    // one run from the row's initial state, every later segment a run from the
+    // zero state and a transition run
+    const int bs = grp / p.Hqk, run = member / hg;
+    seg = bs % p.nseg;
+    b = bs / p.nseg;
+    if (seg == 0 && run > 0) return;
+    h = (grp % p.Hqk) * hg + member % hg;
+    phi = run == 1;
+    n = seg == 0 ? b : p.batch + b * 2 * (p.nseg - 1) + 2 * (seg - 1) + run;  // (virtual sequence)
+    bos = b * p.T + seg * p.seg_len;
+    eos = min(b * p.T + p.T, bos + p.seg_len);
+  } else {
+    const int unit = grp * p.grp + member;  // = sequence * Hv + h
+    h = unit % p.Hv;
+    n = p.order ? p.order[unit / p.Hv] : unit / p.Hv;
+    b = n;
+    bos = p.cu ? p.cu[n] : n * p.T;
+    eos = p.cu ? p.cu[n + 1] : bos + p.T;
+  }
   const int hq = h / hg;
   const int nch = (eos - bos + C - 1) / C;
   const int col0 = slice * BV;
@@ -203,7 +421,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
   const T* qg = static_cast<const T*>(p.q);
   const T* kgp = static_cast<const T*>(p.k);
   const T* vg = static_cast<const T*>(p.v);
-  T* og = static_cast<T*>(p.o);
+  T* og = static_cast<T*>(SEG && phi ? p.qt : p.o);
   const size_t qk_tok = static_cast<size_t>(p.Hqk) * DK;
   const size_t v_tok = static_cast<size_t>(p.Hv) * DV;
 
@@ -218,7 +436,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
     const size_t tg = static_cast<size_t>(cs) * p.Hv + h;
     pre.load(kgp + tq, qg + tq, vg + tv, static_cast<uint32_t>(qk_tok * sizeof(T)),
              static_cast<uint32_t>(v_tok * sizeof(T)), p.g + tg, p.beta + tg, static_cast<uint32_t>(p.Hv * 4),
-             min(C, eos - cs), tid);
+             min(C, eos - cs), tid, SEG && phi);
   };
 
   // Stage the chunk's K, Q, V and gates; issue the next chunk's loads.  (The
@@ -370,13 +588,26 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
   const size_t sbase = (static_cast<size_t>(n) * p.Hv + h) * DK * DV;
   const int slane = MM::state_row(0, lg, 0) * DV + wcol + lr;
   if (consumer) {
-    const float* h0 = p.h0 + sbase;
+    if constexpr (SEG) {  // the row's initial state, the zero state, or (transition runs) the identity
+      const float* h0 = seg == 0 && p.h0 ? p.h0 + (static_cast<size_t>(b) * p.Hv + h) * DK * DV : nullptr;
 #pragma unroll
-    for (int a = 0; a < KT; ++a)
+      for (int a = 0; a < KT; ++a)
 #pragma unroll
-      for (int j = 0; j < NTW; ++j)
+        for (int j = 0; j < NTW; ++j)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) Ms[a][j][s] = p.h0 ? h0[slane + MM::state_row(a, 0, s) * DV + 16 * j] : 0.f;
+          for (int s = 0; s < 4; ++s) {
+            const int row = MM::state_row(a, lg, s), col = wcol + 16 * j + lr;
+            Ms[a][j][s] = h0 ? h0[row * DV + col] : (phi && row == col ? 1.f : 0.f);
+          }
+    } else {
+      const float* h0 = p.h0 + sbase;
+#pragma unroll
+      for (int a = 0; a < KT; ++a)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) Ms[a][j][s] = p.h0 ? h0[slane + MM::state_row(a, 0, s) * DV + 16 * j] : 0.f;
+    }
   }
 
   // The state at the start of chunk c (SAVE).
@@ -836,7 +1067,17 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
     }
   }
 
-  if (consumer && p.hT) {
+  if constexpr (SEG) {  // every run's end state, for the scan over segments
+    if (consumer) {
+      float* e = (phi ? p.seg_phi : p.seg_fin) + ((static_cast<size_t>(seg) * p.batch + b) * p.Hv + h) * DK * DV;
+#pragma unroll
+      for (int a = 0; a < KT; ++a)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) e[slane + MM::state_row(a, 0, s) * DV + 16 * j] = Ms[a][j][s];
+    }
+  } else if (consumer && p.hT) {
     float* hT = p.hT + sbase;
 #pragma unroll
     for (int a = 0; a < KT; ++a)
@@ -847,8 +1088,8 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
   }
 }
 
-template <class T, int DK, int DV, int BV, int NSTAGE, int NCW, bool OUTW, bool SAVE>
-hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
+template <class T, int DK, int DV, int BV, int NSTAGE, int NCW, bool OUTW, bool SAVE, bool SEG = false>
+hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream, const SegPlan* sp = nullptr) {
   using L = Layout<T, DK, BV, NSTAGE, NCW, OUTW>;
   static_assert(L::bytes <= 160 * 1024, "LDS budget of one gfx950 compute unit");
   Params p;
@@ -872,14 +1113,27 @@ hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
   p.grp = a.Hv / a.Hqk;
   p.ngroups = a.num_seqs * a.Hqk;
   p.scale = a.scale;
+  p.qt = nullptr;
+  p.seg_fin = p.seg_phi = nullptr;
+  p.seg_len = p.nseg = 0;
+  p.batch = a.batch;
+  if constexpr (SEG) {  // virtual sequences: every row's segments, later ones twice
+    p.qt = sp->qt;
+    p.seg_fin = sp->fin;
+    p.seg_phi = sp->phi;
+    p.seg_len = sp->seg_len;
+    p.nseg = sp->nseg;
+    p.grp = 2 * (a.Hv / a.Hqk);  // (segment 0 uses half of its group)
+    p.ngroups = a.batch * sp->nseg * a.Hqk;
+  }
   if (p.ngroups == 0) return hipSuccess;
   const int groups_pad = (p.ngroups + 7) / 8 * 8;
   const dim3 grid(groups_pad * p.grp * p.nslices);
   hipError_t e = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&prefill_kernel<T, DK, DV, BV, NSTAGE, NCW, OUTW, SAVE>),
+      reinterpret_cast<const void*>(&prefill_kernel<T, DK, DV, BV, NSTAGE, NCW, OUTW, SAVE, SEG>),
       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(L::bytes));
   if (e != hipSuccess) return e;
-  prefill_kernel<T, DK, DV, BV, NSTAGE, NCW, OUTW, SAVE>
+  prefill_kernel<T, DK, DV, BV, NSTAGE, NCW, OUTW, SAVE, SEG>
       <<<grid, dim3(64 * (NP + NCW * (OUTW ? 2 : 1))), L::bytes, stream>>>(p);
   return hipGetLastError();
 }
@@ -912,6 +1166,8 @@ int slice_config(int units, int dv) {
 // lengths as uneven as a lognormal mix, that tail was a quarter of the time).
 // Rank of sequence i = the number of sequences longer than it, or as long and
 // before it: one thread per sequence, all lengths staged through LDS in turn.
+constexpr int kMaxOrdered = 4096;  // beyond this many sequences the natural order is kept
+
 __global__ __launch_bounds__(256) void order_kernel(const int32_t* cu, int N, int32_t* order) {
   __shared__ int len[256];
   const int i = blockIdx.x * 256 + threadIdx.x;
@@ -932,23 +1188,32 @@ __global__ __launch_bounds__(256) void order_kernel(const int32_t* cu, int N, in
 }
 }  // namespace
 
-hipError_t launch_order(const int32_t* cu, int num_seqs, int32_t* order, hipStream_t stream) {
-  order_kernel<<<dim3((num_seqs + 255) / 256), dim3(256), 0, stream>>>(cu, num_seqs, order);
-  return hipGetLastError();
+size_t order_workspace_bytes(int num_seqs) {
+  return num_seqs >= 2 && num_seqs <= kMaxOrdered ? (static_cast<size_t>(num_seqs) * 4 + 255) / 256 * 256 : 0;
 }
 
 hipError_t launch_prefill(const PrefillArgs& args, hipStream_t stream) {
   if (args.chunk != C) return hipErrorInvalidValue;
   PrefillArgs a = args;
   const int units = a.num_seqs * a.Hv;
-  // Few units: a chunk-parallel pass for the state-independent operands, then the recurrence alone.
-  if (!a.save_state && a.workspace && two_pass_applies(a.bf16, a.dk, a.dv, a.num_seqs, a.Hv, a.seqlen))
-    return launch_two_pass(a, stream);
-  if (a.cu_seqlens && !a.save_state && a.workspace && order_workspace_bytes(a.num_seqs)) {
+  if (a.cu_seqlens && !a.save_state && a.workspace && order_workspace_bytes(a.num_seqs) &&
+      a.workspace_bytes >= order_workspace_bytes(a.num_seqs)) {
     int32_t* order = static_cast<int32_t*>(a.workspace);
-    const hipError_t e = launch_order(a.cu_seqlens, a.num_seqs, order, stream);
+    order_kernel<<<dim3((a.num_seqs + 255) / 256), dim3(256), 0, stream>>>(a.cu_seqlens, a.num_seqs, order);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     a.order = order;
+  }
+  // A few long rows: segments side by side, finished by a scan and a correction.
+  if (a.bf16 && a.dk == 128 && a.dv == 128 && !a.cu_seqlens && !a.save_state && a.workspace) {
+    SegPlan sp;
+    if (seg_plan(a.batch, a.seqlen, a.Hv, &sp) &&
+        a.workspace_bytes >= seg_workspace_bytes(a.batch, a.seqlen, a.Hv)) {
+      seg_carve(a.workspace, a.batch, a.seqlen, a.Hv, &sp);
+      const hipError_t e = launch_cfg<bf16, 128, 128, 128, 2, 4, false, false, true>(a, stream, &sp);
+      if (e != hipSuccess) return e;
+      return launch_seg_finish(a, sp, stream);
+    }
   }
   if (a.bf16) {
     if (a.dk == 128 && a.dv == 128) {

@@ -33,15 +33,15 @@ CSRC = os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc")
 
 # Source files of each family of kernels the bench measures.
 SOURCES = {
-    "prefill": ["prefill.hip", "scan.hip", "prefill_common.hpp", "device_common.hpp", "plan.cpp"],
-    "bwd": ["prefill.hip", "bwd.hip", "scan.hip", "prefill_common.hpp", "device_common.hpp", "plan.cpp"],
+    "prefill": ["prefill.hip", "seg.hip", "device_common.hpp"],
+    "bwd": ["prefill.hip", "bwd.hip", "device_common.hpp"],
     "decode": ["decode.hip"],
     "verify": ["verify.hip"],
     "epilogue": ["epilogue.hip"],
     "short_conv": ["conv.hip"],
 }
 # The kernel whose dispatches count the family's calls.
-MAIN = {"prefill": ("prefill", "scan"), "bwd": ("bwd_dlocal",), "decode": ("decode",), "verify": ("verify",),
+MAIN = {"prefill": ("prefill", "prefill_seg"), "bwd": ("bwd_dlocal",), "decode": ("decode",), "verify": ("verify",),
         "epilogue": ("epilogue",), "short_conv": ("short_conv",)}
 
 
@@ -64,12 +64,14 @@ def _find(d, suffix):
 
 def kind(name):
     """(family, kernel) of a dispatch, or None for kernels that are not measured."""
-    if "prefill_kernel" in name:  # the last template flag: the saving variant a backward pass runs
-        return ("bwd", "prefill_save") if name.endswith("Lb1EEEvNS0_6ParamsE") else ("prefill", "prefill")
-    for sub, fam, k in (("order_kernel", "prefill", "order"), ("chunk_base_kernel", "prefill", "chunk_base"),
-                        ("prep_kernel", "prefill", "prep"), ("scan_kernel", "prefill", "scan"),
+    if "prefill_kernel" in name:  # the two last template flags: the saving variant a backward pass
+        if name.endswith("Lb1ELb0EEEvNS0_6ParamsE"):  # runs, and the segmented variant of long rows
+            return ("bwd", "prefill_save")
+        return ("prefill", "prefill_seg" if name.endswith("Lb0ELb1EEEvNS0_6ParamsE") else "prefill")
+    for sub, fam, k in (("order_kernel", "prefill", "order"), ("seg_correct_kernel", "prefill", "seg_correct"),
+                        ("seg_scan_step_kernel", "prefill", "seg_scan"),
                         ("dstate_kernel", "bwd", "bwd_dstate"), ("dlocal_kernel", "bwd", "bwd_dlocal"),
-                        ("zero_kernel", "bwd", "bwd_zero"),
+                        ("chunk_prefix_kernel", "bwd", "bwd_prefix"), ("zero_kernel", "bwd", "bwd_zero"),
                         ("decode_kernel", "decode", "decode"), ("verify_kernel", "verify", "verify"),
                         ("norm_gate_kernel", "epilogue", "epilogue"), ("conv_kernel", "short_conv", "short_conv")):
         if sub in name:

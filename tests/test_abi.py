@@ -154,60 +154,45 @@ def test_decode_invalid(gdn):
 
 
 def test_workspace_size_is_zero_for_the_fused_prefill(gdn):
-    # many units fill the chip with the fused prefill; fp32, d = 64 and empty rows run fused too
-    assert gdn.fwd_chunked_workspace_size(dims(gdn, B=4, T=4096, N=4, Hqk=16, Hv=64)) == 0
-    assert gdn.fwd_chunked_workspace_size(dims(gdn, B=1, T=65536, N=1, Hqk=16, Hv=129)) == 0
+    assert gdn.fwd_chunked_workspace_size(dims(gdn)) == 0
+    # rows that fill the chip with their own units, short rows, fp32 and d = 64 run fused
+    assert gdn.fwd_chunked_workspace_size(dims(gdn, B=4, T=4096, N=4, Hqk=16, Hv=16)) == 0
+    assert gdn.fwd_chunked_workspace_size(dims(gdn, B=1, T=65536, N=1, Hqk=16, Hv=52)) == 0
+    assert gdn.fwd_chunked_workspace_size(dims(gdn, T=3071, Hv=1, Hqk=1)) == 0
     assert gdn.fwd_chunked_workspace_size(dims(gdn, T=8192, dk=64, dv=64, dtype=0)) == 0
     assert gdn.fwd_chunked_workspace_size(dims(gdn, T=8192, dk=64, dv=64)) == 0
-    assert gdn.fwd_chunked_workspace_size(dims(gdn, T=0)) == 0
 
 
 def test_packed_sequences_workspace(gdn):
-    # packed sequences (batch 1, N > 1) with many units: N int32 for their longest-first order, up to 4096
-    kw = dict(B=1, Hqk=16, Hv=128)
-    assert gdn.fwd_chunked_workspace_size(dims(gdn, T=1000, N=2, **kw)) == 256
-    assert gdn.fwd_chunked_workspace_size(dims(gdn, T=1000, N=64, **kw)) == 256
-    assert gdn.fwd_chunked_workspace_size(dims(gdn, T=1000, N=65, **kw)) == 512
-    assert gdn.fwd_chunked_workspace_size(dims(gdn, T=0, N=4096, **kw)) == 16384
-    assert gdn.fwd_chunked_workspace_size(dims(gdn, T=1000, N=4097, **kw)) == 0
+    # packed sequences (batch 1, N > 1): N int32 for their longest-first order, up to 4096 sequences
+    assert gdn.fwd_chunked_workspace_size(dims(gdn, B=1, T=1000, N=2)) == 256
+    assert gdn.fwd_chunked_workspace_size(dims(gdn, B=1, T=1000, N=64)) == 256
+    assert gdn.fwd_chunked_workspace_size(dims(gdn, B=1, T=1000, N=65)) == 512
+    assert gdn.fwd_chunked_workspace_size(dims(gdn, B=1, T=0, N=4096)) == 16384
+    assert gdn.fwd_chunked_workspace_size(dims(gdn, B=1, T=1000, N=4097)) == 0
     assert gdn.fwd_chunked_workspace_size(dims(gdn, B=1, T=1000, N=64, dk=64, dv=64, dtype=0)) == 256
-    d = dims(gdn, T=1000, N=64, **kw)
+    d = dims(gdn, B=1, T=1000, N=64)
     assert call_fwd(gdn, d, cu=FAKE, ws_bytes=255) == WORKSPACE_TOO_SMALL
 
 
-BLOCK = 13312  # per (chunk slot, value head): bf16 T and P fragments (6 KB each) and four gate vectors
-
-
-def two_pass_ws_bytes(B, T, N, Hv, packed):
-    """Two-pass prefill workspace: packed sequences first get their chunk offsets (N + 1 int32) and
-    longest-first order (N int32, 2 <= N <= 4096), each part padded to 256 bytes; then one block per
-    (chunk slot, value head), with B * ceil(T / 64) slots for batch rows and T // 64 + N for packed
-    sequences (every partial last chunk adds one)."""
+def seg_ws_bytes(B, T, Hv, nseg):
+    """Segmented prefill workspace: per-token bf16 vectors scale Phi_t^T q_t, then per segment and
+    value head the zero-start end state and the transition (fp32), the start state (bf16, for the
+    correction), and two fp32 states for the scan; each part padded to 256 bytes."""
     al = lambda x: (x + 255) // 256 * 256
-    if packed:
-        slots = T // 64 + N
-        head = al((N + 1) * 4) + (al(N * 4) if 2 <= N <= 4096 else 0)
-    else:
-        slots = B * ((T + 63) // 64)
-        head = 0
-    return head + slots * Hv * BLOCK
+    mat = 128 * 128
+    return (al(B * T * Hv * 128 * 2) + 2 * al(nseg * B * Hv * mat * 4) + al(nseg * B * Hv * mat * 2)
+            + 2 * al(B * Hv * mat * 4))
 
 
-def test_two_pass_prefill_workspace(gdn):
-    # few (sequence, value head) units in bf16 with dk = dv = 128: 4 x 4096 tokens x 16 heads, one
-    # 65536-token row with 32 value heads, up to 128 units, batch rows and packed sequences
-    assert gdn.fwd_chunked_workspace_size(dims(gdn, B=4, T=4096, N=4, Hqk=16, Hv=16)) == \
-        two_pass_ws_bytes(4, 4096, 4, 16, False)
+def test_segmented_prefill_workspace(gdn):
+    # B = 1, T = 65536, 32 value heads: four segments (7 runs per head fill 224 of 256 compute units)
     d = dims(gdn, B=1, T=65536, N=1, Hqk=16, Hv=32)
-    assert gdn.fwd_chunked_workspace_size(d) == two_pass_ws_bytes(1, 65536, 1, 32, False) == 1024 * 32 * BLOCK
-    assert gdn.fwd_chunked_workspace_size(dims(gdn, B=1, T=65536, N=1, Hqk=16, Hv=128)) == \
-        two_pass_ws_bytes(1, 65536, 1, 128, False)
-    assert gdn.fwd_chunked_workspace_size(dims(gdn, B=2, T=100, N=2, Hqk=1, Hv=2)) == \
-        two_pass_ws_bytes(2, 100, 2, 2, False)
-    assert gdn.fwd_chunked_workspace_size(dims(gdn, B=1, T=1000, N=10, Hqk=2, Hv=4)) == \
-        two_pass_ws_bytes(1, 1000, 10, 4, True)
-    assert gdn.fwd_chunked_workspace_size(dims(gdn, B=1, T=1000, N=1, Hqk=2, Hv=4)) == \
-        two_pass_ws_bytes(1, 1000, 1, 4, False)
+    assert gdn.fwd_chunked_workspace_size(d) == seg_ws_bytes(1, 65536, 32, 4)
+    # one head: at most T / 1024 segments, and none of them empty
+    assert gdn.fwd_chunked_workspace_size(dims(gdn, T=3072, Hv=1, Hqk=1)) == seg_ws_bytes(1, 3072, 1, 3)
+    assert gdn.fwd_chunked_workspace_size(dims(gdn, T=5000, Hv=1, Hqk=1)) == seg_ws_bytes(1, 5000, 1, 4)
+    assert gdn.fwd_chunked_workspace_size(dims(gdn, B=1, T=65536, N=1, Hqk=1, Hv=51)) == seg_ws_bytes(1, 65536, 51, 3)
     need = gdn.fwd_chunked_workspace_size(d)
     assert call_fwd(gdn, d, ws_bytes=need - 1) == WORKSPACE_TOO_SMALL
     assert call_fwd(gdn, d, ws=FAKE + 128, ws_bytes=need) == MISALIGNED
@@ -216,8 +201,7 @@ def test_two_pass_prefill_workspace(gdn):
 def test_needed_workspace_must_be_given(gdn):
     """A declared size is not a buffer: with a workspace needed, a NULL one is rejected, whatever
     workspace_bytes says (no silent path without it)."""
-    for d, cu in ((dims(gdn, B=1, T=65536, N=1, Hqk=16, Hv=32), 0), (dims(gdn, B=1, T=1000, N=64, Hqk=16, Hv=128), FAKE),
-                  (dims(gdn, B=1, T=1000, N=8, Hqk=2, Hv=4), FAKE)):
+    for d, cu in ((dims(gdn, B=1, T=65536, N=1, Hqk=16, Hv=32), 0), (dims(gdn, B=1, T=1000, N=64), FAKE)):
         need = gdn.fwd_chunked_workspace_size(d)
         assert need > 0
         assert call_fwd(gdn, d, cu=cu, ws=0, ws_bytes=need) == INVALID
