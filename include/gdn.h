@@ -23,7 +23,8 @@
  *    accumulators to nearest even.  All tensors are dense, row-major and contiguous.
  *  - Every pointer except `d` is a DEVICE pointer owned by the caller.  The library
  *    allocates no device memory, keeps no mutable global state and may be called
- *    concurrently from several host threads on different streams.
+ *    concurrently from several host threads on different streams (except
+ *    gdn_fwd_chunked_noalloc, whose static array is shared: see there).
  *  - Work is enqueued asynchronously on `stream` (0 = the null stream); buffers must
  *    stay alive until the stream has passed the work.
  *  - Errors: every call returns a status and never throws, aborts or prints.  All
@@ -121,6 +122,29 @@ gdn_status_t gdn_fwd_chunked(const gdn_dims_t* d, const void* q, const void* k, 
                              const float* g, const float* beta, const float* initial_state,
                              const int32_t* cu_seqlens, void* o, float* final_state,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * gdn_fwd_chunked for callers that cannot allocate: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments, layouts
+ * and results as gdn_fwd_chunked, without the workspace; it calls no hipMalloc,
+ * hipFree or allocating library routine.
+ *   - Packed sequences get their longest-first order in a 16 KiB static device
+ *     array of the library (one copy per GPU, held until the process ends), so
+ *     cu_seqlens may describe at most 4096 sequences: more return
+ *     GDN_STATUS_WORKSPACE_TOO_SMALL before any HIP call.
+ *   - Rows that gdn_fwd_chunked would cut into segments (bf16, dk = dv = 128,
+ *     B * Hv <= 51, T >= 3072) run in one pass of the fused kernel instead: the
+ *     same recurrence, different rounding order, slower on such rows.
+ *   - Calls that overlap on one GPU (other streams, other threads) share the
+ *     static array and race: serialise them.
+ *   - The first call on a device looks up that device's copy of the array with
+ *     the calling thread's current device, which must be the device of stream
+ *     and of the buffers.
+ */
+gdn_status_t gdn_fwd_chunked_noalloc(const gdn_dims_t* d, const void* q, const void* k, const void* v,
+                                     const float* g, const float* beta, const float* initial_state,
+                                     const int32_t* cu_seqlens, void* o, float* final_state,
+                                     hipStream_t stream);
 
 /*
  * Single-token recurrent decode step for N independent sequences, updating the

@@ -46,9 +46,15 @@ size_t gdn_fwd_chunked_workspace_size(const gdn_dims_t* d) {
   return gdn::seg_workspace_bytes(d->batch, d->seqlen, d->num_v_heads);
 }
 
-gdn_status_t gdn_fwd_chunked(const gdn_dims_t* d, const void* q, const void* k, const void* v, const float* g,
-                             const float* beta, const float* initial_state, const int32_t* cu_seqlens, void* o,
-                             float* final_state, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of a prefill call shared by gdn_fwd_chunked and gdn_fwd_chunked_noalloc (everything but the
+// workspace), then its launcher arguments.
+gdn_status_t check_fwd(const gdn_dims_t* d, const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, const float* initial_state, const int32_t* cu_seqlens, const void* o,
+                       const float* final_state) {
   gdn_status_t st = check_common(d);
   if (st != GDN_STATUS_SUCCESS) return st;
   if (d->batch < 0 || d->seqlen < 0) return GDN_STATUS_INVALID_VALUE;
@@ -63,16 +69,16 @@ gdn_status_t gdn_fwd_chunked(const gdn_dims_t* d, const void* q, const void* k, 
   const bool has_tokens = static_cast<int64_t>(d->batch) * d->seqlen > 0;
   if (has_tokens && (!q || !k || !v || !g || !beta || !o)) return GDN_STATUS_INVALID_VALUE;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(g, 4) ||
-      !aligned(beta, 4) || !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(cu_seqlens, 4) ||
-      !aligned(workspace, 256))
+      !aligned(beta, 4) || !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(cu_seqlens, 4))
     return GDN_STATUS_MISALIGNED;
-  const size_t need = gdn_fwd_chunked_workspace_size(d);
-  if (workspace_bytes < need) return GDN_STATUS_WORKSPACE_TOO_SMALL;
-  if (need > 0 && !workspace) return GDN_STATUS_INVALID_VALUE;
-  if (d->num_seqs == 0) return GDN_STATUS_SUCCESS;
   // Token indices are 32-bit inside the kernels.
   if (static_cast<int64_t>(d->batch) * d->seqlen >= (int64_t(1) << 31)) return GDN_STATUS_NOT_SUPPORTED;
+  return GDN_STATUS_SUCCESS;
+}
 
+gdn::PrefillArgs fwd_args(const gdn_dims_t* d, const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, const float* initial_state, const int32_t* cu_seqlens, void* o,
+                          float* final_state) {
   gdn::PrefillArgs a;
   a.q = q;
   a.k = k;
@@ -95,9 +101,39 @@ gdn_status_t gdn_fwd_chunked(const gdn_dims_t* d, const void* q, const void* k, 
   a.chunk = d->chunk_size;
   a.scale = d->scale;
   a.bf16 = d->dtype == GDN_DTYPE_BFLOAT16;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status_t gdn_fwd_chunked(const gdn_dims_t* d, const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, const float* initial_state, const int32_t* cu_seqlens, void* o,
+                             float* final_state, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  gdn_status_t st = check_fwd(d, q, k, v, g, beta, initial_state, cu_seqlens, o, final_state);
+  if (st != GDN_STATUS_SUCCESS) return st;
+  if (!aligned(workspace, 256)) return GDN_STATUS_MISALIGNED;
+  const size_t need = gdn_fwd_chunked_workspace_size(d);
+  if (workspace_bytes < need) return GDN_STATUS_WORKSPACE_TOO_SMALL;
+  if (need > 0 && !workspace) return GDN_STATUS_INVALID_VALUE;
+  if (d->num_seqs == 0) return GDN_STATUS_SUCCESS;
+  gdn::PrefillArgs a = fwd_args(d, q, k, v, g, beta, initial_state, cu_seqlens, o, final_state);
   a.workspace = workspace;
   a.workspace_bytes = workspace_bytes;
   return from_hip(gdn::launch_prefill(a, stream));
+}
+
+gdn_status_t gdn_fwd_chunked_noalloc(const gdn_dims_t* d, const void* q, const void* k, const void* v,
+                                     const float* g, const float* beta, const float* initial_state,
+                                     const int32_t* cu_seqlens, void* o, float* final_state, hipStream_t stream) {
+  gdn_status_t st = check_fwd(d, q, k, v, g, beta, initial_state, cu_seqlens, o, final_state);
+  if (st != GDN_STATUS_SUCCESS) return st;
+  // The static scratch holds the order of at most kMaxOrderedSeqs packed sequences.
+  if (cu_seqlens && d->num_seqs > gdn::kMaxOrderedSeqs) return GDN_STATUS_WORKSPACE_TOO_SMALL;
+  if (d->num_seqs == 0) return GDN_STATUS_SUCCESS;
+  return from_hip(
+      gdn::launch_prefill_noalloc(fwd_args(d, q, k, v, g, beta, initial_state, cu_seqlens, o, final_state), stream));
 }
 
 gdn_status_t gdn_decode_step(const gdn_dims_t* d, const void* q, const void* k, const void* v, const float* g,

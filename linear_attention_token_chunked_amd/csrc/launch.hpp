@@ -45,7 +45,8 @@ struct PrefillArgs {
 };
 
 // Workspace bytes for the longest-first order of num_seqs packed sequences
-// (0 where the natural order is kept).
+// (0 where the natural order is kept: fewer than 2 or more than kMaxOrderedSeqs).
+constexpr int kMaxOrderedSeqs = 4096;
 size_t order_workspace_bytes(int num_seqs);
 
 // Segmented prefill of a few long batch rows (bf16, dk = dv = 128, no cu_seqlens):
@@ -126,5 +127,8 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t stream);
 hipError_t launch_norm_gate(const EpilogueArgs& a, hipStream_t stream);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// The prefill without a caller's workspace: the fused kernel for every unit count, and for packed
+// sequences (at most kMaxOrderedSeqs) the longest-first order in a static device array of the library.
+hipError_t launch_prefill_noalloc(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace gdn

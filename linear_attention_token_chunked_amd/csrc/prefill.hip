@@ -37,6 +37,7 @@
 // other (the fp32 stage does not fit twice in LDS).  Accumulators feed the next
 // product straight from registers (see device_common.hpp).  Decay factors are
 // exp2 of log2(e)-scaled prefix sums; exp(G_i - G_j) is formed only for i >= j.
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -1166,7 +1167,7 @@ int slice_config(int units, int dv) {
 // lengths as uneven as a lognormal mix, that tail was a quarter of the time).
 // Rank of sequence i = the number of sequences longer than it, or as long and
 // before it: one thread per sequence, all lengths staged through LDS in turn.
-constexpr int kMaxOrdered = 4096;  // beyond this many sequences the natural order is kept
+constexpr int kMaxOrdered = kMaxOrderedSeqs;  // beyond this many sequences the natural order is kept
 
 __global__ __launch_bounds__(256) void order_kernel(const int32_t* cu, int N, int32_t* order) {
   __shared__ int len[256];
@@ -1188,6 +1189,56 @@ __global__ __launch_bounds__(256) void order_kernel(const int32_t* cu, int N, in
 }
 }  // namespace
 
+// Scratch of the allocation-free prefill (launch_prefill_noalloc): the longest-first order of up to
+// kMaxOrdered packed sequences, 16 KiB.  Every GPU the library runs on holds its own copy until the
+// process ends.  In host code the name stands for a host-side handle, not a device address: host code
+// uses only the per-device address hipGetSymbolAddress returns (noalloc_scratch below).
+static __device__ __align__(256) int32_t scratch[kMaxOrdered];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int32_t*> g_scratch[kMaxDevices];  // the address of scratch on each device, looked up once
+
+// The current device's copy of scratch.  Two threads that both find it missing look up the same
+// address and store the same value.
+hipError_t noalloc_scratch(int32_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  int32_t* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    void* sym = nullptr;
+    e = hipGetSymbolAddress(&sym, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptr = static_cast<int32_t*>(sym);
+    g_scratch[dev].store(ptr, std::memory_order_release);
+  }
+  *out = ptr;
+  return hipSuccess;
+}
+
+// The fused kernel in the configuration the unit count selects (no workspace).
+hipError_t launch_fused(const PrefillArgs& a, hipStream_t stream) {
+  const int units = a.num_seqs * a.Hv;
+  if (a.bf16) {
+    if (a.dk == 128 && a.dv == 128) {
+      switch (slice_config(units, 128)) {
+        case 128: return launch<bf16, 128, 128, 128, 2, 4, false>(a, stream);
+        case 64: return launch<bf16, 128, 128, 64, 2, 4, false>(a, stream);
+        default: return launch<bf16, 128, 128, 32, 2, 2, true>(a, stream);
+      }
+    }
+    if (a.dk == 64 && a.dv == 64)
+      return slice_config(units, 64) == 64 ? launch<bf16, 64, 64, 64, 2, 4, false>(a, stream)
+                                           : launch<bf16, 64, 64, 32, 2, 2, true>(a, stream);
+  } else {
+    if (a.dk == 64 && a.dv == 64) return launch<float, 64, 64, 64, 1, 4, false>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+}  // namespace
+
 size_t order_workspace_bytes(int num_seqs) {
   return num_seqs >= 2 && num_seqs <= kMaxOrdered ? (static_cast<size_t>(num_seqs) * 4 + 255) / 256 * 256 : 0;
 }
@@ -1195,7 +1246,6 @@ size_t order_workspace_bytes(int num_seqs) {
 hipError_t launch_prefill(const PrefillArgs& args, hipStream_t stream) {
   if (args.chunk != C) return hipErrorInvalidValue;
   PrefillArgs a = args;
-  const int units = a.num_seqs * a.Hv;
   if (a.cu_seqlens && !a.save_state && a.workspace && order_workspace_bytes(a.num_seqs) &&
       a.workspace_bytes >= order_workspace_bytes(a.num_seqs)) {
     int32_t* order = static_cast<int32_t*>(a.workspace);
@@ -1215,21 +1265,24 @@ hipError_t launch_prefill(const PrefillArgs& args, hipStream_t stream) {
       return launch_seg_finish(a, sp, stream);
     }
   }
-  if (a.bf16) {
-    if (a.dk == 128 && a.dv == 128) {
-      switch (slice_config(units, 128)) {
-        case 128: return launch<bf16, 128, 128, 128, 2, 4, false>(a, stream);
-        case 64: return launch<bf16, 128, 128, 64, 2, 4, false>(a, stream);
-        default: return launch<bf16, 128, 128, 32, 2, 2, true>(a, stream);
-      }
-    }
-    if (a.dk == 64 && a.dv == 64)
-      return slice_config(units, 64) == 64 ? launch<bf16, 64, 64, 64, 2, 4, false>(a, stream)
-                                           : launch<bf16, 64, 64, 32, 2, 2, true>(a, stream);
-  } else {
-    if (a.dk == 64 && a.dv == 64) return launch<float, 64, 64, 64, 1, 4, false>(a, stream);
+  return launch_fused(a, stream);
+}
+
+hipError_t launch_prefill_noalloc(const PrefillArgs& args, hipStream_t stream) {
+  if (args.chunk != C || args.save_state || args.num_seqs > kMaxOrdered) return hipErrorInvalidValue;
+  PrefillArgs a = args;
+  a.workspace = nullptr;
+  a.workspace_bytes = 0;
+  if (a.cu_seqlens && order_workspace_bytes(a.num_seqs)) {
+    int32_t* order = nullptr;
+    hipError_t e = noalloc_scratch(&order);
+    if (e != hipSuccess) return e;
+    order_kernel<<<dim3((a.num_seqs + 255) / 256), dim3(256), 0, stream>>>(a.cu_seqlens, a.num_seqs, order);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.order = order;
   }
-  return hipErrorInvalidValue;
+  return launch_fused(a, stream);
 }
 
 }  // namespace gdn

@@ -38,7 +38,8 @@ class Dims(ctypes.Structure):
 
 DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1}
 
-EXPORTED = ("gdn_fwd_chunked_workspace_size", "gdn_fwd_chunked", "gdn_decode_step", "gdn_decode_verify",
+EXPORTED = ("gdn_fwd_chunked_workspace_size", "gdn_fwd_chunked", "gdn_fwd_chunked_noalloc", "gdn_decode_step",
+            "gdn_decode_verify",
             "gdn_output_norm_gate", "gdn_short_conv", "gdn_bwd_chunked_workspace_size", "gdn_bwd_chunked",
             "gdn_status_string")
 
@@ -53,6 +54,8 @@ def _load():
     lib.gdn_fwd_chunked_workspace_size.restype = sz
     lib.gdn_fwd_chunked.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, fp, fp, fp, vp, vp, fp, vp, sz, vp]
     lib.gdn_fwd_chunked.restype = ctypes.c_int
+    lib.gdn_fwd_chunked_noalloc.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, fp, fp, fp, vp, vp, fp, vp]
+    lib.gdn_fwd_chunked_noalloc.restype = ctypes.c_int
     lib.gdn_decode_step.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, fp, fp, fp, vp, vp]
     lib.gdn_decode_step.restype = ctypes.c_int
     lib.gdn_decode_verify.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, fp, fp, fp, fp, fp, vp, vp]
@@ -173,6 +176,49 @@ def fwd_chunked(q, k, v, g, beta, *, initial_state=None, cu_seqlens=None, chunk_
         code = lib.gdn_fwd_chunked(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                    _ptr(initial_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state), _ptr(ws),
                                    ctypes.c_size_t(ws_bytes), _stream(dev))
+    _check(code)
+    return out, final_state
+
+
+def fwd_chunked_noalloc(q, k, v, g, beta, *, initial_state=None, cu_seqlens=None, chunk_size=64, scale=1.0,
+                        out, final_state=None):
+    """fwd_chunked through gdn_fwd_chunked_noalloc: nothing is allocated, by the library or here.
+    ``out`` [B, T, Hv, dv] is required; ``final_state`` [N, Hv, dk, dv] fp32 is written when given.
+    Returns (out, final_state)."""
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU")
+    if q.dtype not in DTYPE_CODE:
+        raise TypeError("q, k, v must be float32 or bfloat16")
+    _need(q, "q", q.dtype, dev, 4)
+    B, T, Hqk, dk = q.shape
+    _need(k, "k", q.dtype, dev, 4)
+    _need(v, "v", q.dtype, dev, 4)
+    Hv, dv = v.shape[2], v.shape[3]
+    if k.shape != q.shape or v.shape[:2] != (B, T):
+        raise ValueError("q, k, v shapes disagree")
+    _need(g, "g", torch.float32, dev, 3)
+    _need(beta, "beta", torch.float32, dev, 3)
+    if g.shape != (B, T, Hv) or beta.shape != (B, T, Hv):
+        raise ValueError("g and beta must be [B, T, Hv]")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev, 1)
+        N = cu_seqlens.shape[0] - 1
+    else:
+        N = B
+    for name, st in (("initial_state", initial_state), ("final_state", final_state)):
+        if st is not None:
+            _need(st, name, torch.float32, dev, 4)
+            if st.shape != (N, Hv, dk, dv):
+                raise ValueError(f"{name} must be [N, Hv, dk, dv]")
+    _need(out, "out", q.dtype, dev, 4)
+    if out.shape != (B, T, Hv, dv):
+        raise ValueError("out must be [B, T, Hv, dv]")
+    dims = make_dims(B, T, N, Hqk, Hv, dk, dv, chunk_size, scale, q.dtype)
+    with torch.cuda.device(dev):
+        code = lib.gdn_fwd_chunked_noalloc(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                           _ptr(initial_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state),
+                                           _stream(dev))
     _check(code)
     return out, final_state
 

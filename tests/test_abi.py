@@ -20,11 +20,11 @@ def declared_functions():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gdn_\w+)\s*\(", text, flags=re.M)))
 
 
-def test_header_declares_the_nine_entry_points():
+def test_header_declares_the_ten_entry_points():
     assert declared_functions() == sorted(
         ["gdn_bwd_chunked", "gdn_bwd_chunked_workspace_size", "gdn_decode_step", "gdn_decode_verify",
-         "gdn_fwd_chunked", "gdn_fwd_chunked_workspace_size", "gdn_output_norm_gate", "gdn_short_conv",
-         "gdn_status_string"])
+         "gdn_fwd_chunked", "gdn_fwd_chunked_noalloc", "gdn_fwd_chunked_workspace_size", "gdn_output_norm_gate",
+         "gdn_short_conv", "gdn_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -60,6 +60,24 @@ def call_fwd(gdn, d, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=0, cu=0, o=FA
     P = ctypes.c_void_p
     return gdn.lib.gdn_fwd_chunked(ctypes.byref(d), P(q), P(k), P(v), P(g), P(beta), P(h0), P(cu), P(o), P(hT), P(ws),
                                    ctypes.c_size_t(ws_bytes), P(0))
+
+
+def call_noalloc(gdn, d, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, h0=0, cu=0, o=FAKE, hT=0):
+    P = ctypes.c_void_p
+    return gdn.lib.gdn_fwd_chunked_noalloc(ctypes.byref(d), P(q), P(k), P(v), P(g), P(beta), P(h0), P(cu), P(o),
+                                           P(hT), P(0))
+
+
+def test_noalloc_validates_like_the_workspace_entry_point(gdn):
+    """Invalid calls are rejected before any HIP call, with the statuses of gdn_fwd_chunked; the static
+    scratch orders at most 4096 packed sequences, and more are rejected as too large for it."""
+    assert call_noalloc(gdn, dims(gdn, Hv=3)) == INVALID
+    assert call_noalloc(gdn, dims(gdn, chunk_size=32)) == NOT_SUPPORTED
+    assert call_noalloc(gdn, dims(gdn), q=0) == INVALID
+    assert call_noalloc(gdn, dims(gdn), q=FAKE + 8) == MISALIGNED
+    assert call_noalloc(gdn, dims(gdn, B=2, N=2), cu=FAKE) == INVALID
+    assert call_noalloc(gdn, dims(gdn, B=1, T=9000, N=4097, Hqk=1, Hv=1), cu=FAKE) == WORKSPACE_TOO_SMALL
+    assert call_noalloc(gdn, dims(gdn, B=0, N=0)) == 0
 
 
 def call_dec(gdn, d, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, state=FAKE, o=FAKE):
