@@ -57,7 +57,8 @@ typedef enum { GDN_DTYPE_FLOAT32 = 0, GDN_DTYPE_BFLOAT16 = 1 } gdn_dtype_t;
 
 typedef struct {
   int32_t batch;        /* B: batch rows of q/k/v/o; must be 1 when cu_seqlens is given   */
-  int32_t seqlen;       /* T: tokens per row (total packed tokens with cu_seqlens); >= 0  */
+  int32_t seqlen;       /* T: tokens per row (total packed tokens with cu_seqlens); >= 0; */
+                        /* B * T >= 2^31 - 256 returns NOT_SUPPORTED (32-bit indices)     */
   int32_t num_seqs;     /* N: number of sequences = B, or len(cu_seqlens) - 1             */
   int32_t num_qk_heads; /* Hqk >= 1                                                       */
   int32_t num_v_heads;  /* Hv >= 1, a multiple of Hqk; NOT_SUPPORTED above 4096          */

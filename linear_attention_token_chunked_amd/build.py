@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 
-SOURCES = ["gdn_api.cpp", "decode.hip", "verify.hip", "epilogue.hip", "conv.hip", "bwd.hip", "seg.hip", "prefill.hip"]
+SOURCES = ["gdn_api.cpp", "plan.cpp", "decode.hip", "verify.hip", "epilogue.hip", "conv.hip", "bwd.hip", "seg.hip",
+           "prefill.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are switched off for every device compile: the kernels rely on plain

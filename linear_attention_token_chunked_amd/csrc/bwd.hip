@@ -740,29 +740,13 @@ __global__ __launch_bounds__(1024) void chunk_prefix_kernel(const int32_t* cu, i
   }
 }
 
-struct WsParts {
-  size_t cpre, state, dm, u, dz, total;
-};
-WsParts ws_parts(int64_t tokens, int N, int Hv, int dk, int dv, int esize) {
-  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-  const size_t chunks = static_cast<size_t>(tokens / C + N);
-  WsParts w;
-  w.cpre = 0;
-  w.state = al(static_cast<size_t>(N + 1) * 4);
-  w.dm = w.state + al(chunks * Hv * dk * dv * esize);
-  w.u = w.dm + al(chunks * Hv * dk * dv * esize);
-  w.dz = w.u + al(static_cast<size_t>(tokens) * Hv * dv * esize);
-  w.total = w.dz + al(static_cast<size_t>(tokens) * Hv * dv * esize);
-  return w;
-}
-
 template <class T, int DK, int DV, int BV>
 hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   using LS = DsLayout<T, DK, BV>;
   using LL = DlLayout<T, DK, DV>;
   static_assert(LS::bytes <= 160 * 1024 && LL::bytes <= 160 * 1024, "LDS budget of one gfx950 compute unit");
   const int64_t tokens = static_cast<int64_t>(a.batch) * a.seqlen;
-  const WsParts w = ws_parts(tokens, a.num_seqs, a.Hv, DK, DV, sizeof(T));
+  const BwdParts w = bwd_parts(tokens, a.num_seqs, a.Hv, DK, DV, sizeof(T) == 2);
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);  // 256-byte aligned
   int32_t* cpre = a.cu_seqlens ? reinterpret_cast<int32_t*>(ws + w.cpre) : nullptr;
   if (cpre) chunk_prefix_kernel<<<dim3(1), dim3(1024), 0, stream>>>(a.cu_seqlens, a.num_seqs, cpre);
@@ -839,10 +823,6 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
-
-size_t bwd_workspace_bytes(int64_t tokens, int num_seqs, int Hv, int dk, int dv, bool bf16) {
-  return ws_parts(tokens, num_seqs, Hv, dk, dv, bf16 ? 2 : 4).total;
-}
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   if (a.bf16) {

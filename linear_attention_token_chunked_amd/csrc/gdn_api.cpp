@@ -4,6 +4,7 @@
 #include "gdn.h"
 
 #include <stdint.h>
+#include <string.h>
 
 #include "launch.hpp"
 
@@ -13,13 +14,27 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
 
+// Token indices are 32-bit inside the kernels, which also form a sequence's end plus a chunk length.
+constexpr int64_t kMaxTokens = (int64_t(1) << 31) - 256;
+
+// A dtype as the integer the caller stored: a C caller may store any int in a gdn_dtype_t, and reading
+// an out-of-range value through the enum type would be undefined in C++.
+static_assert(sizeof(gdn_dtype_t) == sizeof(int), "gdn_dtype_t is an int-sized C enum");
+int raw_dtype(const gdn_dtype_t& t) {
+  int v;
+  memcpy(&v, &t, sizeof v);
+  return v;
+}
+bool dtype_ok(const gdn_dtype_t& t) { return raw_dtype(t) == GDN_DTYPE_FLOAT32 || raw_dtype(t) == GDN_DTYPE_BFLOAT16; }
+bool is_bf16(const gdn_dtype_t& t) { return raw_dtype(t) == GDN_DTYPE_BFLOAT16; }
+
 // Checks shared by every entry point.
 gdn_status_t check_common(const gdn_dims_t* d) {
   if (!d) return GDN_STATUS_INVALID_VALUE;
   if (d->num_qk_heads < 1 || d->num_v_heads < 1 || d->head_dim_k < 1 || d->head_dim_v < 1 || d->num_seqs < 0)
     return GDN_STATUS_INVALID_VALUE;
   if (d->num_v_heads % d->num_qk_heads != 0) return GDN_STATUS_INVALID_VALUE;
-  if (d->dtype != GDN_DTYPE_FLOAT32 && d->dtype != GDN_DTYPE_BFLOAT16) return GDN_STATUS_INVALID_VALUE;
+  if (!dtype_ok(d->dtype)) return GDN_STATUS_INVALID_VALUE;
   if (!head_dim_ok(d->head_dim_k) || !head_dim_ok(d->head_dim_v)) return GDN_STATUS_NOT_SUPPORTED;
   // The kernels address one token row of q, k, v with 32-bit byte offsets.
   if (d->num_v_heads > 4096) return GDN_STATUS_NOT_SUPPORTED;
@@ -41,7 +56,7 @@ size_t gdn_fwd_chunked_workspace_size(const gdn_dims_t* d) {
   if (!d || d->batch < 1 || d->seqlen < 0 || d->num_v_heads < 1 || d->chunk_size != 64) return 0;
   if (d->num_seqs != d->batch) return d->batch == 1 ? gdn::order_workspace_bytes(d->num_seqs) : 0;
   if (d->seqlen < 1) return 0;
-  if (d->dtype != GDN_DTYPE_BFLOAT16 || d->head_dim_k != 128 || d->head_dim_v != 128 || d->chunk_size != 64)
+  if (!is_bf16(d->dtype) || d->head_dim_k != 128 || d->head_dim_v != 128 || d->chunk_size != 64)
     return 0;
   return gdn::seg_workspace_bytes(d->batch, d->seqlen, d->num_v_heads);
 }
@@ -65,14 +80,13 @@ gdn_status_t check_fwd(const gdn_dims_t* d, const void* q, const void* k, const 
   }
   if (d->chunk_size != 64) return GDN_STATUS_NOT_SUPPORTED;
   if (d->head_dim_k != d->head_dim_v) return GDN_STATUS_NOT_SUPPORTED;
-  if (d->dtype == GDN_DTYPE_FLOAT32 && d->head_dim_k != 64) return GDN_STATUS_NOT_SUPPORTED;
+  if (!is_bf16(d->dtype) && d->head_dim_k != 64) return GDN_STATUS_NOT_SUPPORTED;
   const bool has_tokens = static_cast<int64_t>(d->batch) * d->seqlen > 0;
   if (has_tokens && (!q || !k || !v || !g || !beta || !o)) return GDN_STATUS_INVALID_VALUE;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(g, 4) ||
       !aligned(beta, 4) || !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(cu_seqlens, 4))
     return GDN_STATUS_MISALIGNED;
-  // Token indices are 32-bit inside the kernels.
-  if (static_cast<int64_t>(d->batch) * d->seqlen >= (int64_t(1) << 31)) return GDN_STATUS_NOT_SUPPORTED;
+  if (static_cast<int64_t>(d->batch) * d->seqlen >= kMaxTokens) return GDN_STATUS_NOT_SUPPORTED;
   return GDN_STATUS_SUCCESS;
 }
 
@@ -100,7 +114,7 @@ gdn::PrefillArgs fwd_args(const gdn_dims_t* d, const void* q, const void* k, con
   a.dv = d->head_dim_v;
   a.chunk = d->chunk_size;
   a.scale = d->scale;
-  a.bf16 = d->dtype == GDN_DTYPE_BFLOAT16;
+  a.bf16 = is_bf16(d->dtype);
   return a;
 }
 
@@ -162,7 +176,7 @@ gdn_status_t gdn_decode_step(const gdn_dims_t* d, const void* q, const void* k, 
   a.dk = d->head_dim_k;
   a.dv = d->head_dim_v;
   a.scale = d->scale;
-  a.bf16 = d->dtype == GDN_DTYPE_BFLOAT16;
+  a.bf16 = is_bf16(d->dtype);
   return from_hip(gdn::launch_decode(a, stream));
 }
 
@@ -197,14 +211,14 @@ gdn_status_t gdn_decode_verify(const gdn_dims_t* d, const void* q, const void* k
   a.dk = d->head_dim_k;
   a.dv = d->head_dim_v;
   a.scale = d->scale;
-  a.bf16 = d->dtype == GDN_DTYPE_BFLOAT16;
+  a.bf16 = is_bf16(d->dtype);
   return from_hip(gdn::launch_verify(a, stream));
 }
 
 gdn_status_t gdn_output_norm_gate(int64_t rows, int32_t dv, float eps, gdn_dtype_t dtype, const void* o,
                                   const void* z, const float* weight, void* y, hipStream_t stream) {
   if (rows < 0 || dv < 1 || !(eps >= 0.f)) return GDN_STATUS_INVALID_VALUE;
-  if (dtype != GDN_DTYPE_FLOAT32 && dtype != GDN_DTYPE_BFLOAT16) return GDN_STATUS_INVALID_VALUE;
+  if (!dtype_ok(dtype)) return GDN_STATUS_INVALID_VALUE;
   if (dv != 64 && dv != 128) return GDN_STATUS_NOT_SUPPORTED;
   if (rows == 0) return GDN_STATUS_SUCCESS;
   if (!o || !z || !weight || !y) return GDN_STATUS_INVALID_VALUE;
@@ -219,7 +233,7 @@ gdn_status_t gdn_output_norm_gate(int64_t rows, int32_t dv, float eps, gdn_dtype
   a.rows = rows;
   a.dv = dv;
   a.eps = eps;
-  a.bf16 = dtype == GDN_DTYPE_BFLOAT16;
+  a.bf16 = is_bf16(dtype);
   return from_hip(gdn::launch_norm_gate(a, stream));
 }
 
@@ -228,7 +242,7 @@ gdn_status_t gdn_short_conv(int32_t batch, int32_t seqlen, int32_t num_seqs, con
                             const void* x, const float* weight, void* y, hipStream_t stream) {
   if (batch < 0 || seqlen < 0 || num_seqs < 0 || heads < 1 || head_dim < 1 || !(eps >= 0.f))
     return GDN_STATUS_INVALID_VALUE;
-  if (dtype != GDN_DTYPE_FLOAT32 && dtype != GDN_DTYPE_BFLOAT16) return GDN_STATUS_INVALID_VALUE;
+  if (!dtype_ok(dtype)) return GDN_STATUS_INVALID_VALUE;
   if (cu_seqlens) {
     if (batch != 1) return GDN_STATUS_INVALID_VALUE;
   } else if (num_seqs != batch) {
@@ -241,7 +255,7 @@ gdn_status_t gdn_short_conv(int32_t batch, int32_t seqlen, int32_t num_seqs, con
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(weight, 16) || !aligned(cu_seqlens, 4))
     return GDN_STATUS_MISALIGNED;
   // tokens, and runs of 8 tokens times heads, are 32-bit indices in the kernel
-  if (tokens >= (int64_t(1) << 31) || (tokens + 7) / 8 * heads >= (int64_t(1) << 31) - 64)
+  if (tokens >= kMaxTokens || (tokens + 7) / 8 * heads >= (int64_t(1) << 31) - 64)
     return GDN_STATUS_NOT_SUPPORTED;
   gdn::ConvArgs a;
   a.x = x;
@@ -255,16 +269,17 @@ gdn_status_t gdn_short_conv(int32_t batch, int32_t seqlen, int32_t num_seqs, con
   a.head_dim = head_dim;
   a.l2norm = l2norm != 0;
   a.eps = eps;
-  a.bf16 = dtype == GDN_DTYPE_BFLOAT16;
+  a.bf16 = is_bf16(dtype);
   return from_hip(gdn::launch_conv(a, stream));
 }
 
 size_t gdn_bwd_chunked_workspace_size(const gdn_dims_t* d) {
   if (!d || d->batch < 0 || d->seqlen < 0 || d->num_seqs < 0 || d->num_v_heads < 1 || d->head_dim_k < 1 ||
-      d->head_dim_v < 1)
+      d->head_dim_v < 1 || static_cast<int64_t>(d->batch) * d->seqlen >= kMaxTokens)
     return 0;
-  return gdn::bwd_workspace_bytes(static_cast<int64_t>(d->batch) * d->seqlen, d->num_seqs, d->num_v_heads,
-                                  d->head_dim_k, d->head_dim_v, d->dtype == GDN_DTYPE_BFLOAT16);
+  return gdn::bwd_parts(static_cast<int64_t>(d->batch) * d->seqlen, d->num_seqs, d->num_v_heads, d->head_dim_k,
+                        d->head_dim_v, is_bf16(d->dtype))
+      .total;
 }
 
 gdn_status_t gdn_bwd_chunked(const gdn_dims_t* d, const void* q, const void* k, const void* v, const float* g,
@@ -282,7 +297,7 @@ gdn_status_t gdn_bwd_chunked(const gdn_dims_t* d, const void* q, const void* k, 
   }
   if (d->chunk_size != 64) return GDN_STATUS_NOT_SUPPORTED;
   if (d->head_dim_k != d->head_dim_v) return GDN_STATUS_NOT_SUPPORTED;
-  if (d->dtype == GDN_DTYPE_FLOAT32 && d->head_dim_k != 64) return GDN_STATUS_NOT_SUPPORTED;
+  if (!is_bf16(d->dtype) && d->head_dim_k != 64) return GDN_STATUS_NOT_SUPPORTED;
   const bool has_tokens = static_cast<int64_t>(d->batch) * d->seqlen > 0;
   if (has_tokens && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
     return GDN_STATUS_INVALID_VALUE;
@@ -296,7 +311,7 @@ gdn_status_t gdn_bwd_chunked(const gdn_dims_t* d, const void* q, const void* k, 
   if (workspace_bytes < need) return GDN_STATUS_WORKSPACE_TOO_SMALL;
   if (need > 0 && !workspace) return GDN_STATUS_INVALID_VALUE;
   // Token indices are 32-bit inside the kernels, and so is the grid of up to 16 workgroups per unit.
-  if (static_cast<int64_t>(d->batch) * d->seqlen >= (int64_t(1) << 31) ||
+  if (static_cast<int64_t>(d->batch) * d->seqlen >= kMaxTokens ||
       static_cast<int64_t>(d->num_seqs) * d->num_v_heads * 16 >= (int64_t(1) << 31))
     return GDN_STATUS_NOT_SUPPORTED;
 
@@ -325,7 +340,7 @@ gdn_status_t gdn_bwd_chunked(const gdn_dims_t* d, const void* q, const void* k, 
   a.head_dim_k = d->head_dim_k;
   a.head_dim_v = d->head_dim_v;
   a.scale = d->scale;
-  a.bf16 = d->dtype == GDN_DTYPE_BFLOAT16;
+  a.bf16 = is_bf16(d->dtype);
   return from_hip(gdn::launch_bwd(a, stream));
 }
 

@@ -114,12 +114,16 @@ struct BwdArgs {
   const int32_t* cu_seqlens;   // may be null
   float *dq, *dk, *dv, *dg, *dbeta;
   float* d_initial_state;      // may be null (not written)
-  void* workspace;             // bwd_workspace_bytes, 256-byte aligned
+  void* workspace;             // bwd_parts(...).total bytes, 256-byte aligned
   int batch, seqlen, num_seqs, Hqk, Hv, head_dim_k, head_dim_v;
   float scale;
   bool bf16;
 };
-size_t bwd_workspace_bytes(int64_t tokens, int num_seqs, int Hv, int dk, int dv, bool bf16);
+// Workspace of the backward pass (byte offsets of its parts and the total size).
+struct BwdParts {
+  size_t cpre = 0, state = 0, dm = 0, u = 0, dz = 0, total = 0;
+};
+BwdParts bwd_parts(int64_t tokens, int num_seqs, int Hv, int dk, int dv, bool bf16);
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);

@@ -1239,9 +1239,6 @@ hipError_t launch_fused(const PrefillArgs& a, hipStream_t stream) {
 }
 }  // namespace
 
-size_t order_workspace_bytes(int num_seqs) {
-  return num_seqs >= 2 && num_seqs <= kMaxOrdered ? (static_cast<size_t>(num_seqs) * 4 + 255) / 256 * 256 : 0;
-}
 
 hipError_t launch_prefill(const PrefillArgs& args, hipStream_t stream) {
   if (args.chunk != C) return hipErrorInvalidValue;

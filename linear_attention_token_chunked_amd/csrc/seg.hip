@@ -183,58 +183,7 @@ __global__ __launch_bounds__(256) void seg_correct_kernel(bf16* o, const bf16* q
   }
 }
 
-struct SegParts {
-  size_t qt, fin, phi, mstart, mbuf, total;
-};
-SegParts seg_parts(int batch, int T, int Hv, int nseg) {
-  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-  const size_t mat = static_cast<size_t>(D) * D;
-  SegParts w;
-  w.qt = 0;
-  w.fin = al(static_cast<size_t>(batch) * T * Hv * D * 2);
-  w.phi = w.fin + al(static_cast<size_t>(nseg) * batch * Hv * mat * 4);
-  w.mstart = w.phi + al(static_cast<size_t>(nseg) * batch * Hv * mat * 4);
-  w.mbuf = w.mstart + al(static_cast<size_t>(nseg) * batch * Hv * mat * 2);
-  w.total = w.mbuf + 2 * al(static_cast<size_t>(batch) * Hv * mat * 4);
-  return w;
-}
-
 }  // namespace
-
-bool seg_plan(int batch, int T, int Hv, SegPlan* sp) {
-  const int64_t units = static_cast<int64_t>(batch) * Hv;
-  if (units <= 0 || units > kComputeUnits) return false;
-  // 2 nseg - 1 runs per unit fill at most every compute unit (one 128-column
-  // workgroup each), each segment holds at least 16 chunks, and fewer than
-  // three segments would not pay for the wider slices and the extra runs
-  int nseg = static_cast<int>((kComputeUnits / units + 1) / 2);
-  nseg = std::min(nseg, T / (16 * C));
-  if (nseg < 3) return false;
-  const int nch = (T + C - 1) / C;
-  const int len = (nch + nseg - 1) / nseg * C;
-  nseg = (T + len - 1) / len;  // (no empty segment)
-  if (nseg < 3) return false;
-  sp->nseg = nseg;
-  sp->seg_len = len;
-  return true;
-}
-
-size_t seg_workspace_bytes(int batch, int T, int Hv) {
-  SegPlan sp;
-  if (!seg_plan(batch, T, Hv, &sp)) return 0;
-  return seg_parts(batch, T, Hv, sp.nseg).total;
-}
-
-void seg_carve(void* ws, int batch, int T, int Hv, SegPlan* sp) {
-  const SegParts w = seg_parts(batch, T, Hv, sp->nseg);
-  unsigned char* base = static_cast<unsigned char*>(ws);
-  sp->qt = base + w.qt;
-  sp->fin = reinterpret_cast<float*>(base + w.fin);
-  sp->phi = reinterpret_cast<float*>(base + w.phi);
-  sp->mstart = base + w.mstart;
-  sp->mbuf = reinterpret_cast<float*>(base + w.mbuf);
-  sp->mbuf_stride = (w.total - w.mbuf) / 2 / sizeof(float);
-}
 
 hipError_t launch_seg_finish(const PrefillArgs& a, const SegPlan& sp, hipStream_t stream) {
   const size_t scan_lds = (D + 16) * LDS_F * sizeof(float);

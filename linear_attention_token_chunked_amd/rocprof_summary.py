@@ -33,8 +33,8 @@ CSRC = os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc")
 
 # Source files of each family of kernels the bench measures.
 SOURCES = {
-    "prefill": ["prefill.hip", "seg.hip", "device_common.hpp"],
-    "bwd": ["prefill.hip", "bwd.hip", "device_common.hpp"],
+    "prefill": ["prefill.hip", "seg.hip", "device_common.hpp", "plan.cpp"],
+    "bwd": ["prefill.hip", "bwd.hip", "device_common.hpp", "plan.cpp"],
     "decode": ["decode.hip"],
     "verify": ["verify.hip"],
     "epilogue": ["epilogue.hip"],
