@@ -286,8 +286,11 @@ size_t gdn_bwd_chunked_workspace_size(const gdn_dims_t* d);
  *   d_initial_state [N, Hv, dk, dv] fp32, 16-byte aligned, or NULL (not written)
  *   workspace      at least gdn_bwd_chunked_workspace_size(d) bytes, 256-byte
  *                  aligned; its contents on entry and exit are unspecified
- * Every gradient element is written (the kernels clear dq, dk, dg and dbeta on
- * the stream first).  Outputs must not overlap each other or any input.
+ * Every gradient element is written once, with a plain store (no atomics, no
+ * clearing pass), and every sum is taken in a fixed order: the same inputs give
+ * bitwise the same gradients on every call.  dq and dk are summed over the value
+ * heads of a query/key head in one workgroup.  Outputs must not overlap each
+ * other or any input.
  * Supported: dk = dv in {64, 128}, C = 64, dtype bf16; dtype fp32 with dk = 64.
  */
 gdn_status_t gdn_bwd_chunked(const gdn_dims_t* d, const void* q, const void* k, const void* v,

@@ -25,9 +25,12 @@
 //   2. dstate_kernel walks each (sequence, value head, 32-column slice of dv)
 //      backwards over its chunks, holding dM in registers: it keeps dM' and dZ
 //      per chunk and leaves dM of the first chunk as the initial state's gradient;
-//   3. dlocal_kernel forms every per-token gradient of one chunk and one value
-//      head, all chunks in parallel (value heads that share a query/key head
-//      add their dq and dk with atomics).
+//   3. dlocal_kernel forms every per-token gradient of one chunk, all chunks in
+//      parallel, one workgroup per query/key head walking the value heads that
+//      share it (their dq and dk summed in registers).
+// Every sum is taken in a fixed order and every output element is written once
+// (no atomics), so a call's gradients do not depend on scheduling: the same
+// inputs give bitwise the same gradients.
 // Products run on the matrix cores over 16-wide k-steps with operands in LDS
 // (bf16 inputs: bf16 operands, fp32 accumulation; fp32 inputs: fp32 throughout).
 // Workgroup barriers order LDS only (lds_barrier): the stores to the workspace
@@ -443,6 +446,8 @@ template <class T, int DK, int DV>
 struct DlLayout {
   static constexpr int PAD = 32 / sizeof(T);
   static constexpr int LDK = DK + PAD, LDV = DV + PAD, LDC = C + PAD;
+  static constexpr int KTL = DK / 16;             // key-dim tiles (16-column blocks of dq and dk)
+  static constexpr int NOT = (C / 16) * KTL / 8;  // dq (and dk) tiles per wavefront
   static constexpr int oQ = 0;
   static constexpr int oK = oQ + C * LDK * sizeof(T);
   static constexpr int odO = oK + C * LDK * sizeof(T);
@@ -452,17 +457,36 @@ struct DlLayout {
   static constexpr int odP = oM + DK * LDV * sizeof(T);
   static constexpr int oS = odP + C * LDC * sizeof(T);
   static constexpr int oVec = oS + C * LDC * sizeof(T);
-  static constexpr int odG = oVec + (V_N * C + 4) * 4;
-  static constexpr int odB = odG + C * 4;
-  static constexpr int bytes = odB + C * 4;
+  // The per-token sums that make dG and dbeta, one slot per contribution, each
+  // written once per value head and added in a fixed order at the end (so the
+  // gradients do not depend on the order in which wavefronts finish):
+  //   RG [kind][tj][token]  row sums of the Gram tiles (kind 0: dP, 1: dA) of column block tj
+  //   CG [kind][ti][token]  their column sums, by row block ti
+  //   RB [tj][token]        the dbeta row sums of the dA tiles
+  //   B0 [token]            the dZ . v part of dbeta
+  //   QG, QB [kt][token]    the dq / dk tiles' terms of key block kt (dG, dbeta)
+  //   DG [kt][token]        the U dM'^T tiles' terms
+  //   SC                    terms of the last token: <dM', M> per wavefront, then
+  //                         the U dM'^T terms per wavefront and tile
+  static constexpr int oRG = oVec + (V_N * C + 4) * 4;
+  static constexpr int oCG = oRG + 2 * 4 * C * 4;
+  static constexpr int oRB = oCG + 2 * 4 * C * 4;
+  static constexpr int oB0 = oRB + 4 * C * 4;
+  static constexpr int oQG = oB0 + C * 4;
+  static constexpr int oQB = oQG + KTL * C * 4;
+  static constexpr int oDG = oQB + KTL * C * 4;
+  static constexpr int oSC = oDG + KTL * C * 4;
+  static constexpr int bytes = oSC + (8 + 8 * NOT) * 4;
 };
 
+// One workgroup per (chunk, query/key head): it walks the value heads that
+// share the query/key head, summing their dq and dk tiles in registers, and
+// writes every gradient element once with a plain store.
 template <class T, int DK, int DV>
 __global__ __launch_bounds__(512) void dlocal_kernel(BwdParams p) {
   using L = DlLayout<T, DK, DV>;
   constexpr int LDK = L::LDK, LDV = L::LDV, LDC = L::LDC, NT = 512;
-  constexpr int KTL = DK / 16;             // key-dim tiles
-  constexpr int NOT = (C / 16) * KTL / 8;  // dq (and dk) tiles per wavefront
+  constexpr int KTL = L::KTL, NOT = L::NOT;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   T* sQ = reinterpret_cast<T*>(smem + L::oQ);
   T* sK = reinterpret_cast<T*>(smem + L::oK);
@@ -473,12 +497,17 @@ __global__ __launch_bounds__(512) void dlocal_kernel(BwdParams p) {
   T* sdP = reinterpret_cast<T*>(smem + L::odP);
   T* sS = reinterpret_cast<T*>(smem + L::oS);
   float* vec = reinterpret_cast<float*>(smem + L::oVec);
-  float* sdG = reinterpret_cast<float*>(smem + L::odG);
-  float* sdB = reinterpret_cast<float*>(smem + L::odB);
+  float* sRG = reinterpret_cast<float*>(smem + L::oRG);
+  float* sCG = reinterpret_cast<float*>(smem + L::oCG);
+  float* sRB = reinterpret_cast<float*>(smem + L::oRB);
+  float* sB0 = reinterpret_cast<float*>(smem + L::oB0);
+  float* sQG = reinterpret_cast<float*>(smem + L::oQG);
+  float* sQB = reinterpret_cast<float*>(smem + L::oQB);
+  float* sDG = reinterpret_cast<float*>(smem + L::oDG);
+  float* sSC = reinterpret_cast<float*>(smem + L::oSC);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lg = lane >> 4, lr = lane & 15;
-  const int gc = blockIdx.x / p.Hv, h = blockIdx.x - (blockIdx.x / p.Hv) * p.Hv;
+  const int tid0 = threadIdx.x;
+  const int gc = blockIdx.x / p.Hqk, hq = blockIdx.x - (blockIdx.x / p.Hqk) * p.Hqk;
   // the chunk's sequence: the last n with chunk base <= gc
   int n, c;
   if (p.cu) {
@@ -499,221 +528,255 @@ __global__ __launch_bounds__(512) void dlocal_kernel(BwdParams p) {
   }
   const Seq sq = seq_of(p.cu, p.cpre, p.T, n);
   const int cs = sq.bos + c * C, Lc = min(C, sq.eos - cs);
-  const int rep = p.Hv / p.Hqk, hq = h / rep;
+  const int rep = p.Hv / p.Hqk;
   const size_t qk_tok = static_cast<size_t>(p.Hqk) * DK, v_tok = static_cast<size_t>(p.Hv) * DV;
   const float s = p.scale;
-  const size_t ck = (static_cast<size_t>(sq.cbase + c) * p.Hv + h) * DK * DV;
   const size_t qo = static_cast<size_t>(cs) * qk_tok + static_cast<size_t>(hq) * DK;
-  const size_t vo = static_cast<size_t>(cs) * v_tok + static_cast<size_t>(h) * DV;
-  // dq, dk: value heads that share a query/key head add into the same rows
-  auto put = [&](float* dst, size_t off, float x) {
-    if (rep == 1) dst[off] = x;
-    else atomicAdd(dst + off, x);
-  };
+  // A wavefront's dq and dk tiles share one 16-column block kt (tile t = wave + 8i, kt = t % KTL), so
+  // the B operands are read once for all of them.
+  static_assert(8 % KTL == 0, "one key block per wavefront");
+  floatx4 dqa[NOT], dka[NOT];  // dq and dk tiles, summed over the value heads
+#pragma unroll
+  for (int i = 0; i < NOT; ++i) dqa[i] = dka[i] = zero4();
 
-  // -- stage: Q, K, dO, U, dZ, M; gates
-  if (tid < C) {
-    sdG[tid] = 0.f;
-    sdB[tid] = 0.f;
-  }
-  // every global operand is requested here, so the workgroup waits for memory once;
-  // v and dM' stay in registers until they are used
-  RowsInFlight<T, DV, NT> rv;
-  RowsInFlight<T, DV, NT, DK> rdm;
-  {
-    RowsInFlight<T, DK, NT> rq, rk;
-    RowsInFlight<T, DV, NT> rdo, ru, rdz;
-    RowsInFlight<T, DV, NT, DK> rm;
-    rq.load(static_cast<const T*>(p.q) + qo, qk_tok, Lc, tid);
-    rk.load(static_cast<const T*>(p.k) + qo, qk_tok, Lc, tid);
-    rdo.load(static_cast<const T*>(p.dout) + vo, v_tok, Lc, tid);
-    ru.load(static_cast<const T*>(p.ck_u) + vo, v_tok, Lc, tid);
-    rdz.load(static_cast<const T*>(p.dz) + vo, v_tok, Lc, tid);
-    rm.load(static_cast<const T*>(p.ck_state) + ck, DV, DK, tid);
-    rv.load(static_cast<const T*>(p.v) + vo, v_tok, Lc, tid);
-    rdm.load(static_cast<const T*>(p.dm) + ck, DV, DK, tid);
-    if (wave == 0) {
-      const size_t gi = static_cast<size_t>(cs) * p.Hv + h;
-      gate_vectors(vec, p.g + gi, p.beta + gi, p.Hv, Lc, lane);
-    }
-    rq.store(sQ, LDK, tid);
-    rk.store(sK, LDK, tid);
-    rdo.store(sdO, LDV, tid);
-    ru.store(sU, LDV, tid);
-    rdz.store(sdZ, LDV, tid);
-    rm.store(sM, LDV, tid);
-  }
-  lds_barrier();
-  {  // the dZ . v part of dbeta
-    constexpr int PR = DV / 4, IT = C * PR / NT;
-    static_assert(C * PR % NT == 0 && NT % PR == 0 && IT == decltype(rv)::IT, "whole rows per pass");
-    static_assert(PR == 16 || PR == 32, "a row is one or two 16-lane groups");
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const int i = tid + it * NT, t = i / PR, e = (i - t * PR) * 4;
-      float part = 0.f;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) part += to_float(sdZ[t * LDV + e + x]) * to_float(rv.v[it][x]);
-      part = sum16(part);  // the row's lanes first, then one atomic per row
-      if constexpr (PR == 32) part += __shfl_xor(part, 16);
-      if ((lane & (PR - 1)) == 0 && t < Lc) atomicAdd(&sdB[t], part);
-    }
-  }
-  // -- C x C tiles: dP (masked, times s exp(G_i - G_j)) and D + D^T, with their dG and dbeta terms
-  for (int job = wave; job < 20; job += 8) {
-    const int kind = job / 10, lt = job % 10;
-    const int ti = lt < 1 ? 0 : lt < 3 ? 1 : lt < 6 ? 2 : 3;
-    const int tj = lt - ti * (ti + 1) / 2;
-    floatx4 gr = zero4(), d = zero4();
-    tile_mm_nn<T, DK>(gr, (kind ? sK : sQ) + 16 * ti * LDK, LDK, sK + 16 * tj * LDK, LDK, lane);
-    tile_mm_nn<T, DV>(d, (kind ? sdZ : sdO) + 16 * ti * LDV, LDV, sU + 16 * tj * LDV, LDV, lane);
-    const int j = 16 * tj + lr, i0 = 16 * ti + 4 * lg;
-    const floatx4 Gi = vec4_at(vec + V_GL * C + i0), bi = vec4_at(vec + V_BETA * C + i0);
-    const float Gj = vec[V_GL * C + j];
-    float colsum = 0.f;
-    floatx4 rw, rb;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {  // branch-free: the masks are selects
-      const int i = i0 + r;
-      const float e = __builtin_amdgcn_exp2f(Gi[r] - Gj);
-      float w, rowb = 0.f;
-      if (kind == 0) {  // P_ij = s dec (QK^T)_ij, dP_ij = (dO U^T)_ij, j <= i
-        const float dps = j <= i ? d[r] * s * e : 0.f;  // dP s dec
-        w = dps * gr[r];
-        sdP[i * LDC + j] = from_float<T>(dps);
-      } else {  // A_ij = beta_i dec (KK^T)_ij, dA_ij = -(dZ U^T)_ij, j < i
-        const float dae = j < i ? -d[r] * e : 0.f;  // dA dec
-        w = dae * bi[r] * gr[r];
-        rowb = dae * gr[r];
-        const T dd = from_float<T>(dae * bi[r]);
-        if (j < i) sS[j * LDC + i] = dd;
-        if (j <= i) sS[i * LDC + j] = dd;  // (zero on the diagonal)
-      }
-      colsum += w;
-      rw[r] = sum16(w);
-      rb[r] = sum16(rowb);
-    }
-    if (kind == 0 && ti != tj) {  // the tile above the diagonal is zero
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sdP[j * LDC + i0 + r] = from_float<T>(0.f);
-    }
-    if (lr == 0) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        atomicAdd(&sdG[i0 + r], rw[r]);
-        if (kind) atomicAdd(&sdB[i0 + r], rb[r]);
-      }
-    }
-    colsum += __shfl_xor(colsum, 16);
-    colsum += __shfl_xor(colsum, 32);
-    if (lg == 0) atomicAdd(&sdG[j], -colsum);
-  }
-  lds_barrier();
-  // -- dq = s diag(gam) dO M^T + (dP s dec) K  (written out);
-  //    dk = -diag(beta gam) dZ M^T + (dP s dec)^T Q + (D + D^T) K  (kept; the dM' term follows)
-  // A wavefront's tiles share one 16-column block kt of dq and dk (tile t = wave + 8i, kt = t % KTL),
-  // so the B operands are read once for all of them.
-  static_assert(8 % KTL == 0 || KTL % 8 == 0, "one key block per wavefront");
-  const int kt = wave % KTL;
-  floatx4 dka[NOT];
-  {
-    const RowFrags<T, DV> mf(sM + 16 * kt * LDV, LDV, lane);  // M rows of the block
-    const ColFrags<T, C> kcol(sK + 16 * kt, LDK, lane), qcol(sQ + 16 * kt, LDK, lane);
-#pragma unroll
-  for (int i = 0; i < NOT; ++i) {
-    const int t = wave + 8 * i, it = t / KTL;
-    floatx4 a = zero4(), b = zero4();
-    tile_mm_nn<T, DV>(a, sdO + 16 * it * LDV, LDV, mf, lane);  // dO M^T
-    tile_mm_nn<T, DV>(b, sdZ + 16 * it * LDV, LDV, mf, lane);  // dZ M^T
-    floatx4 dq = zero4();
-    dka[i] = zero4();
+  for (int hh = 0; hh < rep; ++hh) {
+    // The body's LDS addresses derive from the thread index; formed from an
+    // opaque copy of it each pass, they are computed where they are used
+    // rather than hoisted out of the loop and held in registers throughout.
+    int tid;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"(tid0));
+    const int lane = tid & 63, wave = tid >> 6, lg = lane >> 4, lr = lane & 15, kt = wave % KTL;
+    const int h = hq * rep + hh;
+    const size_t ck = (static_cast<size_t>(sq.cbase + c) * p.Hv + h) * DK * DV;
+    const size_t vo = static_cast<size_t>(cs) * v_tok + static_cast<size_t>(h) * DV;
+    // -- stage: Q and K (once), dO, U, dZ, M; gates.  Every global operand is requested first, so the
+    //    workgroup waits for memory once per value head; v and dM' stay in registers until they are used.
+    RowsInFlight<T, DV, NT> rv;
+    RowsInFlight<T, DV, NT, DK> rdm;
     {
-      const int r0 = 16 * it + 4 * lg, key = 16 * kt + lr;
-      const floatx4 gam = vec4_at(vec + V_GAM * C + r0), bt = vec4_at(vec + V_BETA * C + r0);
-      floatx4 gq, gk;
+      RowsInFlight<T, DK, NT> rq, rk;
+      RowsInFlight<T, DV, NT> rdo, ru, rdz;
+      RowsInFlight<T, DV, NT, DK> rm;
+      if (hh == 0) {
+        rq.load(static_cast<const T*>(p.q) + qo, qk_tok, Lc, tid);
+        rk.load(static_cast<const T*>(p.k) + qo, qk_tok, Lc, tid);
+      }
+      rdo.load(static_cast<const T*>(p.dout) + vo, v_tok, Lc, tid);
+      ru.load(static_cast<const T*>(p.ck_u) + vo, v_tok, Lc, tid);
+      rdz.load(static_cast<const T*>(p.dz) + vo, v_tok, Lc, tid);
+      rm.load(static_cast<const T*>(p.ck_state) + ck, DV, DK, tid);
+      rv.load(static_cast<const T*>(p.v) + vo, v_tok, Lc, tid);
+      rdm.load(static_cast<const T*>(p.dm) + ck, DV, DK, tid);
+      float gt = 0.f, bt = 0.f;  // tokens past the end act as g = 0, beta = 0
+      if (wave == 0 && lane < Lc) {
+        const size_t gi = static_cast<size_t>(cs + lane) * p.Hv + h;
+        gt = p.g[gi];
+        bt = p.beta[gi];
+      }
+      if (hh > 0) lds_barrier();  // the previous value head's reads of LDS are done
+      if (wave == 0) gate_vectors_from(vec, gt, bt, lane);
+      if (hh == 0) {
+        rq.store(sQ, LDK, tid);
+        rk.store(sK, LDK, tid);
+      }
+      rdo.store(sdO, LDV, tid);
+      ru.store(sU, LDV, tid);
+      rdz.store(sdZ, LDV, tid);
+      rm.store(sM, LDV, tid);
+    }
+    lds_barrier();
+    {  // the dZ . v part of dbeta
+      constexpr int PR = DV / 4, IT = C * PR / NT;
+      static_assert(C * PR % NT == 0 && NT % PR == 0 && IT == decltype(rv)::IT, "whole rows per pass");
+      static_assert(PR == 16 || PR == 32, "a row is one or two 16-lane groups");
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        dq[r] = s * gam[r] * a[r];
-        dka[i][r] = -bt[r] * gam[r] * b[r];
-        gq[r] = sum16(to_float(sQ[(r0 + r) * LDK + key]) * a[r]);
-        gk[r] = sum16(to_float(sK[(r0 + r) * LDK + key]) * b[r]);
+      for (int it = 0; it < IT; ++it) {
+        const int i = tid + it * NT, t = i / PR, e = (i - t * PR) * 4;
+        float part = 0.f;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) part += to_float(sdZ[t * LDV + e + x]) * to_float(rv.v[it][x]);
+        part = sum16(part);  // the row's lanes first
+        if constexpr (PR == 32) part += __shfl_xor(part, 16);
+        if ((lane & (PR - 1)) == 0) sB0[t] = part;
+      }
+    }
+    // -- C x C tiles: dP (masked, times s exp(G_i - G_j)) and D + D^T, with their dG and dbeta terms
+    for (int job = wave; job < 20; job += 8) {
+      const int kind = job / 10, lt = job % 10;
+      const int ti = lt < 1 ? 0 : lt < 3 ? 1 : lt < 6 ? 2 : 3;
+      const int tj = lt - ti * (ti + 1) / 2;
+      floatx4 gr = zero4(), d = zero4();
+      tile_mm_nn<T, DK>(gr, (kind ? sK : sQ) + 16 * ti * LDK, LDK, sK + 16 * tj * LDK, LDK, lane);
+      tile_mm_nn<T, DV>(d, (kind ? sdZ : sdO) + 16 * ti * LDV, LDV, sU + 16 * tj * LDV, LDV, lane);
+      const int j = 16 * tj + lr, i0 = 16 * ti + 4 * lg;
+      const floatx4 Gi = vec4_at(vec + V_GL * C + i0), bi = vec4_at(vec + V_BETA * C + i0);
+      const float Gj = vec[V_GL * C + j];
+      float colsum = 0.f;
+      floatx4 rw, rb;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {  // branch-free: the masks are selects
+        const int i = i0 + r;
+        const float e = __builtin_amdgcn_exp2f(Gi[r] - Gj);
+        float w, rowb = 0.f;
+        if (kind == 0) {  // P_ij = s dec (QK^T)_ij, dP_ij = (dO U^T)_ij, j <= i
+          const float dps = j <= i ? d[r] * s * e : 0.f;  // dP s dec
+          w = dps * gr[r];
+          sdP[i * LDC + j] = from_float<T>(dps);
+        } else {  // A_ij = beta_i dec (KK^T)_ij, dA_ij = -(dZ U^T)_ij, j < i
+          const float dae = j < i ? -d[r] * e : 0.f;  // dA dec
+          w = dae * bi[r] * gr[r];
+          rowb = dae * gr[r];
+          const T dd = from_float<T>(dae * bi[r]);
+          if (j < i) sS[j * LDC + i] = dd;
+          if (j <= i) sS[i * LDC + j] = dd;  // (zero on the diagonal)
+        }
+        colsum += w;
+        rw[r] = sum16(w);
+        rb[r] = sum16(rowb);
+      }
+      if (kind == 0 && ti != tj) {  // the tile above the diagonal is zero
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sdP[j * LDC + i0 + r] = from_float<T>(0.f);
       }
       if (lr == 0) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          atomicAdd(&sdG[r0 + r], s * gam[r] * gq[r] - bt[r] * gam[r] * gk[r]);
-          atomicAdd(&sdB[r0 + r], -gam[r] * gk[r]);
+          sRG[(kind * 4 + tj) * C + i0 + r] = rw[r];
+          if (kind) sRB[tj * C + i0 + r] = rb[r];
         }
       }
+      colsum += __shfl_xor(colsum, 16);
+      colsum += __shfl_xor(colsum, 32);
+      if (lg == 0) sCG[(kind * 4 + ti) * C + j] = -colsum;
     }
-    tile_mm<T, false, C>(dq, sdP + 16 * it * LDC, LDC, kcol, lane);
-    tile_mm<T, true, C>(dka[i], sdP + 16 * it, LDC, qcol, lane);
-    tile_mm<T, false, C>(dka[i], sS + 16 * it * LDC, LDC, kcol, lane);
+    lds_barrier();
+    // -- dq += s diag(gam) dO M^T + (dP s dec) K;
+    //    dk += -diag(beta gam) dZ M^T + (dP s dec)^T Q + (D + D^T) K  (the dM' term follows)
+    {
+      const RowFrags<T, DV> mf(sM + 16 * kt * LDV, LDV, lane);  // M rows of the block
+      const ColFrags<T, C> kcol(sK + 16 * kt, LDK, lane), qcol(sQ + 16 * kt, LDK, lane);
+#pragma unroll
+      for (int i = 0; i < NOT; ++i) {
+        const int t = wave + 8 * i, it = t / KTL;
+        floatx4 a = zero4(), b = zero4();
+        tile_mm_nn<T, DV>(a, sdO + 16 * it * LDV, LDV, mf, lane);  // dO M^T
+        tile_mm_nn<T, DV>(b, sdZ + 16 * it * LDV, LDV, mf, lane);  // dZ M^T
+        {
+          const int r0 = 16 * it + 4 * lg, key = 16 * kt + lr;
+          const floatx4 gam = vec4_at(vec + V_GAM * C + r0), bt = vec4_at(vec + V_BETA * C + r0);
+          floatx4 gq, gk;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            dqa[i][r] += s * gam[r] * a[r];
+            dka[i][r] -= bt[r] * gam[r] * b[r];
+            gq[r] = sum16(to_float(sQ[(r0 + r) * LDK + key]) * a[r]);
+            gk[r] = sum16(to_float(sK[(r0 + r) * LDK + key]) * b[r]);
+          }
+          if (lr == 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              sQG[kt * C + r0 + r] = s * gam[r] * gq[r] - bt[r] * gam[r] * gk[r];
+              sQB[kt * C + r0 + r] = -gam[r] * gk[r];
+            }
+          }
+        }
+        tile_mm<T, false, C>(dqa[i], sdP + 16 * it * LDC, LDC, kcol, lane);
+        tile_mm<T, true, C>(dka[i], sdP + 16 * it, LDC, qcol, lane);
+        tile_mm<T, false, C>(dka[i], sS + 16 * it * LDC, LDC, kcol, lane);
+      }
+    }
+    // -- dM' replaces M in LDS; gam_C <dM', M> enters dG at the chunk's end
+    {
+      constexpr int PR = DV / 4, IT = DK * PR / NT;
+      static_assert(DK * PR % NT == 0 && IT == decltype(rdm)::IT, "whole passes");
+      float part = 0.f;
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const int i = tid + it * NT, r = i / PR, e = (i - r * PR) * 4;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) part += to_float(rdm.v[it][x]) * to_float(sM[r * LDV + e + x]);
+      }
+      part = sum16(part);
+      part += __shfl_xor(part, 16);
+      part += __shfl_xor(part, 32);
+      if (lane == 0) sSC[wave] = vec[V_N * C] * part;
+      lds_barrier();  // every M value is read before dM' replaces it
+      rdm.store(sM, LDV, tid);
+    }
+    lds_barrier();
+    // -- dk += diag(kf) U dM'^T, with its dG terms
+    {
+      const RowFrags<T, DV> dmf(sM + 16 * kt * LDV, LDV, lane);  // dM' rows of the block
+#pragma unroll
+      for (int i = 0; i < NOT; ++i) {
+        const int t = wave + 8 * i, it = t / KTL;
+        floatx4 a = zero4();
+        tile_mm_nn<T, DV>(a, sU + 16 * it * LDV, LDV, dmf, lane);  // U dM'^T
+        const int r0 = 16 * it + 4 * lg, key = 16 * kt + lr;
+        const floatx4 kf = vec4_at(vec + V_KF * C + r0);
+        floatx4 sj;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          dka[i][r] += kf[r] * a[r];
+          sj[r] = kf[r] * sum16(to_float(sK[(r0 + r) * LDK + key]) * a[r]);
+        }
+        if (lr == 0) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sDG[kt * C + r0 + r] = -sj[r];
+        }
+        float tot = (sj[0] + sj[1]) + (sj[2] + sj[3]);  // this tile's part of the last token's term
+        tot += __shfl_xor(tot, 16);
+        tot += __shfl_xor(tot, 32);
+        if (lane == 0) sSC[8 + wave * NOT + i] = tot;
+      }
+    }
+    lds_barrier();
+    // -- dg = reverse cumsum of dG over the chunk; dbeta.  The slots of token t, added in a fixed order.
+    if (wave == 0) {
+      const int t = C - 1 - lane, tt = t / 16;
+      float dG = 0.f, dB = sB0[t];
+#pragma unroll
+      for (int kind = 0; kind < 2; ++kind)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          if (b <= tt) dG += sRG[(kind * 4 + b) * C + t];  // tiles (tt, b), b <= tt
+          if (b >= tt) dG += sCG[(kind * 4 + b) * C + t];  // tiles (b, tt), b >= tt
+        }
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        if (b <= tt) dB += sRB[b * C + t];
+#pragma unroll
+      for (int x = 0; x < KTL; ++x) {
+        dG += sQG[x * C + t] + sDG[x * C + t];
+        dB += sQB[x * C + t];
+      }
+      if (t == C - 1) {
+#pragma unroll
+        for (int x = 0; x < 8 + 8 * NOT; ++x) dG += sSC[x];
+      }
+      const float dg = wave_inclusive_sum(dG);
+      if (t < Lc) {
+        const size_t gi = static_cast<size_t>(cs + t) * p.Hv + h;
+        p.dg[gi] = dg;
+        p.dbeta[gi] = dB;
+      }
+    }
+  }
+  // -- dq and dk, the sums over the value heads
+  const int lane = tid0 & 63, wave = tid0 >> 6, lg = lane >> 4, lr = lane & 15, kt = wave % KTL;
+#pragma unroll
+  for (int i = 0; i < NOT; ++i) {
+    const int it = (wave + 8 * i) / KTL;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * it + 4 * lg + r;
-      if (row < Lc) put(p.dq, qo + static_cast<size_t>(row) * qk_tok + 16 * kt + lr, dq[r]);
+      if (row < Lc) {
+        const size_t o = qo + static_cast<size_t>(row) * qk_tok + 16 * kt + lr;
+        p.dq[o] = dqa[i][r];
+        p.dk[o] = dka[i][r];
+      }
     }
   }
-  }
-  // -- dM' replaces M in LDS; gam_C <dM', M> enters dG at the chunk's end
-  {
-    constexpr int PR = DV / 4, IT = DK * PR / NT;
-    static_assert(DK * PR % NT == 0 && IT == decltype(rdm)::IT, "whole passes");
-    float part = 0.f;
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const int i = tid + it * NT, r = i / PR, e = (i - r * PR) * 4;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) part += to_float(rdm.v[it][x]) * to_float(sM[r * LDV + e + x]);
-    }
-    part = sum16(part);
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
-    if (lane == 0) atomicAdd(&sdG[C - 1], vec[V_N * C] * part);
-    lds_barrier();  // every M value is read before dM' replaces it
-    rdm.store(sM, LDV, tid);
-  }
-  lds_barrier();
-  // -- dk += diag(kf) U dM'^T, with its dG terms
-  const RowFrags<T, DV> dmf(sM + 16 * kt * LDV, LDV, lane);  // dM' rows of the block
-#pragma unroll
-  for (int i = 0; i < NOT; ++i) {
-    const int t = wave + 8 * i, it = t / KTL;
-    floatx4 a = zero4();
-    tile_mm_nn<T, DV>(a, sU + 16 * it * LDV, LDV, dmf, lane);  // U dM'^T
-    const int r0 = 16 * it + 4 * lg, key = 16 * kt + lr;
-    const floatx4 kf = vec4_at(vec + V_KF * C + r0);
-    floatx4 sj;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      dka[i][r] += kf[r] * a[r];
-      sj[r] = kf[r] * sum16(to_float(sK[(r0 + r) * LDK + key]) * a[r]);
-      if (r0 + r < Lc) put(p.dk, qo + static_cast<size_t>(r0 + r) * qk_tok + key, dka[i][r]);
-    }
-    if (lr == 0) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) atomicAdd(&sdG[r0 + r], -sj[r]);
-      atomicAdd(&sdG[C - 1], sj[0] + sj[1] + sj[2] + sj[3]);
-    }
-  }
-  lds_barrier();
-  // -- dg = reverse cumsum of dG over the chunk; dbeta
-  if (wave == 0) {
-    const int t = C - 1 - lane;
-    const float dg = wave_inclusive_sum(sdG[t]);
-    if (t < Lc) {
-      const size_t gi = static_cast<size_t>(cs + t) * p.Hv + h;
-      p.dg[gi] = dg;
-      p.dbeta[gi] = sdB[t];
-    }
-  }
-}
-
-// Zeroes n floats.
-__global__ void zero_kernel(float* x, size_t n) {
-  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) x[i] = 0.f;
 }
 
 // Exclusive prefix sum of the chunk counts of the packed sequences: out[n] is
@@ -812,13 +875,7 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dlocal_kernel<T, DK, DV>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, LL::bytes);
   if (e != hipSuccess) return e;
-  if (a.Hv != a.Hqk) {  // value heads that share a query/key head add their dq, dk
-    const size_t nqk = static_cast<size_t>(tokens) * a.Hqk * DK;
-    const dim3 zg(static_cast<unsigned>((nqk + 255) / 256));
-    zero_kernel<<<zg, dim3(256), 0, stream>>>(a.dq, nqk);
-    zero_kernel<<<zg, dim3(256), 0, stream>>>(a.dk, nqk);
-  }
-  dlocal_kernel<T, DK, DV><<<dim3(p.chunk_bound * a.Hv), dim3(512), LL::bytes, stream>>>(p);
+  dlocal_kernel<T, DK, DV><<<dim3(p.chunk_bound * a.Hqk), dim3(512), LL::bytes, stream>>>(p);
   return hipGetLastError();
 }
 

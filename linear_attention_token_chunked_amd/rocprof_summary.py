@@ -71,7 +71,7 @@ def kind(name):
     for sub, fam, k in (("order_kernel", "prefill", "order"), ("seg_correct_kernel", "prefill", "seg_correct"),
                         ("seg_scan_step_kernel", "prefill", "seg_scan"),
                         ("dstate_kernel", "bwd", "bwd_dstate"), ("dlocal_kernel", "bwd", "bwd_dlocal"),
-                        ("chunk_prefix_kernel", "bwd", "bwd_prefix"), ("zero_kernel", "bwd", "bwd_zero"),
+                        ("chunk_prefix_kernel", "bwd", "bwd_prefix"),
                         ("decode_kernel", "decode", "decode"), ("verify_kernel", "verify", "verify"),
                         ("norm_gate_kernel", "epilogue", "epilogue"), ("conv_kernel", "short_conv", "short_conv")):
         if sub in name:

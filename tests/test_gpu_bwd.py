@@ -58,13 +58,14 @@ def test_bwd_small_matches_oracle(gdn, dtype, B, T, Hqk, Hv, d, init, final):
     check(got, ref, TOL[DT[dtype]])
 
 
-@pytest.mark.parametrize("d,lengths", [
-    (128, [0, 70, 1, 129, 64]),
-    (64, [5, 0, 300, 63, 65]),
+@pytest.mark.parametrize("d,lengths,Hqk", [
+    (128, [0, 70, 1, 129, 64], 2),
+    (64, [5, 0, 300, 63, 65], 2),
+    (128, [200, 0, 33], 1),  # four value heads on one query/key head
 ])
-def test_bwd_packed_with_empty_sequences(gdn, d, lengths):
-    flush(f"bwd packed d={d} lengths={lengths}")
-    inp = make_prefill(1, 0, 2, 4, d, d, "bf16", init_state=True, lengths=lengths, seed=3)
+def test_bwd_packed_with_empty_sequences(gdn, d, lengths, Hqk):
+    flush(f"bwd packed d={d} lengths={lengths} Hqk={Hqk}")
+    inp = make_prefill(1, 0, Hqk, 4, d, d, "bf16", init_state=True, lengths=lengths, seed=3)
     cot = make_cotangents(1, sum(lengths), 4, d, len(lengths), d, "bf16", seed=3)
     got, ref = run_case(gdn, inp, cot, scale=1.0)
     check(got, ref, TOL[torch.bfloat16])
@@ -96,17 +97,25 @@ def test_bwd_without_initial_state_gradient(gdn):
 
 
 def test_bwd_repeat_calls_are_identical(gdn):
-    """Every gradient is overwritten by each call (nothing accumulates across calls): a second call gives
-    the same gradients, up to the order of the in-workgroup sums of dg and dbeta."""
+    """Every gradient is overwritten by each call (nothing accumulates across calls), and every sum is taken
+    in a fixed order (no atomics): repeated calls give bitwise the same gradients, also when value heads
+    share a query/key head and sequences are packed."""
     flush("bwd repeat")
-    inp = to_dev(make_prefill(1, 130, 2, 4, 128, 128, "bf16", init_state=True, seed=2))
-    cot = make_cotangents(1, 130, 4, 128, 1, 128, "bf16", seed=2)
-    args = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], cot["d_o"].cuda())
-    a = gdn.bwd_chunked(*args, initial_state=inp["initial_state"], d_final_state=cot["d_final"].cuda())
-    b = gdn.bwd_chunked(*args, initial_state=inp["initial_state"], d_final_state=cot["d_final"].cuda())
-    torch.cuda.synchronize()
-    for name in NAMES:
-        assert rel_l2(f64(a[name]), f64(b[name])) <= 1e-6, name
+    for lengths, Hqk, Hv in [(None, 2, 4), ([130, 7, 300, 64], 1, 4)]:
+        T = 130 if lengths is None else 0
+        inp = to_dev(make_prefill(1, T, Hqk, Hv, 128, 128, "bf16", init_state=True, lengths=lengths, seed=2))
+        N = 1 if lengths is None else len(lengths)
+        tokens = inp["q"].shape[1]
+        cot = make_cotangents(1, tokens, Hv, 128, N, 128, "bf16", seed=2)
+        args = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], cot["d_o"].cuda())
+        kw = dict(initial_state=inp["initial_state"], d_final_state=cot["d_final"].cuda(),
+                  cu_seqlens=inp["cu_seqlens"], scale=128 ** -0.5)
+        a = gdn.bwd_chunked(*args, **kw)
+        for _ in range(2):
+            b = gdn.bwd_chunked(*args, **kw)
+            torch.cuda.synchronize()
+            for name in NAMES:
+                assert torch.equal(a[name], b[name]), (lengths, name)
 
 
 def test_bwd_full_workload_sampled_units(gdn):
