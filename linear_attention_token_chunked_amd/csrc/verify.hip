@@ -23,41 +23,43 @@ namespace {
 
 constexpr int kVerifyThreads = 256;
 
+// Each wavefront owns a block of DV / 4 state columns over all DK rows, so the
+// reductions over the key dimension (M^T k, M^T q, k . q) stay inside the
+// wavefront (lane shuffles) and the token loop runs without a workgroup
+// barrier.  A thread holds rows rg, rg + RG, ... of four columns, so a load
+// instruction covers RG consecutive rows.
 template <class T, int DK, int DV>
 __global__ __launch_bounds__(kVerifyThreads) void verify_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ g,
     const float* __restrict__ beta, const float* state_in, float* state_out, float* __restrict__ token_states,
     T* __restrict__ o, int Tv, int Hqk, int Hv, float scale) {
-  constexpr int TPR = DV / 4;                  // threads per state row (one float4 each)
-  constexpr int RG = kVerifyThreads / TPR;     // row groups
-  constexpr int RPT = DK / RG;                 // rows per thread: rg, rg + RG, ...
   constexpr int NWAVE = kVerifyThreads / 64;
-  static_assert(DK % RG == 0 && 64 % TPR == 0, "shape");
+  constexpr int CPW = DV / NWAVE;  // state columns per wavefront
+  constexpr int TPR = CPW / 4;     // threads per row of them (one float4 each)
+  constexpr int RG = 64 / TPR;     // row groups of a wavefront
+  constexpr int RPT = DK / RG;     // rows per thread: rg, rg + RG, ...
+  static_assert(CPW % 4 == 0 && 64 % TPR == 0 && DK % RG == 0, "shape");
 
   const int unit = blockIdx.x;  // n * Hv + h
   const int n = unit / Hv;
   const int h = unit - n * Hv;
   const int hq = h / (Hv / Hqk);
   const int tid = threadIdx.x;
-  const int cg = tid % TPR;
-  const int rg = tid / TPR;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int rg = lane / TPR;
+  const int col = (tid >> 6) * CPW + 4 * (lane % TPR);
 
   __shared__ float sk[kMaxVerifyTokens][DK];
   __shared__ float sq[kMaxVerifyTokens][DK];
   __shared__ float sv[kMaxVerifyTokens][DV];
-  __shared__ float sab[kMaxVerifyTokens][2];        // alpha, beta per token
-  __shared__ floatx4 red_r[2][NWAVE][TPR];          // by token parity: one barrier per token
-  __shared__ floatx4 red_p[2][NWAVE][TPR];
-  __shared__ float red_kq[2][NWAVE];
+  __shared__ float sab[kMaxVerifyTokens][2];  // alpha, beta per token
 
   // The state slice first: these loads dominate the run time.
   const size_t sbase = static_cast<size_t>(unit) * DK * DV;
   floatx4 m[RPT];
 #pragma unroll
   for (int r = 0; r < RPT; ++r)
-    m[r] = *reinterpret_cast<const floatx4*>(state_in + sbase + static_cast<size_t>(rg + RG * r) * DV + 4 * cg);
+    m[r] = *reinterpret_cast<const floatx4*>(state_in + sbase + static_cast<size_t>(rg + RG * r) * DV + col);
 
   // Every token's key, query, value and gates into LDS.
   for (int i = tid; i < Tv * DK; i += kVerifyThreads) {
@@ -78,7 +80,6 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_kernel(
   __syncthreads();
 
   for (int t = 0; t < Tv; ++t) {
-    const int par = t & 1;
     floatx4 r = zero4(), p = zero4();
     float kq = 0.f;
 #pragma unroll
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_kernel(
       p += qi * m[i];
       kq += ki * qi;
     }
-    // Sum over the row groups inside the wavefront, then across wavefronts.
+    // Sum over the wavefront's row groups: every lane ends with the full sums of its columns.
 #pragma unroll
     for (int off = TPR; off < 64; off <<= 1) {
 #pragma unroll
@@ -98,36 +99,21 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_kernel(
       }
       kq += __shfl_xor(kq, off);
     }
-    if (lane < TPR) {
-      red_r[par][wave][cg] = r;
-      red_p[par][wave][cg] = p;
-      if (lane == 0) red_kq[par][wave] = kq;
-    }
-    __syncthreads();
-    r = red_r[par][0][cg];
-    p = red_p[par][0][cg];
-    kq = red_kq[par][0];
-#pragma unroll
-    for (int w = 1; w < NWAVE; ++w) {
-      r += red_r[par][w][cg];
-      p += red_p[par][w][cg];
-      kq += red_kq[par][w];
-    }
     const float alpha = sab[t][0], b = sab[t][1];
-    const floatx4 vv = *reinterpret_cast<const floatx4*>(&sv[t][4 * cg]);
+    const floatx4 vv = *reinterpret_cast<const floatx4*>(&sv[t][col]);
     const floatx4 u = b * (vv - alpha * r);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) m[i] = alpha * m[i] + sk[t][rg + RG * i] * u;
     const size_t tu = (static_cast<size_t>(n) * Tv + t) * Hv + h;
     if (rg == 0) {
       const floatx4 ov = scale * (alpha * p + kq * u);
-      *reinterpret_cast<typename Vec4<T>::type*>(o + tu * DV + 4 * cg) = pack4<T>(ov[0], ov[1], ov[2], ov[3]);
+      *reinterpret_cast<typename Vec4<T>::type*>(o + tu * DV + col) = pack4<T>(ov[0], ov[1], ov[2], ov[3]);
     }
     if (token_states) {
       float* ts = token_states + tu * DK * DV;
 #pragma unroll
       for (int i = 0; i < RPT; ++i)
-        __builtin_nontemporal_store(m[i], reinterpret_cast<floatx4*>(ts + static_cast<size_t>(rg + RG * i) * DV + 4 * cg));
+        __builtin_nontemporal_store(m[i], reinterpret_cast<floatx4*>(ts + static_cast<size_t>(rg + RG * i) * DV + col));
     }
   }
   // Streaming stores: the state is not read again until the next call (as in
@@ -137,7 +123,7 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_kernel(
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
       __builtin_nontemporal_store(m[i], reinterpret_cast<floatx4*>(state_out + sbase +
-                                                                    static_cast<size_t>(rg + RG * i) * DV + 4 * cg));
+                                                                    static_cast<size_t>(rg + RG * i) * DV + col));
   }
 }
 
