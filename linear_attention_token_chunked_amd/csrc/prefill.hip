@@ -628,6 +628,16 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
   // next to K M which takes the same operands; with two, holding it until
   // seg 2 would exceed the register budget, and seg 2 forms it instead.
   constexpr bool QM_EARLY = NTW == 1 && !OUTW;
+  // Where the consumers copy a chunk's output rows from LDS to HBM.  With two
+  // state tiles per wave, segment 1 (K M and Z only) ends before the
+  // producers' and leaves the consumers idle at its barrier, while segment 3
+  // is the longest of the chunk; so the rows of chunk c go out at the end of
+  // the consumers' segment 1 of chunk c + 1 (their LDS tile, in the spent V
+  // tile of c's stage, is refilled only in segment 2 of chunk c + 1), and the
+  // last chunk's after the loop: 9 % off the 128-column launches, the same
+  // results.  With one tile per wave, segment 1 also forms (Q M)^T and has no
+  // slack; the rows go out at the start of segment 3 of the same chunk.
+  constexpr bool ROWS_NEXT = !OUTW && !SAVE && !QM_EARLY;
   frag* sMx = reinterpret_cast<frag*>(smem + L::oMx) + cw * KGK * 64;  // this column tile's exchange slots
   frag* sUx = reinterpret_cast<frag*>(smem + L::oUx) + cw * KGC * 64;
   // The state as matrix-core operands (bf16-rounded for bf16 inputs); with
@@ -876,7 +886,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
     return v;
   };
   auto cons_seg3 = [&](int c, int s) __attribute__((always_inline)) {
-    if constexpr (!OUTW && !SAVE) o_rows_out(c, s);
+    if constexpr (!OUTW && !SAVE && !ROWS_NEXT) o_rows_out(c, s);
     const unsigned char* S = stage(s);
     const int olane = opaque_lane();
     const T* sK = reinterpret_cast<const T*>(S + L::sK);
@@ -961,7 +971,8 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
   // live at the same time) that execute the same sequence of barriers.  With
   // a double-buffered stage, iteration c runs three segments:
   //            producers                              consumers (chunk c)
-  //   seg 1    inverses, P and -A of chunk c          Y = K M, Z, (Q M)^T
+  //   seg 1    inverses, P and -A of chunk c          Y = K M, Z, (Q M)^T; chunk c - 1's
+  //                                                   output rows to HBM (ROWS_NEXT)
   //   seg 2    K, Q, V, gates of chunk c + 1;         U, O
   //            loads of chunk c + 2
   //   seg 3    Gram products of chunk c + 1           state update
@@ -1046,11 +1057,17 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
       for (int c = 0; c < nch; ++c) {
         if constexpr (SAVE && !OUTW) save_state(c);
         cons_seg1(c & 1);
+        if constexpr (ROWS_NEXT) {
+          if (c > 0) o_rows_out(c - 1, (c - 1) & 1);
+        }
         lds_barrier();
         cons_seg2(c, c & 1);
         lds_barrier();
         cons_seg3(c, c & 1);
         lds_barrier();
+      }
+      if constexpr (ROWS_NEXT) {
+        if (nch > 0) o_rows_out(nch - 1, (nch - 1) & 1);
       }
     } else {
       for (int c = 0; c < nch; ++c) {
