@@ -634,8 +634,8 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
   // is the longest of the chunk; so the rows of chunk c go out at the end of
   // the consumers' segment 1 of chunk c + 1 (their LDS tile, in the spent V
   // tile of c's stage, is refilled only in segment 2 of chunk c + 1), and the
-  // last chunk's after the loop: 9 % off the 128-column launches, the same
-  // results.  With one tile per wave, segment 1 also forms (Q M)^T and has no
+  // last chunk's after the loop: 4 % off the packed 64-sequence launch, 9 %
+  // off the segmented long row, the same results.  With one tile per wave, segment 1 also forms (Q M)^T and has no
   // slack; the rows go out at the start of segment 3 of the same chunk.
   constexpr bool ROWS_NEXT = !OUTW && !SAVE && !QM_EARLY;
   frag* sMx = reinterpret_cast<frag*>(smem + L::oMx) + cw * KGK * 64;  // this column tile's exchange slots
