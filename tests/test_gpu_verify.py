@@ -1,7 +1,6 @@
 """GPU parity of gdn_decode_verify (multi-token verify from a live state) against the fp64 oracle,
 through the C ABI, and its agreement with repeated gdn_decode_step calls."""
 
-import numpy as np
 import pytest
 import torch
 
@@ -80,30 +79,31 @@ def test_verify_state_out_none_and_separate(gdn):
     assert_close("separate state_out", f64(s_out), ref_states[:, -1], TOL[torch.float32])
 
 
-def test_verify_full_workload_sampled_units(gdn):
-    """256 sequences x 32 value heads, 4 drafted tokens from a live 512 MiB state; oracle on 24 sampled units."""
+def test_verify_full_workload_whole_tensors(gdn, oracle_pool):
+    """256 sequences x 32 value heads, 4 drafted tokens from a live 512 MiB state, updated in place: every
+    element of o for every token and of the state after the last token against four oracle decode steps
+    per sequence (a verify call is that many consecutive decode steps), whole tensors and every
+    (sequence, value head) unit."""
+    from oracle.parallel import decode_errors
+
     w = WORKLOADS["verify_n256_t4"]
-    flush(f"verify full {w}")
+    flush(f"verify full {w.name}: drawing inputs")
     inp = make_verify(w.N, w.steps, w.Hqk, w.Hv, w.dk, w.dv, w.dtype, seed=0)
     dev = to_dev(inp)
     state = dev["state"].clone()
     o = gdn.decode_verify(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], state)
     torch.cuda.synchronize()
-    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(state).all())
-    rng = np.random.default_rng(321)
-    units = [(0, 0), (w.N - 1, w.Hv - 1)] + [(int(a), int(b)) for a, b in
-                                             zip(rng.integers(0, w.N, 22), rng.integers(0, w.Hv, 22))]
-    rep = w.Hv // w.Hqk
-    got_o, ref_o, got_s, ref_s = [], [], [], []
-    for n, h in units:
-        hq = h // rep
-        sl_qk = lambda x: x[n:n + 1, :, hq:hq + 1]
-        sl_v = lambda x: x[n:n + 1, :, h:h + 1]
-        ro, rs = oracle_verify(sl_qk(inp["q"]), sl_qk(inp["k"]), sl_v(inp["v"]), sl_v(inp["g"]), sl_v(inp["beta"]),
-                               inp["state"][n:n + 1, h:h + 1])
-        got_o.append(f64(o[n, :, h]))
-        ref_o.append(ro[0, :, 0])
-        got_s.append(f64(state[n, h]))
-        ref_s.append(rs[0, -1, 0])
-    assert_close("o sampled", np.stack(got_o), np.stack(ref_o), TOL[torch.bfloat16])
-    assert_close("state sampled", np.stack(got_s), np.stack(ref_s), TOL[torch.bfloat16])
+    o_steps = o.transpose(0, 1).cpu()  # [Tv, N, Hv, dv], the decode driver's layout
+    fin = state.cpu()
+    steps_inp = {name: inp[name].transpose(0, 1) for name in ("q", "k", "v", "g", "beta")}
+    steps_inp["state"] = inp["state"]
+    flush("  oracle on the host")
+    err, secs = decode_errors(oracle_pool, steps_inp, o_steps, fin)
+    s = err.summary()
+    tol = TOL[torch.bfloat16]
+    flush(f"  {w.name}: rel-L2 o {s['rel_l2_o']:.3e} ({w.steps} tokens) state {s['rel_l2_state']:.3e} over "
+          f"{s['units']} units; worst unit o {s['worst_unit_o'][0]} {s['worst_unit_o'][1]:.3e}, state "
+          f"{s['worst_unit_state'][0]} {s['worst_unit_state'][1]:.3e} (oracle {secs:.1f} s)")
+    assert s["finite"] and s["units"] == w.N * w.Hv
+    assert s["rel_l2_o"] <= tol and s["rel_l2_state"] <= tol
+    assert s["worst_unit_o"][1] <= tol and s["worst_unit_state"][1] <= tol
