@@ -40,15 +40,16 @@ def test_short_conv_matches_oracle(gdn, dtype, B, T, H, hd, l2, packed):
 
 
 def test_short_conv_b4_t4096_qk_shape(gdn):
-    """q/k of prefill_b4_t4096 (4 x 4096 tokens, 16 heads x 128), L2-normalised; rows sampled."""
+    """q/k of prefill_b4_t4096 (4 x 4096 tokens, 16 heads x 128), L2-normalised: every element against the
+    oracle, as a whole tensor and per (token, head) row."""
     flush("short conv full 4x4096x16x128")
     inp = make_conv(4, 4096, 16, 128, "bf16", seed=0)
     y = gdn.short_conv(inp["x"].cuda(), inp["w"].cuda(), l2norm=True)
     torch.cuda.synchronize()
-    assert bool(torch.isfinite(y.float()).all())
-    norms = y.float().pow(2).sum(-1).sqrt()
-    assert float((norms - 1).abs().max()) < 1e-2
-    for b, t0 in [(0, 0), (3, 4090), (1, 1000), (2, 2047)]:
-        sl = slice(max(0, t0 - 3), t0 + 4)
-        ref = oracle_conv(inp["x"][b:b + 1, :t0 + 4], inp["w"], l2norm=True)[0, sl]
-        assert_close(f"y rows {b},{t0}", f64(y[b, sl]), ref, TOL[torch.bfloat16])
+    got = f64(y)
+    ref = oracle_conv(inp["x"], inp["w"], l2norm=True)
+    tol = TOL[torch.bfloat16]
+    err = assert_close("y", got, ref, tol)
+    per_row = np.sqrt(((got - ref) ** 2).sum(-1) / np.maximum((ref ** 2).sum(-1), 1e-300))
+    flush(f"  rel-L2 {err:.2e}, worst row {per_row.max():.2e}")
+    assert per_row.max() <= tol

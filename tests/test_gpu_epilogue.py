@@ -55,16 +55,19 @@ def test_norm_gate_in_place_and_shapes(gdn):
     assert_close("y", f64(dev_o), oracle_norm_gate(o, z, inp["w"]), TOL[torch.bfloat16])
 
 
-def test_norm_gate_full_prefill_output_sampled(gdn):
-    """The output of prefill_b4_t4096 (4 x 4096 tokens x 16 heads x 128), rows sampled for the oracle."""
+def test_norm_gate_full_prefill_output(gdn):
+    """The output of prefill_b4_t4096 (4 x 4096 tokens x 16 heads x 128 = 262144 rows): every element against
+    the oracle, as a whole tensor and row by row."""
     rows, dv = 4 * 4096 * 16, 128
     flush(f"norm gate full rows={rows}")
     inp = make_epilogue(rows, dv, "bf16", seed=0)
     dev = to_dev(inp)
     y = gdn.output_norm_gate(dev["o"], dev["z"], dev["w"])
     torch.cuda.synchronize()
-    assert bool(torch.isfinite(y.float()).all())
-    rng = np.random.default_rng(5)
-    pick = np.concatenate([[0, rows - 1], rng.integers(0, rows, 2000)])
-    ref = oracle_norm_gate(inp["o"][pick], inp["z"][pick], inp["w"])
-    assert_close("y sampled", f64(y[torch.from_numpy(pick).cuda()]), ref, TOL[torch.bfloat16])
+    got = f64(y)
+    ref = oracle_norm_gate(inp["o"], inp["z"], inp["w"])
+    tol = TOL[torch.bfloat16]
+    err = assert_close("y", got, ref, tol)
+    per_row = np.sqrt(((got - ref) ** 2).sum(-1) / np.maximum((ref ** 2).sum(-1), 1e-300))
+    flush(f"  rel-L2 {err:.2e}, worst row {per_row.max():.2e}")
+    assert per_row.max() <= tol
