@@ -3,7 +3,8 @@
 TEST INFRASTRUCTURE ONLY, like the rest of ``oracle/``: only ``tests/``,
 ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
 use it.  It holds none of the mixer's arithmetic: every result comes from
-``recurrent`` and ``decode_step`` in ``gdn_oracle.py``; this module only cuts a
+``recurrent`` and ``decode_step`` in ``gdn_oracle.py`` and ``recurrent_grads`` in
+``backward.py``; this module only cuts a
 workload into independent pieces, runs the oracle on them in forked worker
 processes and measures how far a candidate result is from the oracle's.
 
@@ -30,9 +31,10 @@ import time
 
 import numpy as np
 
+from .backward import recurrent_grads
 from .gdn_oracle import decode_step, recurrent
 
-__all__ = ["host_workers", "make_pool", "prefill_errors", "decode_errors", "Errors"]
+__all__ = ["host_workers", "grad_workers", "make_pool", "prefill_errors", "decode_errors", "bwd_errors", "Errors", "GRADS"]
 
 
 def host_workers():
@@ -43,6 +45,14 @@ def host_workers():
     if share.isdigit() and int(share) > 0:
         n = min(n, int(share))
     return max(1, n)
+
+
+def grad_workers():
+    """Worker count for pieces that run the autograd oracle (recurrent_grads): its first backward
+    pass makes torch ask the GPU runtime how many devices there are, which opens the GPU in that
+    process; at most 14, so that with the caller such a pool stays within the 16 processes a GPU
+    host admits with the GPU open."""
+    return max(1, min(14, host_workers() - 2))
 
 
 def _worker_init():
@@ -79,23 +89,25 @@ def _unpack(p):
 
 
 class Errors:
-    """Sums of squares of (candidate - oracle) and of the oracle, whole-tensor and per unit."""
+    """Sums of squares of (candidate - oracle) and of the oracle, whole-tensor and per unit, for each
+    named result (o and the final state; or the gradients)."""
 
-    def __init__(self):
-        self.d = {"o": 0.0, "state": 0.0}
-        self.r = {"o": 0.0, "state": 0.0}
-        self.unit = {"o": {}, "state": {}}  # (sequence, value head) -> relative L2
+    def __init__(self, keys=("o", "state")):
+        self.keys = tuple(keys)
+        self.d = {key: 0.0 for key in self.keys}
+        self.r = {key: 0.0 for key in self.keys}
+        self.unit = {key: {} for key in self.keys}  # unit -> relative L2
         self.finite = True
         self.units = 0
 
     def add(self, res):
-        for key in ("o", "state"):
+        for key in self.keys:
             for unit, (d, r) in res[key].items():
                 self.d[key] += d
                 self.r[key] += r
                 self.unit[key][unit] = np.sqrt(d / r) if r > 0 else np.sqrt(d)
         self.finite &= res["finite"]
-        self.units += len(res["o"])
+        self.units += len(res[self.keys[0]])
 
     def rel(self, key):
         return float(np.sqrt(self.d[key] / self.r[key])) if self.r[key] > 0 else float(np.sqrt(self.d[key]))
@@ -215,4 +227,81 @@ def decode_errors(pool, inp, o_steps, final_state, scale=1.0):
     t0 = time.perf_counter()
     for res in pool.imap_unordered(_decode_piece, pieces(), chunksize=4):
         err.add(res)
+    return err, time.perf_counter() - t0
+
+
+# ---------------------------------------------------------------- backward
+GRADS = ("dq", "dk", "dv", "dg", "dbeta", "d_initial_state")
+
+
+def _bwd_piece(args):
+    """Worker: the autograd oracle's gradients of one (sequence, query/key head) piece; error sums
+    against the candidate's.  dq and dk are one unit per (sequence, query/key head) (summed over its
+    value heads); the other gradients one unit per (sequence, value head)."""
+    import torch
+
+    torch.set_num_threads(1)
+    n, hq, heads, q, k, v, g, beta, d_o, s0, dfin, cand, scale = args
+    q, k, v, g, beta, d_o = (_unpack(x) for x in (q, k, v, g, beta, d_o))
+    s0 = _unpack(s0) if s0 is not None else None
+    dfin = _unpack(dfin) if dfin is not None else None
+    cand = {key: (_unpack(x) if x is not None else None) for key, x in cand.items()}
+    ref = recurrent_grads(q[None, :, None], k[None, :, None], v[None], g[None], beta[None], d_o[None],
+                          initial_state=None if s0 is None else s0[None],
+                          d_final=None if dfin is None else dfin[None], scale=scale)
+    res = {key: {} for key in GRADS}
+    res["finite"] = all(bool(np.all(np.isfinite(x))) for x in cand.values() if x is not None)
+    res["dq"][(n, hq)] = _sq(cand["dq"], ref["dq"][0, :, 0])
+    res["dk"][(n, hq)] = _sq(cand["dk"], ref["dk"][0, :, 0])
+    for i, h in enumerate(heads):
+        for key in ("dv", "dg", "dbeta"):
+            res[key][(n, h)] = _sq(cand[key][:, i], ref[key][0, :, i])
+        if cand["d_initial_state"] is not None:
+            res["d_initial_state"][(n, h)] = _sq(cand["d_initial_state"][i], ref["d_initial_state"][0, i])
+    return res
+
+
+def bwd_errors(pool, inp, cot, grads, scale=1.0, progress=None):
+    """Whole-workload error of a backward result against the autograd oracle (``recurrent_grads``).
+
+    ``inp``: the forward's CPU input dict; ``cot``: d_o [B, T, Hv, dv] and d_final [N, Hv, dk, dv]
+    or None; ``grads``: the candidate's dict (dq, dk, dv, dg, dbeta, d_initial_state or None);
+    ``progress(done, total)``, if given, is called as pieces finish.
+    Returns (Errors over GRADS, wall seconds)."""
+    q, k, v, g, beta = (inp[x] for x in ("q", "k", "v", "g", "beta"))
+    S0, cu = inp.get("initial_state"), inp.get("cu_seqlens")
+    d_o, dfin = cot["d_o"], cot.get("d_final")
+    B, T, Hqk, _ = q.shape
+    Hv = v.shape[2]
+    rep = Hv // Hqk
+    cpu = {key: (x.detach().cpu() if x is not None else None) for key, x in grads.items()}
+    if cu is not None:
+        cu = [int(x) for x in cu]
+        seqs = [(0, cu[i], cu[i + 1]) for i in range(len(cu) - 1)]
+    else:
+        seqs = [(b, 0, T) for b in range(B)]
+
+    def pieces():
+        order = sorted(range(len(seqs)), key=lambda i: seqs[i][1] - seqs[i][2])  # longest first
+        for n in order:
+            b, s, e = seqs[n]
+            for hq in range(Hqk):
+                hs = slice(hq * rep, (hq + 1) * rep)
+                cand = {"dq": _pack(cpu["dq"][b, s:e, hq]), "dk": _pack(cpu["dk"][b, s:e, hq])}
+                for key in ("dv", "dg", "dbeta"):
+                    cand[key] = _pack(cpu[key][b, s:e, hs])
+                dh0 = cpu.get("d_initial_state")
+                cand["d_initial_state"] = _pack(dh0[n, hs]) if dh0 is not None else None
+                yield (n, hq, list(range(hq * rep, (hq + 1) * rep)), _pack(q[b, s:e, hq]), _pack(k[b, s:e, hq]),
+                       _pack(v[b, s:e, hs]), _pack(g[b, s:e, hs]), _pack(beta[b, s:e, hs]), _pack(d_o[b, s:e, hs]),
+                       _pack(S0[n, hs]) if S0 is not None else None,
+                       _pack(dfin[n, hs]) if dfin is not None else None, cand, scale)
+
+    err = Errors(GRADS)
+    total = len(seqs) * Hqk
+    t0 = time.perf_counter()
+    for done, res in enumerate(pool.imap_unordered(_bwd_piece, pieces(), chunksize=1), 1):
+        err.add(res)
+        if progress:
+            progress(done, total)
     return err, time.perf_counter() - t0

@@ -20,18 +20,23 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     # Worker processes for the fp64 oracle over whole full-size workloads.  They are forked here,
     # before any test touches the GPU (a process that has initialised HIP must not fork).
-    config._oracle_pool = None
+    # A second, smaller pool runs the autograd oracle of the backward: torch's autograd engine asks the
+    # GPU runtime for its device count on its first backward pass, which opens the GPU in that worker,
+    # and a GPU machine admits at most 16 processes with the GPU open (this one and the workers).
+    config._oracle_pool = config._oracle_grad_pool = None
     if not _gpu_tests_deselected(config):
-        from oracle.parallel import make_pool
+        from oracle.parallel import grad_workers, make_pool
 
         config._oracle_pool = make_pool()
+        config._oracle_grad_pool = make_pool(grad_workers())
 
 
 def pytest_unconfigure(config):
-    pool = getattr(config, "_oracle_pool", None)
-    if pool is not None:
-        pool.terminate()
-        pool.join()
+    for name in ("_oracle_pool", "_oracle_grad_pool"):
+        pool = getattr(config, name, None)
+        if pool is not None:
+            pool.terminate()
+            pool.join()
 
 
 @pytest.fixture(scope="session")
@@ -42,4 +47,15 @@ def oracle_pool(request):
 
         # only reached when the marker expression deselected the GPU tests: no GPU in this process
         pool = request.config._oracle_pool = make_pool(2)
+    return pool
+
+
+@pytest.fixture(scope="session")
+def oracle_grad_pool(request):
+    pool = request.config._oracle_grad_pool
+    if pool is None:
+        from oracle.parallel import make_pool
+
+        # only reached when the marker expression deselected the GPU tests: no GPU in this process
+        pool = request.config._oracle_grad_pool = make_pool(2)
     return pool

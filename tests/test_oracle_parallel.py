@@ -1,17 +1,18 @@
 """The parallel oracle driver (oracle/parallel.py) that the full-size GPU parity tests use.
 
 It must return the oracle's own result as error-free, find a planted error in the
-one unit that holds it, transport bf16 values exactly, and reproduce the serial
-oracle's decode steps.  CPU only.
+one unit that holds it, transport bf16 values exactly, reproduce the serial
+oracle's decode steps, and cut the backward into pieces whose gradients equal the
+whole-input autograd oracle's (dq and dk summed over grouped value heads).  CPU only.
 """
 
 import numpy as np
 import torch
 
-from oracle import decode_step, recurrent
-from oracle.parallel import _pack, _unpack, decode_errors, prefill_errors
+from oracle import decode_step, recurrent, recurrent_grads
+from oracle.parallel import GRADS, _pack, _unpack, bwd_errors, decode_errors, prefill_errors
 
-from linear_attention_token_chunked_amd.inputs import make_decode, make_prefill
+from linear_attention_token_chunked_amd.inputs import make_cotangents, make_decode, make_prefill
 
 
 def _as_candidate(x, dtype):
@@ -68,3 +69,25 @@ def test_decode_driver_equals_serial_steps(oracle_pool):
     bad[4, 2, 3] = 0.0  # the last step of unit (2, 3)
     err, _ = decode_errors(oracle_pool, inp, bad, _as_candidate(s, torch.float32))
     assert err.worst("o")[0] == (2, 3)
+
+
+def test_bwd_driver_equals_whole_input_autograd(oracle_grad_pool):
+    """Packed sequences (one empty) with two value heads per query/key head: the pieces' gradients
+    equal those of one autograd pass over the whole input, and a planted error lands in its unit."""
+    lens = [9, 0, 40, 17]
+    inp = make_prefill(1, 0, 2, 4, 8, 8, "fp32", init_state=True, lengths=lens, seed=6)
+    cot = make_cotangents(1, sum(lens), 4, 8, len(lens), 8, "fp32", seed=6)
+    ref = recurrent_grads(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], cot["d_o"], inp["initial_state"],
+                          cot["d_final"], inp["cu_seqlens"].numpy(), 0.7)
+    cand = {key: _as_candidate(ref[key], torch.float32) for key in GRADS}
+    err, _ = bwd_errors(oracle_grad_pool, inp, cot, cand, scale=0.7)
+    assert err.finite and err.units == 4 * 2  # (sequence, query/key head) pieces
+    for key in GRADS:
+        assert err.rel(key) < 1e-6, key
+    assert len(err.unit["dv"]) == 4 * 4 and len(err.unit["dq"]) == 4 * 2
+    bad = dict(cand)
+    bad["dg"] = cand["dg"].clone()
+    bad["dg"][0, 9 + 30, 3] += 5.0  # sequence 2 covers tokens 9..48: unit (2, 3)
+    err, _ = bwd_errors(oracle_grad_pool, inp, cot, bad, scale=0.7)
+    assert err.worst("dg")[0] == (2, 3) and err.unit["dg"][(2, 2)] < 1e-6
+    assert err.rel("dq") < 1e-6
