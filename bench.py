@@ -239,7 +239,8 @@ def bench_prefill(name, gdn, torch, steps, warmup, keep=False, repeats=3, flushe
     res = {
         "workload": name, "tokens": tokens, "B": B, "T": T, "num_seqs": N, "Hqk": Hqk, "Hv": Hv, "dk": dk, "dv": dv,
         "chunk": w.chunk, "ms_per_step": wall / steps * 1e3, "kernel_ms_mean": kern_ms,
-        "kernel_ms_p10": per[len(per) // 10], "kernel_ms_p90": per[(len(per) * 9) // 10], "cold_ms": cold_ms,
+        "kernel_ms_p10": per[len(per) // 10], "kernel_ms_median": per[len(per) // 2],
+        "kernel_ms_p90": per[(len(per) * 9) // 10], "cold_ms": cold_ms,
         "repeats_kernel_ms": [round(x, 4) for x in spread],
         "repeat_spread_pct": round(100 * (max(spread) - min(spread)) / min(spread), 2),
         "flushed_kernel_ms_median": fl[len(fl) // 2],
