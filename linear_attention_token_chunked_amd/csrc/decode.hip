@@ -13,6 +13,7 @@
 // with 16-byte loads, keeps it in registers across the dk-reduction, and
 // writes it back.
 #include "device_common.hpp"
+#include "lane_sums.hpp"
 #include "launch.hpp"
 
 namespace gdn {
@@ -26,8 +27,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
     T* __restrict__ o, int Hqk, int Hv, float scale) {
   // Each wavefront owns a block of DV / 4 state columns over all DK rows, so the
-  // reductions over the key dimension stay inside the wavefront (lane
-  // shuffles).  A thread holds rows rg, rg + RG, ... of four columns, so a load
+  // reductions over the key dimension stay inside the wavefront (DPP and row
+  // swaps, no LDS).  A thread holds rows rg, rg + RG, ... of four columns, so a load
   // instruction covers RG consecutive rows.
   constexpr int NWAVE = kDecodeThreads / 64;
   constexpr int CPW = DV / NWAVE;  // state columns per wavefront
@@ -77,14 +78,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     kq += ki * qi;
   }
   // Sum over the wavefront's row groups: every lane ends with the full sums of its columns.
-#pragma unroll
-  for (int off = TPR; off < 64; off <<= 1) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      r[c] += __shfl_xor(r[c], off);
-      p[c] += __shfl_xor(p[c], off);
-    }
-    kq += __shfl_xor(kq, off);
+  {
+    float x9[9] = {r[0], r[1], r[2], r[3], p[0], p[1], p[2], p[3], kq};
+    xor_sums9<TPR>(x9);
+    r = floatx4{x9[0], x9[1], x9[2], x9[3]};
+    p = floatx4{x9[4], x9[5], x9[6], x9[7]};
+    kq = x9[8];
   }
   floatx4 u;
   u[0] = b * (v0 - alpha * r[0]);
@@ -99,7 +98,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   // (non-temporal loads, by contrast, are slower).
 #pragma unroll
   for (int i = 0; i < RPT; ++i)
-    __builtin_nontemporal_store(alpha * m[i] + sk[rg + RG * i] * u,
+    __builtin_nontemporal_store(decay_write(m[i], alpha, sk[rg + RG * i], u),
                                 reinterpret_cast<floatx4*>(M + static_cast<size_t>(rg + RG * i) * DV + col));
   if (rg == 0) {
     const floatx4 ov = scale * (alpha * p + kq * u);

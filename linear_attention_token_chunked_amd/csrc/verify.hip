@@ -16,6 +16,7 @@
 // after its last accepted token).  Like the single step it is bound by HBM
 // bandwidth, with Tv times the tokens per state pass.
 #include "device_common.hpp"
+#include "lane_sums.hpp"
 #include "launch.hpp"
 
 namespace gdn {
@@ -25,7 +26,7 @@ constexpr int kVerifyThreads = 256;
 
 // Each wavefront owns a block of DV / 4 state columns over all DK rows, so the
 // reductions over the key dimension (M^T k, M^T q, k . q) stay inside the
-// wavefront (lane shuffles) and the token loop runs without a workgroup
+// wavefront (DPP and row swaps, no LDS) and the token loop runs without a workgroup
 // barrier.  A thread holds rows rg, rg + RG, ... of four columns, so a load
 // instruction covers RG consecutive rows.
 template <class T, int DK, int DV>
@@ -90,20 +91,18 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_kernel(
       kq += ki * qi;
     }
     // Sum over the wavefront's row groups: every lane ends with the full sums of its columns.
-#pragma unroll
-    for (int off = TPR; off < 64; off <<= 1) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        r[c] += __shfl_xor(r[c], off);
-        p[c] += __shfl_xor(p[c], off);
-      }
-      kq += __shfl_xor(kq, off);
+    {
+      float x9[9] = {r[0], r[1], r[2], r[3], p[0], p[1], p[2], p[3], kq};
+      xor_sums9<TPR>(x9);
+      r = floatx4{x9[0], x9[1], x9[2], x9[3]};
+      p = floatx4{x9[4], x9[5], x9[6], x9[7]};
+      kq = x9[8];
     }
     const float alpha = sab[t][0], b = sab[t][1];
     const floatx4 vv = *reinterpret_cast<const floatx4*>(&sv[t][col]);
     const floatx4 u = b * (vv - alpha * r);
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) m[i] = alpha * m[i] + sk[t][rg + RG * i] * u;
+    for (int i = 0; i < RPT; ++i) m[i] = decay_write(m[i], alpha, sk[t][rg + RG * i], u);
     const size_t tu = (static_cast<size_t>(n) * Tv + t) * Hv + h;
     if (rg == 0) {
       const floatx4 ov = scale * (alpha * p + kq * u);

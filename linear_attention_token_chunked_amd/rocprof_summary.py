@@ -35,8 +35,8 @@ CSRC = os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc")
 SOURCES = {
     "prefill": ["prefill.hip", "seg.hip", "device_common.hpp", "plan.cpp"],
     "bwd": ["prefill.hip", "bwd.hip", "device_common.hpp", "plan.cpp"],
-    "decode": ["decode.hip"],
-    "verify": ["verify.hip"],
+    "decode": ["decode.hip", "lane_sums.hpp"],
+    "verify": ["verify.hip", "lane_sums.hpp"],
     "epilogue": ["epilogue.hip"],
     "short_conv": ["conv.hip"],
 }
