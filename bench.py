@@ -20,8 +20,10 @@ inputs resident in HBM.  The same JSON line also carries
                 heads (512 MiB fp32 state): algorithmic GB/s against 8 TB/s;
   verify        gdn_decode_verify, 4 drafted tokens per sequence from the same
                 kind of live state: algorithmic GB/s against 8 TB/s;
-  epilogue      gdn_output_norm_gate over a 4 x 4096 x 16-head output: GB/s against 8 TB/s;
-  short_conv    gdn_short_conv with L2 norm over that workload's q: GB/s against 8 TB/s;
+  epilogue      gdn_output_norm_gate over an output of the headline's tokens (210,119 tokens x 32
+                value heads): GB/s against 8 TB/s;
+  short_conv    gdn_short_conv with L2 norm over a q of the headline's tokens and sequence starts
+                (16 heads): GB/s against 8 TB/s;
   bwd           gdn_bwd_chunked (all gradients) over the 4 x 4096 x 16-head prefill:
                 algorithmic GB/s against 8 TB/s (its 197 flops per algorithmic
                 byte sit below the chip's ridge), and its dense-tile TFLOP/s;
@@ -51,8 +53,8 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-EPILOGUE_WORKLOAD = "epilogue_b4_t4096"
-SHORT_CONV_WORKLOAD = "short_conv_q_b4_t4096"
+EPILOGUE_WORKLOAD = "epilogue_varlen_64"
+SHORT_CONV_WORKLOAD = "short_conv_q_varlen_64"
 
 
 # ------------------------------------------------------------------ algorithmic work
@@ -316,12 +318,29 @@ def bench_verify(gdn, torch, steps=20):
     }
 
 
-def bench_epilogue(gdn, torch, steps=50):
-    """Output epilogue (zero-centred RMSNorm + sigmoid gate) over the prefill_b4_t4096 output."""
-    from linear_attention_token_chunked_amd.inputs import make_epilogue
+def headline_lengths():
+    """The packed sequence lengths of the headline workload (its inputs' first draw at seed 0)."""
+    import numpy as np
 
-    rows, dv = 4 * 4096 * 16, 128
-    dev = {k: v.cuda() for k, v in make_epilogue(rows, dv, "bf16").items()}
+    from linear_attention_token_chunked_amd.inputs import WORKLOADS, packed_lengths
+
+    return packed_lengths(np.random.default_rng(0), WORKLOADS["varlen_64"].num_packed)
+
+
+def gpu_normal(torch, shape, dtype, seed, scale=1.0):
+    """Seeded N(0, scale^2) draws made on the GPU (tensors too large to draw on the host quickly)."""
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    x = torch.randn(shape, generator=gen, device="cuda", dtype=dtype)
+    return x.mul_(scale) if scale != 1.0 else x
+
+
+def bench_epilogue(gdn, torch, steps=20):
+    """Output epilogue (zero-centred RMSNorm + sigmoid gate) over an output of the headline's tokens:
+    o, z ~ N(0, 1) [tokens x 32 value heads, 128] bf16, weight ~ 0.1 N(0, 1)."""
+    tokens, hv, dv = int(headline_lengths().sum()), 32, 128
+    rows = tokens * hv
+    dev = {"o": gpu_normal(torch, (rows, dv), torch.bfloat16, 11), "z": gpu_normal(torch, (rows, dv), torch.bfloat16, 12),
+           "w": gpu_normal(torch, (dv,), torch.float32, 13, 0.1)}
     y = torch.empty_like(dev["o"])
 
     def step():
@@ -332,7 +351,8 @@ def bench_epilogue(gdn, torch, steps=50):
     nbytes = 3 * rows * dv * dev["o"].element_size() + dv * 4
     gbps = nbytes / (us * 1e-6) / 1e9
     return {
-        "workload": EPILOGUE_WORKLOAD, "what": "prefill_b4_t4096 output (262144 rows x 128, bf16)", "rows": rows,
+        "workload": EPILOGUE_WORKLOAD, "what": f"output of the headline's tokens ({rows} rows x 128, bf16)",
+        "rows": rows,
         "dv": dv, "us_per_call_mean": us, "bytes_per_call": nbytes, "GBps": gbps,
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(gbps / PEAK_HBM_GBPS, 4),
@@ -340,25 +360,28 @@ def bench_epilogue(gdn, torch, steps=50):
     }
 
 
-def bench_short_conv(gdn, torch, steps=50):
-    """Pre-mixer short convolution + per-head L2 norm over q (or k) of prefill_b4_t4096."""
-    from linear_attention_token_chunked_amd.inputs import make_conv
+def bench_short_conv(gdn, torch, steps=20):
+    """Pre-mixer short convolution + per-head L2 norm over a q of the headline's tokens, restarting at
+    its sequence starts: x ~ N(0, 1) [1, tokens, 16, 128] bf16, taps ~ N(0, 1) / 2."""
+    import numpy as np
 
-    B, T, H, hd = 4, 4096, 16, 128
-    inp = make_conv(B, T, H, hd, "bf16")
-    x, w = inp["x"].cuda(), inp["w"].cuda()
+    lengths = headline_lengths()
+    T, H, hd = int(lengths.sum()), 16, 128
+    x = gpu_normal(torch, (1, T, H, hd), torch.bfloat16, 21)
+    w = gpu_normal(torch, (H * hd, 4), torch.float32, 22, 0.5)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32, device="cuda")
     y = torch.empty_like(x)
 
     def step():
-        gdn.short_conv(x, w, l2norm=True, out=y)
+        gdn.short_conv(x, w, cu_seqlens=cu, l2norm=True, out=y)
 
     wall, mean_ms, per = time_launches(step, steps, 5, torch)
     us = mean_ms * 1e3
-    nbytes = 2 * x.numel() * x.element_size() + w.numel() * 4
+    nbytes = 2 * x.numel() * x.element_size() + w.numel() * 4 + cu.numel() * 4
     gbps = nbytes / (us * 1e-6) / 1e9
     return {
         "workload": SHORT_CONV_WORKLOAD,
-        "what": "q of prefill_b4_t4096 (4 x 4096 tokens x 16 heads x 128, bf16), width 4, L2 norm",
+        "what": f"q of the headline's tokens ({T} tokens, 64 sequences, 16 heads x 128, bf16), width 4, L2 norm",
         "us_per_call_mean": us, "bytes_per_call": nbytes, "GBps": gbps,
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(gbps / PEAK_HBM_GBPS, 4),

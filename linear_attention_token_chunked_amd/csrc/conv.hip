@@ -31,12 +31,13 @@ __device__ __forceinline__ float row16_sum(float x) {
 }
 
 // A 16-lane group walks a run of kRun consecutive tokens of one head: it
-// loads the head's taps once and slides a window of the last W token rows
-// through registers.  A wavefront's four groups take four consecutive heads of
+// takes the head's taps from LDS (loaded once per workgroup) and slides a
+// window of the last W token rows through registers.  A wavefront's four groups take four consecutive heads of
 // one run, and the workgroup's four wavefronts take four consecutive runs of
 // the same heads: a wavefront hands the last W - 1 rows of its run to the next
 // one through LDS, so only the first run of a workgroup loads the rows before
-// it from memory again (3 of every 32 rows instead of 3 of every 8).
+// it again (3 of every 32 rows instead of 3 of every 8), and those it finds in
+// its XCD's L2 (see the workgroup numbering in the kernel).
 constexpr int kRun = 8;
 constexpr int kWaves = kConvThreads / 64;
 
@@ -44,35 +45,44 @@ template <class T, int HD, bool L2>
 __global__ __launch_bounds__(kConvThreads) void conv_kernel(const T* __restrict__ x, const float* __restrict__ w,
                                                             T* __restrict__ y, const int32_t* __restrict__ cu,
                                                             int num_seqs, int seqlen, int heads, int tokens,
-                                                            int head_blocks, float eps) {
+                                                            int head_blocks, int token_blocks, float eps) {
   constexpr int EPL = HD / 16;  // channels per lane
   constexpr int W = kConvWidth;
   static_assert(W == 4, "one 16-byte load of taps per channel");
   typedef T lane_vec __attribute__((ext_vector_type(EPL)));
   __shared__ lane_vec handoff[kWaves][W - 1][64];  // a wavefront's last W - 1 rows, lane by lane
-  const int lane = threadIdx.x & 63, lane16 = lane & 15, wave = threadIdx.x >> 6;
-  const int hb = blockIdx.x % head_blocks;
+  __shared__ floatx4 stap[4 * HD];                   // the taps of the workgroup's four heads
+  const int lane = threadIdx.x & 63, lane16 = lane & 15;
+  // (made uniform, so that the search for the sequence start below runs on scalar loads)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Workgroup -> (token block, head block).  With head_blocks dividing 8, workgroup ids 8 apart (one
+  // XCD) take consecutive token blocks of one head block, so the rows before a block, which the block
+  // before it loaded, are found in that XCD's L2; the 8 / head_blocks streams split the tokens in
+  // equal parts.  Otherwise: token block id / head_blocks.
+  int hb, tb;
+  if (8 % head_blocks == 0) {
+    const int x = blockIdx.x & 7, j = blockIdx.x >> 3, streams = 8 / head_blocks;
+    hb = x % head_blocks;
+    tb = j + (x / head_blocks) * ((token_blocks + streams - 1) / streams);
+  } else {
+    hb = blockIdx.x % head_blocks;
+    tb = blockIdx.x / head_blocks;
+  }
+  if (tb >= token_blocks) return;  // (whole workgroups)
   const int h = hb * 4 + (lane >> 4);
   const bool active = h < heads;  // (inactive groups still take part in the barrier)
-  const int t0 = (blockIdx.x / head_blocks) * (kWaves * kRun) + wave * kRun;
-  // the sequence of the run's first token, and where the next one starts
-  int start, next;
-  if (cu) {
-    int lo = 0, hi = num_seqs;  // the last n with cu[n] <= t0
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (cu[mid] <= t0) lo = mid; else hi = mid;
-    }
-    start = cu[lo];
-    next = cu[lo + 1];  // > t0 unless t0 is past the last token
-  } else {
-    start = t0 - t0 % seqlen;
-    next = start + seqlen;
-  }
+  const int t0 = tb * (kWaves * kRun) + wave * kRun;
   const int c0 = (active ? h : 0) * HD + lane16 * EPL;  // first channel of this lane
-  floatx4 taps[EPL];
+  // The taps of heads 4 hb .. 4 hb + 3, each channel's four loaded once per workgroup rather than once
+  // per wavefront (unconditional loads, clamped to the last channel), and stored to LDS only after the
+  // rows' loads are issued, so that the store's wait does not hold those back.
+  constexpr int TPT = 4 * HD / kConvThreads;  // tap vectors per thread
+  static_assert(4 * HD % kConvThreads == 0, "taps split evenly");
+  floatx4 tapr[TPT];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) taps[e] = *reinterpret_cast<const floatx4*>(w + (c0 + e) * W);
+  for (int j = 0; j < TPT; ++j)
+    tapr[j] = *reinterpret_cast<const floatx4*>(
+        w + static_cast<size_t>(min(hb * 4 * HD + static_cast<int>(threadIdx.x) + j * kConvThreads, heads * HD - 1)) * W);
   const T* xl = x + c0;  // this lane's channels of token 0
   T* yl = y + c0;
   const size_t tstride = static_cast<size_t>(heads) * HD;
@@ -88,9 +98,30 @@ __global__ __launch_bounds__(kConvThreads) void conv_kernel(const T* __restrict_
     for (int i = 0; i < W - 1; ++i)
       prev[i] = *reinterpret_cast<const lane_vec*>(xl + static_cast<size_t>(max(t0 - (W - 1) + i, 0)) * tstride);
   }
+  // The sequence of the run's first token, and where the next one starts.  The search waits on each
+  // of its reads, so it runs after the rows' loads are issued, on scalar loads (their own counter: it
+  // does not wait for the rows).
+  int start, next;
+  if (cu) {
+    int lo = 0, hi = num_seqs;  // the last n with cu[n] <= t0
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (cu[mid] <= t0) lo = mid; else hi = mid;
+    }
+    start = cu[lo];
+    next = cu[lo + 1];  // > t0 unless t0 is past the last token
+  } else {
+    start = t0 - t0 % seqlen;
+    next = start + seqlen;
+  }
+#pragma unroll
+  for (int j = 0; j < TPT; ++j) stap[threadIdx.x + j * kConvThreads] = tapr[j];
 #pragma unroll
   for (int i = 0; i < W - 1; ++i) handoff[wave][i][lane] = rows[kRun - (W - 1) + i];
   __syncthreads();
+  floatx4 taps[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) taps[e] = stap[(lane >> 4) * HD + lane16 * EPL + e];
   if (wave > 0) {
 #pragma unroll
     for (int i = 0; i < W - 1; ++i) prev[i] = handoff[wave - 1][i][lane];
@@ -149,8 +180,9 @@ __global__ __launch_bounds__(kConvThreads) void conv_kernel(const T* __restrict_
     }
 #pragma unroll
     for (int e = 0; e < EPL; e += 4)
-      *reinterpret_cast<typename Vec4<T>::type*>(yl + static_cast<size_t>(t) * tstride + e) =
-          pack4<T>(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+      // (streaming stores: the rows are read again only by the mixer, after much else)
+      __builtin_nontemporal_store(pack4<T>(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]),
+                                  reinterpret_cast<typename Vec4<T>::type*>(yl + static_cast<size_t>(t) * tstride + e));
   }
 }
 
@@ -158,16 +190,21 @@ template <class T, int HD>
 hipError_t launch(const ConvArgs& a, hipStream_t stream) {
   if (a.tokens == 0) return hipSuccess;
   const int head_blocks = (a.heads + 3) / 4;
-  const int64_t blocks = static_cast<int64_t>((a.tokens + kWaves * kRun - 1) / (kWaves * kRun)) * head_blocks;
+  const int token_blocks = (a.tokens + kWaves * kRun - 1) / (kWaves * kRun);
+  int64_t blocks = static_cast<int64_t>(token_blocks) * head_blocks;
+  if (8 % head_blocks == 0) {  // (see the kernel: 8 / head_blocks token streams, 8 ids per step)
+    const int streams = 8 / head_blocks;
+    blocks = 8 * static_cast<int64_t>((token_blocks + streams - 1) / streams);
+  }
   const dim3 grid(static_cast<unsigned>(blocks));
   if (a.l2norm)
     conv_kernel<T, HD, true><<<grid, dim3(kConvThreads), 0, stream>>>(
         static_cast<const T*>(a.x), a.weight, static_cast<T*>(a.y), a.cu_seqlens, a.num_seqs, a.seqlen, a.heads,
-        a.tokens, head_blocks, a.eps);
+        a.tokens, head_blocks, token_blocks, a.eps);
   else
     conv_kernel<T, HD, false><<<grid, dim3(kConvThreads), 0, stream>>>(
         static_cast<const T*>(a.x), a.weight, static_cast<T*>(a.y), a.cu_seqlens, a.num_seqs, a.seqlen, a.heads,
-        a.tokens, head_blocks, a.eps);
+        a.tokens, head_blocks, token_blocks, a.eps);
   return hipGetLastError();
 }
 

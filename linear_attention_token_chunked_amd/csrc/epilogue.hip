@@ -19,6 +19,11 @@ namespace gdn {
 namespace {
 
 constexpr int kEpiThreads = 256;
+// Rows per 16-lane group: a workgroup covers 16 kEpiRows consecutive rows, group g rows g, g + 16, ...
+// All of a lane's loads are issued before the first row is formed, and the rows go out with streaming
+// (non-temporal) stores: the output is read again only by the next layer, after much else.  Each lane
+// writes exactly the elements it read, so y may be o.
+constexpr int kEpiRows = 4;
 
 // Sum over the 16 lanes of a DPP row (lanes 16r .. 16r + 15).
 __device__ __forceinline__ float row16_sum(float x) {
@@ -34,44 +39,54 @@ __global__ __launch_bounds__(kEpiThreads) void norm_gate_kernel(const T* o, cons
                                                                 const float* __restrict__ w, T* y, int64_t rows,
                                                                 float eps) {
   constexpr int EPL = DV / 16;  // values per lane (16 lanes per row)
+  constexpr int R = kEpiRows;
   static_assert(EPL == 4 || EPL == 8, "dv of 64 or 128");
   const int lane16 = threadIdx.x & 15;
-  const int64_t row = (static_cast<int64_t>(blockIdx.x) * kEpiThreads + threadIdx.x) >> 4;
-  if (row >= rows) return;  // whole 16-lane groups leave together
-  typedef T lane_vec __attribute__((ext_vector_type(EPL)));  // a lane's run: one or two 16-byte pieces
+  typedef T lane_vec __attribute__((ext_vector_type(EPL)));
   typedef float lane_wvec __attribute__((ext_vector_type(EPL)));
-  const int64_t base = row * DV + lane16 * EPL;
-  const lane_vec o_in = *reinterpret_cast<const lane_vec*>(o + base);
-  const lane_vec z_in = *reinterpret_cast<const lane_vec*>(z + base);
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * (kEpiThreads / 16) * R + (threadIdx.x >> 4);
   const lane_wvec w_in = *reinterpret_cast<const lane_wvec*>(w + lane16 * EPL);
-  float ov[EPL], zv[EPL], wv[EPL];
+  lane_vec o_in[R], z_in[R];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    ov[e] = to_float(o_in[e]);
-    zv[e] = to_float(z_in[e]);
-    wv[e] = w_in[e];
-  }
-  float ss = 0.f;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) ss += ov[e] * ov[e];
-  ss = row16_sum(ss);
-  const float rinv = rsqrtf(ss * (1.f / DV) + eps);
-  float out[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    const float gate = 1.f / (1.f + expf(-zv[e]));
-    out[e] = gate * (ov[e] * rinv) * (1.f + wv[e]);
+  for (int i = 0; i < R; ++i) {  // (rows past the end read the last row: never stored)
+    const int64_t row = min(row0 + i * (kEpiThreads / 16), rows - 1);
+    o_in[i] = *reinterpret_cast<const lane_vec*>(o + row * DV + lane16 * EPL);
+    z_in[i] = *reinterpret_cast<const lane_vec*>(z + row * DV + lane16 * EPL);
   }
 #pragma unroll
-  for (int e = 0; e < EPL; e += 4)
-    *reinterpret_cast<typename Vec4<T>::type*>(y + base + e) = pack4<T>(out[e], out[e + 1], out[e + 2], out[e + 3]);
+  for (int i = 0; i < R; ++i) {
+    const int64_t row = row0 + i * (kEpiThreads / 16);
+    float ov[EPL], zv[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      ov[e] = to_float(o_in[i][e]);
+      zv[e] = to_float(z_in[i][e]);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) ss += ov[e] * ov[e];
+    ss = row16_sum(ss);
+    const float rinv = rsqrtf(ss * (1.f / DV) + eps);
+    float out[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float gate = 1.f / (1.f + expf(-zv[e]));
+      out[e] = gate * (ov[e] * rinv) * (1.f + w_in[e]);
+    }
+    if (row < rows) {
+      lane_vec yv;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) yv[e] = from_float<T>(out[e]);
+      __builtin_nontemporal_store(yv, reinterpret_cast<lane_vec*>(y + row * DV + lane16 * EPL));
+    }
+  }
 }
 
 template <class T, int DV>
 hipError_t launch(const EpilogueArgs& a, hipStream_t stream) {
   if (a.rows == 0) return hipSuccess;
-  const int64_t threads = a.rows * 16;
-  const dim3 grid(static_cast<unsigned>((threads + kEpiThreads - 1) / kEpiThreads));
+  const int64_t per_wg = kEpiThreads / 16 * kEpiRows;
+  const dim3 grid(static_cast<unsigned>((a.rows + per_wg - 1) / per_wg));
   norm_gate_kernel<T, DV><<<grid, dim3(kEpiThreads), 0, stream>>>(
       static_cast<const T*>(a.o), static_cast<const T*>(a.z), a.weight, static_cast<T*>(a.y), a.rows, a.eps);
   return hipGetLastError();

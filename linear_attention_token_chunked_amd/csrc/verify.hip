@@ -55,28 +55,53 @@ __global__ __launch_bounds__(kVerifyThreads) void verify_kernel(
   __shared__ float sv[kMaxVerifyTokens][DV];
   __shared__ float sab[kMaxVerifyTokens][2];  // alpha, beta per token
 
-  // The state slice first: these loads dominate the run time.
+  // The tokens' keys, queries and values first, as whole 16-byte pieces, one array per wavefront
+  // (unconditional loads, clamped to the last piece); then the state slice, whose loads dominate the
+  // run time; then the tokens into LDS, which waits only for the first loads, so that the barrier
+  // and the first products overlap the state's arrival.
+  constexpr int EPB = 16 / sizeof(T);  // elements per piece
+  constexpr int PMAX = (kMaxVerifyTokens * (DK > DV ? DK : DV) / EPB + 63) / 64;  // pieces per lane
+  typedef T piece_t __attribute__((ext_vector_type(16 / sizeof(T))));
+  const int wave = tid >> 6;
+  piece_t pc[PMAX];
+  float gb = 0.f;
+  {
+    const int D = wave == 2 ? DV : DK, rowlen = D / EPB, np = Tv * rowlen;
+#pragma unroll
+    for (int i = 0; i < PMAX; ++i) {
+      const int pi = min(lane + 64 * i, np - 1), t = pi / rowlen, e = (pi - t * rowlen) * EPB;
+      const T* src = wave == 0 ? k + ((static_cast<size_t>(n) * Tv + t) * Hqk + hq) * DK + e
+                   : wave == 1 ? q + ((static_cast<size_t>(n) * Tv + t) * Hqk + hq) * DK + e
+                               : v + ((static_cast<size_t>(n) * Tv + t) * Hv + h) * DV + e;
+      if (wave < 3) pc[i] = *reinterpret_cast<const piece_t*>(src);
+    }
+    if (wave == 3) {
+      const size_t tu = (static_cast<size_t>(n) * Tv + min(lane >> 1, Tv - 1)) * Hv + h;
+      gb = (lane & 1) ? beta[tu] : g[tu];
+    }
+  }
   const size_t sbase = static_cast<size_t>(unit) * DK * DV;
   floatx4 m[RPT];
 #pragma unroll
   for (int r = 0; r < RPT; ++r)
     m[r] = *reinterpret_cast<const floatx4*>(state_in + sbase + static_cast<size_t>(rg + RG * r) * DV + col);
-
-  // Every token's key, query, value and gates into LDS.
-  for (int i = tid; i < Tv * DK; i += kVerifyThreads) {
-    const int t = i / DK, c = i - t * DK;
-    const size_t row = (static_cast<size_t>(n) * Tv + t) * Hqk + hq;
-    sk[t][c] = to_float(k[row * DK + c]);
-    sq[t][c] = to_float(q[row * DK + c]);
-  }
-  for (int i = tid; i < Tv * DV; i += kVerifyThreads) {
-    const int t = i / DV, c = i - t * DV;
-    sv[t][c] = to_float(v[((static_cast<size_t>(n) * Tv + t) * Hv + h) * DV + c]);
-  }
-  if (tid < Tv) {
-    const size_t tu = (static_cast<size_t>(n) * Tv + tid) * Hv + h;
-    sab[tid][0] = expf(g[tu]);
-    sab[tid][1] = beta[tu];
+  {
+    const int D = wave == 2 ? DV : DK, rowlen = D / EPB, np = Tv * rowlen;
+    float* dst = wave == 0 ? &sk[0][0] : wave == 1 ? &sq[0][0] : &sv[0][0];
+    const int ld = wave == 2 ? DV : DK;
+    if (wave < 3) {
+#pragma unroll
+      for (int i = 0; i < PMAX; ++i) {
+        const int pi = lane + 64 * i;
+        if (pi < np) {
+          const int t = pi / rowlen, e = (pi - t * rowlen) * EPB;
+#pragma unroll
+          for (int x = 0; x < EPB; ++x) dst[t * ld + e + x] = to_float(pc[i][x]);
+        }
+      }
+    } else if (lane < 2 * Tv) {
+      sab[lane >> 1][lane & 1] = (lane & 1) ? gb : expf(gb);
+    }
   }
   __syncthreads();
 
