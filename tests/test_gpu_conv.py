@@ -28,6 +28,12 @@ def gdn():
     ("fp32", 1, 64, 3, 128, False, 0),
     ("bf16", 1, 3, 1, 64, True, 0),        # shorter than the filter
     ("fp32", 1, 41, 2, 64, True, 7),
+    # head blocks of four heads: 2 and 8 (four and one token streams of workgroups, some past the last
+    # token block), 3 and 5 (the plain numbering); ragged and packed token counts
+    ("bf16", 2, 150, 8, 128, True, 0),
+    ("bf16", 1, 500, 12, 64, True, 9),
+    ("fp32", 1, 97, 32, 64, False, 4),
+    ("bf16", 3, 65, 20, 64, True, 0),
 ])
 def test_short_conv_matches_oracle(gdn, dtype, B, T, H, hd, l2, packed):
     flush(f"short conv {dtype} B={B} T={T} H={H} hd={hd} l2={l2} packed={packed}")
