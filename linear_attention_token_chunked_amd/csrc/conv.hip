@@ -22,12 +22,18 @@ namespace {
 constexpr int kConvThreads = 256;
 constexpr int kConvWidth = 4;
 
+// Sum over the 16 lanes of a DPP row, the same bits in every lane, without LDS: lanes i and 7 - i of
+// each half-row (half-row mirror), then pairs l ^ 1 and l ^ 2 (quad permutations), then l ^ 8
+// (rotation of the row by 8).
+template <int CTRL>
+__device__ __forceinline__ float dpp_plus(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float row16_sum(float x) {
-  x += __shfl_xor(x, 1);
-  x += __shfl_xor(x, 2);
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 8);
-  return x;
+  x = dpp_plus<0x141>(x);  // row_half_mirror
+  x = dpp_plus<0xb1>(x);   // quad_perm [1, 0, 3, 2]
+  x = dpp_plus<0x4e>(x);   // quad_perm [2, 3, 0, 1]
+  return dpp_plus<0x128>(x);  // row_ror:8
 }
 
 // A 16-lane group walks a run of kRun consecutive tokens of one head: it
