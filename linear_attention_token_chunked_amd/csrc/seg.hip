@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void seg_correct_kernel(bf16* o, const bf16* q
   }
   constexpr int IT = C * D / 8 / 256;
   bf16x8 vq[IT], vo[IT];
-  auto fetch = [&](int tt) {  // the tile's rows of qt and o into registers
+  auto fetch = [&](int tt) {  // the tile's rows of qt and o into registers (streaming: read once)
     const int L = min(C, t1 - tt);
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
@@ -135,8 +135,8 @@ __global__ __launch_bounds__(256) void seg_correct_kernel(bf16* o, const bf16* q
       vo[it] = bf16x8{};
       if (r < L) {
         const size_t at = (tt + r) * row + h * D + e;
-        vq[it] = *reinterpret_cast<const bf16x8*>(qt + at);
-        vo[it] = *reinterpret_cast<const bf16x8*>(o + at);
+        vq[it] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(qt + at));
+        vo[it] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(o + at));
       }
     }
   };
@@ -151,25 +151,28 @@ __global__ __launch_bounds__(256) void seg_correct_kernel(bf16* o, const bf16* q
     }
     lds_barrier();  // (the previous tile's stores to o may still be in flight)
     if (tt + C < t1) fetch(tt + C);  // in flight during this tile's products
-    // 4 x 8 output tiles; wavefront w owns column tiles 2w and 2w + 1
+    // 4 x 8 output tiles, formed transposed (o^T += M_s^T qt^T) so that a lane holds four adjacent
+    // columns of one token row: one 8-byte update per lane and tile; wavefront w owns column tiles
+    // 2w and 2w + 1
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
       const int jt = 2 * wave + jj;
-      const bf16* br = sMt + (16 * jt + lr) * LDS_B;
-      Mma<bf16>::frag bf[D / 32];
+      const bf16* ar = sMt + (16 * jt + lr) * LDS_B;
+      Mma<bf16>::frag af[D / 32];
 #pragma unroll
-      for (int kg = 0; kg < D / 32; ++kg) bf[kg] = lds_frag<bf16>(br, kg, lane);
+      for (int kg = 0; kg < D / 32; ++kg) af[kg] = lds_frag<bf16>(ar, kg, lane);
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         floatx4 acc = zero4();
-        const bf16* ar = sQt + (16 * it + lr) * LDS_B;
+        const bf16* br = sQt + (16 * it + lr) * LDS_B;
 #pragma unroll
-        for (int kg = 0; kg < D / 32; ++kg) Mma<bf16>::mma(acc, lds_frag<bf16>(ar, kg, lane), bf[kg]);
+        for (int kg = 0; kg < D / 32; ++kg) Mma<bf16>::mma(acc, af[kg], lds_frag<bf16>(br, kg, lane));
+        // acc[r]: token 16 it + lr, column 16 jt + 4 lg + r (each element has one owner)
+        bf16x4* x = reinterpret_cast<bf16x4*>(sO + (16 * it + lr) * LDS_B + 16 * jt + 4 * lg);
+        bf16x4 ov = *x;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {  // (each element has one owner)
-          bf16* x = sO + (16 * it + 4 * lg + r) * LDS_B + 16 * jt + lr;
-          *x = from_float<bf16>(to_float(*x) + acc[r]);
-        }
+        for (int r = 0; r < 4; ++r) ov[r] = from_float<bf16>(to_float(ov[r]) + acc[r]);
+        *x = ov;
       }
     }
     lds_barrier();
@@ -177,7 +180,8 @@ __global__ __launch_bounds__(256) void seg_correct_kernel(bf16* o, const bf16* q
     for (int it = 0; it < IT; ++it) {
       const int i = tid + it * 256, r = i / (D / 8), e = (i - r * (D / 8)) * 8;
       if (r < L)
-        *reinterpret_cast<bf16x8*>(o + (tt + r) * row + h * D + e) = *reinterpret_cast<const bf16x8*>(sO + r * LDS_B + e);
+        __builtin_nontemporal_store(*reinterpret_cast<const bf16x8*>(sO + r * LDS_B + e),
+                                    reinterpret_cast<bf16x8*>(o + (tt + r) * row + h * D + e));
     }
     lds_barrier();
   }
