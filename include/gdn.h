@@ -201,7 +201,9 @@ gdn_status_t gdn_decode_verify(const gdn_dims_t* d, const void* q, const void* k
  * For every row r (one token of one value head, dv values):
  *   y[r] = sigmoid(z[r]) * (o[r] / sqrt(mean_j o[r, j]^2 + eps)) * (1 + weight)
  * with z the gate pre-activations (x W_g, computed by the caller) and weight
- * the zero-centred per-channel norm weight (the scale is 1 + weight).
+ * the zero-centred per-channel norm weight (the scale is 1 + weight).  All in
+ * fp32; the sigmoid is 1 / (1 + 2^(-z log2 e)) from the GPU's base-2 exponential
+ * and reciprocal, each within about one fp32 ulp.
  *
  *   rows     number of rows, e.g. B * T * Hv for a prefill output; >= 0
  *   dv       values per row: 64 or 128 (NOT_SUPPORTED otherwise)
