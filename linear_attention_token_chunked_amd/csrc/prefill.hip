@@ -330,18 +330,26 @@ struct ChunkRegs {
 
 // Gram tiles (ti >= tj) of producer wave W, grouped by token-row tile so that
 // a wave loads each B fragment (K and Q rows of tile ti) once per k-group.
-// Waves 0 and 1 share their SIMDs with the (higher-priority) consumer waves
-// and get the lighter shares:
-//   wave 0: (3,0) (3,1) (3,2)    wave 1: (2,0) (2,1)
-//   wave 2: (1,0) (1,1) (2,2)    wave 3: (0,0) (3,3)
 // Every tile gives A; P comes from Q K^T of the same tiles, except with two
 // output waves, which form P themselves but for the tiles in pmask (bit t:
-// tile t), which waves 1 and 3 have room for.
-template <int W> struct GramTiles;
-template <> struct GramTiles<0> { static constexpr int n = 3, ti[3] = {3, 3, 3}, tj[3] = {0, 1, 2}, pmask = 0; };
-template <> struct GramTiles<1> { static constexpr int n = 2, ti[3] = {2, 2, 0}, tj[3] = {0, 1, 0}, pmask = 1; };
-template <> struct GramTiles<2> { static constexpr int n = 3, ti[3] = {1, 1, 2}, tj[3] = {0, 1, 2}, pmask = 0; };
-template <> struct GramTiles<3> { static constexpr int n = 2, ti[3] = {0, 3, 0}, tj[3] = {0, 3, 0}, pmask = 2; };
+// tile t), the tiles (2,0) and (3,3) in either assignment.
+// With output waves (ROWS = false):
+//   wave 0: (3,0) (3,1) (3,2)    wave 1: (2,0) (2,1)
+//   wave 2: (1,0) (1,1) (2,2)    wave 3: (0,0) (3,3)
+// Without (ROWS = true), by token-row block, which needs 15 distinct row
+// fragments per k-group over the four waves instead of 18 (0.7-2 % faster on
+// the 128-column shapes, 1 % slower with output waves):
+//   wave 0: (0,0) (1,0) (1,1)    wave 1: (2,0) (2,1) (2,2)
+//   wave 2: (3,0) (3,1)          wave 3: (3,2) (3,3)
+template <int W, bool ROWS> struct GramTiles;
+template <> struct GramTiles<0, false> { static constexpr int n = 3, ti[3] = {3, 3, 3}, tj[3] = {0, 1, 2}, pmask = 0; };
+template <> struct GramTiles<1, false> { static constexpr int n = 2, ti[3] = {2, 2, 0}, tj[3] = {0, 1, 0}, pmask = 1; };
+template <> struct GramTiles<2, false> { static constexpr int n = 3, ti[3] = {1, 1, 2}, tj[3] = {0, 1, 2}, pmask = 0; };
+template <> struct GramTiles<3, false> { static constexpr int n = 2, ti[3] = {0, 3, 0}, tj[3] = {0, 3, 0}, pmask = 2; };
+template <> struct GramTiles<0, true> { static constexpr int n = 3, ti[3] = {0, 1, 1}, tj[3] = {0, 0, 1}, pmask = 0; };
+template <> struct GramTiles<1, true> { static constexpr int n = 3, ti[3] = {2, 2, 2}, tj[3] = {0, 1, 2}, pmask = 1; };
+template <> struct GramTiles<2, true> { static constexpr int n = 2, ti[3] = {3, 3, 0}, tj[3] = {0, 1, 0}, pmask = 0; };
+template <> struct GramTiles<3, true> { static constexpr int n = 2, ti[3] = {3, 3, 0}, tj[3] = {2, 3, 0}, pmask = 2; };
 
 // P tiles (ti >= tj) formed by output wave W (with two output waves only):
 // the eight the producers leave.
@@ -477,7 +485,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
   constexpr bool PMASK = !(OUTW && SAVE);         // a saving run with output waves forms no P (no O)
   floatx4 pkeep[3], akeep[3];
   auto gram = [&](auto wtag, int s) __attribute__((always_inline)) {
-    using GT = GramTiles<decltype(wtag)::value>;
+    using GT = GramTiles<decltype(wtag)::value, !OUTW>;
     const unsigned char* S = stage(s);
     const T* sK = reinterpret_cast<const T*>(S + L::sK);
     const T* sQ = reinterpret_cast<const T*>(S + L::sQ);
@@ -540,7 +548,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
   // P (without output waves) and -A into their (single) buffers; each
   // producer wave inverts one of the four diagonal blocks of I + A.
   auto put = [&](auto wtag) __attribute__((always_inline)) {
-    using GT = GramTiles<decltype(wtag)::value>;
+    using GT = GramTiles<decltype(wtag)::value, !OUTW>;
     T* sPf = reinterpret_cast<T*>(smem + L::oPf);
     T* sAnf = reinterpret_cast<T*>(smem + L::oAnf);
 #pragma unroll
