@@ -66,6 +66,15 @@ template <int W>
 __device__ __forceinline__ int swz_off(int r, int c) {  // element offset of column c of row r
   return r * W + ((((c >> 4) ^ swz<W>(r)) << 4) | (c & 15));
 }
+// The output tile's staging layout for 128-column bf16 tiles: 16-byte piece p of row r at p ^ (r & 15),
+// so that the 16 rows one accumulator store covers, and the 16 pieces one row read covers, fall on
+// distinct 16-byte bank windows.  Other tiles keep the V tile's layout.
+template <class T, int W>
+__device__ __forceinline__ int o_off(int r, int c) {
+  if constexpr (sizeof(T) == 2 && W == 128) return r * W + ((((c >> 3) ^ (r & 15)) << 3) | (c & 7));
+  else if constexpr (sizeof(T) == 2) return swz_off<W>(r, c);
+  else return r * W + c;
+}
 // Transposing 8-byte LDS read (see lds_col4).
 __device__ __forceinline__ bf16x4 tr_read(const bf16* ptr) {
   typedef short s4 __attribute__((ext_vector_type(4)));
@@ -803,8 +812,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
         for (int j = 0; j < NTW; ++j) {
           const floatx4 ov = Ot[ct][j] * p.scale;
           const int r = 16 * ct + lr, col = (cw * NTW + j) * 16 + 4 * lg;
-          *reinterpret_cast<V4*>(sO + (sizeof(T) == 2 ? swz_off<BV>(r, col) : r * LDV + col)) =
-              pack4<T>(ov[0], ov[1], ov[2], ov[3]);
+          *reinterpret_cast<V4*>(sO + o_off<T, BV>(r, col)) = pack4<T>(ov[0], ov[1], ov[2], ov[3]);
         }
     }
   };
@@ -823,7 +831,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
       const int r = t / PPR, col = (t % PPR) * EP;
       if (t < C * PPR && r < Lc)
         *reinterpret_cast<frag*>(og + static_cast<size_t>(cs + r) * v_tok + static_cast<size_t>(h) * DV + col0 + col) =
-            *reinterpret_cast<const frag*>(sO + (sizeof(T) == 2 ? swz_off<BV>(r, col) : r * LDV + col));
+            *reinterpret_cast<const frag*>(sO + o_off<T, BV>(r, col));
     }
   };
 
