@@ -122,17 +122,30 @@ __device__ __forceinline__ float sum16(float x) {
 #undef GDN_ROR_ADD
   return x;
 }
+// Sum over the 8 lanes of a half row group, in every lane of it (quad permutations
+// l ^ 1 and l ^ 2, then the half-row mirror, which pairs the two quads).
+__device__ __forceinline__ float sum8(float x) {
+#define GDN_DPP_ADD(ctrl) \
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, 0xf, 0xf, false))
+  GDN_DPP_ADD(0xb1);
+  GDN_DPP_ADD(0x4e);
+  GDN_DPP_ADD(0x141);
+#undef GDN_DPP_ADD
+  return x;
+}
 __device__ __forceinline__ floatx4 vec4_at(const float* v) { return *reinterpret_cast<const floatx4*>(v); }
 __device__ __forceinline__ float rdlane(float x, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }
 
 // Rows of a row-major tile held in registers on their way to LDS, as raw
-// 4-element vectors: R rows of W columns, NT threads (rows >= L read as zero).
+// 16-byte pieces of EP elements: R rows of W columns, NT threads (rows >= L
+// read as zero).
 template <class T, int W, int NT, int R = C>
 struct RowsInFlight {
-  static constexpr int PR = W / 4, N = R * PR, IT = (N + NT - 1) / NT;
-  typename Vec4<T>::type v[IT];
+  static constexpr int EP = 16 / sizeof(T), PR = W / EP, N = R * PR, IT = (N + NT - 1) / NT;
+  typedef T piece __attribute__((ext_vector_type(EP)));
+  piece v[IT];
   // src is the same for every lane; the per-lane part is a 32-bit byte offset
   // (at most 64 rows of at most 1 MB)
   __device__ __forceinline__ void load(const T* src, size_t ss, int L, int tid) {
@@ -140,17 +153,17 @@ struct RowsInFlight {
     const unsigned stride = static_cast<unsigned>(ss * sizeof(T));
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const int i = tid + it * NT, t = i / PR, e = (i - t * PR) * 4;
+      const int i = tid + it * NT, t = i / PR, e = (i - t * PR) * EP;
       const unsigned off = static_cast<unsigned>(t) * stride + static_cast<unsigned>(e * sizeof(T));
-      if (i < N && t < L) v[it] = *reinterpret_cast<const typename Vec4<T>::type*>(base + off);
-      else v[it] = typename Vec4<T>::type{};
+      if (i < N && t < L) v[it] = *reinterpret_cast<const piece*>(base + off);
+      else v[it] = piece{};
     }
   }
   __device__ __forceinline__ void store(T* dst, int ld, int tid) const {
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const int i = tid + it * NT, t = i / PR, e = (i - t * PR) * 4;
-      if (i < N) *reinterpret_cast<typename Vec4<T>::type*>(dst + t * ld + e) = v[it];
+      const int i = tid + it * NT, t = i / PR, e = (i - t * PR) * EP;
+      if (i < N) *reinterpret_cast<piece*>(dst + t * ld + e) = v[it];
     }
   }
 };
@@ -273,6 +286,36 @@ __global__ __launch_bounds__(512) void dstate_kernel(BwdParams p) {
     rq.store(reinterpret_cast<T*>(B + L::iQ), LDK, t);
     rdo.store(reinterpret_cast<T*>(B + L::idO), LDB, t);
   };
+  // With bf16 inputs the staging wavefronts request a chunk's rows one iteration before they store
+  // them (in the back-substitution phase, after storing the chunk requested the iteration before),
+  // so the memory latency lands on no phase.  The fp32 instantiation has no registers to spare for
+  // that and stages within the phase.
+  constexpr bool AHEAD = sizeof(T) == 2;
+  RowsInFlight<T, DK, NST> nk, nq;
+  RowsInFlight<T, BV, NST> ndo;
+  float ng = 0.f, nb = 0.f;
+  auto stage_load = [&](int c) __attribute__((always_inline)) {
+    const int cs = sq.bos + c * C, Lc = min(C, sq.eos - cs), t = tid - 64 * NJ;
+    const size_t qo = static_cast<size_t>(cs) * qk_tok + static_cast<size_t>(hq) * DK;
+    nk.load(static_cast<const T*>(p.k) + qo, qk_tok, Lc, t);
+    nq.load(static_cast<const T*>(p.q) + qo, qk_tok, Lc, t);
+    ndo.load(static_cast<const T*>(p.dout) + static_cast<size_t>(cs) * v_tok + static_cast<size_t>(h) * DV + col0, v_tok,
+             Lc, t);
+    if (t < 64) {
+      const size_t gi = static_cast<size_t>(cs) * p.Hv + h;
+      const bool live = lane < Lc;
+      ng = live ? p.g[gi + lane * static_cast<size_t>(p.Hv)] : 0.f;
+      nb = live ? p.beta[gi + lane * static_cast<size_t>(p.Hv)] : 0.f;
+    }
+  };
+  auto stage_store = [&](int c) __attribute__((always_inline)) {
+    unsigned char* B = smem + (c & 1) * L::in_bytes;
+    const int t = tid - 64 * NJ;
+    if (t < 64) gate_vectors_from(reinterpret_cast<float*>(B + L::iVec), ng, nb, lane);
+    nk.store(reinterpret_cast<T*>(B + L::iK), LDK, t);
+    nq.store(reinterpret_cast<T*>(B + L::iQ), LDK, t);
+    ndo.store(reinterpret_cast<T*>(B + L::idO), LDB, t);
+  };
   // dM' as matrix-core operands
   floatx4 dM[NMT];  // tile t = wave + NW i -> rows 16 (t / NJ), columns 16 (t % NJ)
   auto dm_to_lds = [&]() __attribute__((always_inline)) {
@@ -294,6 +337,7 @@ __global__ __launch_bounds__(512) void dstate_kernel(BwdParams p) {
       dM[i][r] = p.dhT ? p.dhT[sbase + static_cast<size_t>(16 * a + 4 * lg + r) * DV + col0 + 16 * jc + lr] : 0.f;
   }
   if (nch > 0) stage_in(nch - 1, 0, std::integral_constant<int, NT>());
+  if (AHEAD && nch > 1 && wave >= NJ) stage_load(nch - 2);
   dm_to_lds();
   lds_barrier();
 
@@ -396,7 +440,12 @@ __global__ __launch_bounds__(512) void dstate_kernel(BwdParams p) {
         }
       }
     } else if (c > 0) {
-      stage_in(c - 1, 64 * NJ, std::integral_constant<int, NST>());
+      if constexpr (AHEAD) {
+        stage_store(c - 1);
+        if (c > 1) stage_load(c - 2);
+      } else {
+        stage_in(c - 1, 64 * NJ, std::integral_constant<int, NST>());
+      }
     }
     lds_barrier();
     // -- dZ (workspace, T) and dv = beta dZ out as whole 16-byte pieces, by every
@@ -586,16 +635,17 @@ __global__ __launch_bounds__(512) void dlocal_kernel(BwdParams p) {
     }
     lds_barrier();
     {  // the dZ . v part of dbeta
-      constexpr int PR = DV / 4, IT = C * PR / NT;
+      constexpr int EP = decltype(rv)::EP, PR = DV / EP, IT = C * PR / NT;
       static_assert(C * PR % NT == 0 && NT % PR == 0 && IT == decltype(rv)::IT, "whole rows per pass");
-      static_assert(PR == 16 || PR == 32, "a row is one or two 16-lane groups");
+      static_assert(PR == 8 || PR == 16 || PR == 32, "a row is half, one or two 16-lane groups");
 #pragma unroll
       for (int it = 0; it < IT; ++it) {
-        const int i = tid + it * NT, t = i / PR, e = (i - t * PR) * 4;
+        const int i = tid + it * NT, t = i / PR, e = (i - t * PR) * EP;
         float part = 0.f;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) part += to_float(sdZ[t * LDV + e + x]) * to_float(rv.v[it][x]);
-        part = sum16(part);  // the row's lanes first
+        for (int x = 0; x < EP; ++x) part += to_float(sdZ[t * LDV + e + x]) * to_float(rv.v[it][x]);
+        if constexpr (PR == 8) part = sum8(part);  // the row's lanes first
+        else part = sum16(part);
         if constexpr (PR == 32) part += __shfl_xor(part, 16);
         if ((lane & (PR - 1)) == 0) sB0[t] = part;
       }
@@ -687,14 +737,14 @@ __global__ __launch_bounds__(512) void dlocal_kernel(BwdParams p) {
     }
     // -- dM' replaces M in LDS; gam_C <dM', M> enters dG at the chunk's end
     {
-      constexpr int PR = DV / 4, IT = DK * PR / NT;
+      constexpr int EP = decltype(rdm)::EP, PR = DV / EP, IT = DK * PR / NT;
       static_assert(DK * PR % NT == 0 && IT == decltype(rdm)::IT, "whole passes");
       float part = 0.f;
 #pragma unroll
       for (int it = 0; it < IT; ++it) {
-        const int i = tid + it * NT, r = i / PR, e = (i - r * PR) * 4;
+        const int i = tid + it * NT, r = i / PR, e = (i - r * PR) * EP;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) part += to_float(rdm.v[it][x]) * to_float(sM[r * LDV + e + x]);
+        for (int x = 0; x < EP; ++x) part += to_float(rdm.v[it][x]) * to_float(sM[r * LDV + e + x]);
       }
       part = sum16(part);
       part += __shfl_xor(part, 16);
