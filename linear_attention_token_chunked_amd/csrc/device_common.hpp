@@ -12,6 +12,10 @@ namespace gdn {
 typedef __bf16 bf16;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef unsigned uintx2 __attribute__((ext_vector_type(2)));
+typedef unsigned uintx4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float to_float(float x) { return x; }
@@ -29,14 +33,33 @@ template <class T> struct Vec4;
 template <> struct Vec4<float> { typedef floatx4 type; };
 template <> struct Vec4<bf16> { typedef bf16x4 type; };
 
+// Two floats rounded to nearest even bf16, a in the low half.  Written as one
+// two-element conversion: element-wise casts into a 4- or 8-element bf16 vector
+// are emitted as one conversion per value plus byte permutes, three times the
+// instructions (and on a dependent chain, three times the latency).
+__device__ __forceinline__ unsigned pk_bf16(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(floatx2{a, b}, bf16x2));
+}
+
 template <class T>
 __device__ __forceinline__ typename Vec4<T>::type pack4(float a, float b, float c, float d) {
-  typename Vec4<T>::type r;
-  r[0] = from_float<T>(a);
-  r[1] = from_float<T>(b);
-  r[2] = from_float<T>(c);
-  r[3] = from_float<T>(d);
-  return r;
+  if constexpr (sizeof(T) == 2) {
+    return __builtin_bit_cast(bf16x4, uintx2{pk_bf16(a, b), pk_bf16(c, d)});
+  } else {
+    return floatx4{a, b, c, d};
+  }
+}
+
+// pack4 of (-a, -b, -c, -d): for bf16 the sign bits are flipped after the
+// rounding (exact, since rounding to nearest even is symmetric), one xor per
+// pair instead of one per value.
+template <class T>
+__device__ __forceinline__ typename Vec4<T>::type pack4_neg(float a, float b, float c, float d) {
+  if constexpr (sizeof(T) == 2) {
+    return __builtin_bit_cast(bf16x4, uintx2{pk_bf16(a, b) ^ 0x80008000u, pk_bf16(c, d) ^ 0x80008000u});
+  } else {
+    return floatx4{-a, -b, -c, -d};
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -72,12 +95,8 @@ template <> struct Mma<bf16> {
   }
   // Operand fragment from the two accumulator tiles that cover one k-group.
   __device__ __forceinline__ static frag chain(const floatx4& lo, const floatx4& hi) {
-    frag f;
-    f[0] = static_cast<bf16>(lo[0]); f[1] = static_cast<bf16>(lo[1]);
-    f[2] = static_cast<bf16>(lo[2]); f[3] = static_cast<bf16>(lo[3]);
-    f[4] = static_cast<bf16>(hi[0]); f[5] = static_cast<bf16>(hi[1]);
-    f[6] = static_cast<bf16>(hi[2]); f[7] = static_cast<bf16>(hi[3]);
-    return f;
+    return __builtin_bit_cast(frag, uintx4{pk_bf16(lo[0], lo[1]), pk_bf16(lo[2], lo[3]), pk_bf16(hi[0], hi[1]),
+                                           pk_bf16(hi[2], hi[3])});
   }
   // Key index held by row 4g + s of state accumulator tile a.  Element e of
   // the chained operand of k-group kg is row 4g + (e & 3) of tile 2kg + (e >> 2);
@@ -161,12 +180,7 @@ template <> struct Mma16<bf16> {
                                                    0);
   }
   __device__ __forceinline__ static frag chain(const floatx4& t) {
-    frag f;
-    f[0] = static_cast<bf16>(t[0]);
-    f[1] = static_cast<bf16>(t[1]);
-    f[2] = static_cast<bf16>(t[2]);
-    f[3] = static_cast<bf16>(t[3]);
-    return f;
+    return __builtin_bit_cast(frag, uintx2{pk_bf16(t[0], t[1]), pk_bf16(t[2], t[3])});
   }
 };
 template <> struct Mma16<float> {

@@ -567,7 +567,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
             pack4<T>(pkeep[t][0], pkeep[t][1], pkeep[t][2], pkeep[t][3]);
       if (GT::ti[t] != GT::tj[t])
         *reinterpret_cast<V4*>(sAnf + L::anf(GT::ti[t], GT::tj[t], lane)) =
-            pack4<T>(-akeep[t][0], -akeep[t][1], -akeep[t][2], -akeep[t][3]);
+            pack4_neg<T>(akeep[t][0], akeep[t][1], akeep[t][2], akeep[t][3]);
     }
   };
   auto prod_finish = [&]() __attribute__((always_inline)) {
@@ -782,6 +782,17 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
         }
       }
     }
+    // The query scale, skipped when it is 1 (a uniform branch: the product is
+    // then exact and the multiplies are spared).  Output waves multiply
+    // unconditionally: there the branch measured 1 % slower.
+    if constexpr (!SAVE) {
+      if (OUTW || p.scale != 1.f) {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int j = 0; j < NTW; ++j) Ot[ct][j] *= p.scale;
+      }
+    }
     if constexpr (SAVE) {
       (void)cs;
       (void)Lc;
@@ -792,7 +803,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
         if (16 * ct + lr < Lc) {
 #pragma unroll
           for (int j = 0; j < NTW; ++j) {
-            const floatx4 ov = Ot[ct][j] * p.scale;
+            const floatx4 ov = Ot[ct][j];
             *reinterpret_cast<V4*>(orow + static_cast<size_t>(16 * ct) * v_tok + 16 * j) =
                 pack4<T>(ov[0], ov[1], ov[2], ov[3]);
           }
@@ -810,7 +821,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
-          const floatx4 ov = Ot[ct][j] * p.scale;
+          const floatx4 ov = Ot[ct][j];
           const int r = 16 * ct + lr, col = (cw * NTW + j) * 16 + 4 * lg;
           *reinterpret_cast<V4*>(sO + o_off<T, BV>(r, col)) = pack4<T>(ov[0], ov[1], ov[2], ov[3]);
         }
@@ -822,16 +833,28 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
     constexpr int PPR = BV * sizeof(T) / 16;      // 16-byte pieces per row
     constexpr int NT = 64 * NCW;                  // consumer threads
     constexpr int EP = 16 / sizeof(T);
+    constexpr int NIT = C * PPR / NT;
+    static_assert(C * PPR % NT == 0, "whole passes over the tile");
     const T* sO = reinterpret_cast<const T*>(stage(s) + L::sV);
     const int cs = bos + c * C, Lc = min(C, eos - cs);
     const int ct0 = tid - 64 * NP;
+    // Every row is read from LDS first (the tile holds all C rows), so the
+    // stores wait for LDS once; the stores of rows past the end are skipped.
+    // Addresses: the chunk's first row as a uniform base plus a 32-bit byte
+    // offset per lane (C rows of one head span far less than 4 GiB).
+    frag rows[NIT];
 #pragma unroll
-    for (int it = 0; it < (C * PPR + NT - 1) / NT; ++it) {
+    for (int it = 0; it < NIT; ++it) {
+      const int t = ct0 + it * NT;
+      rows[it] = *reinterpret_cast<const frag*>(sO + o_off<T, BV>(t / PPR, (t % PPR) * EP));
+    }
+    char* obase = reinterpret_cast<char*>(og + static_cast<size_t>(cs) * v_tok + static_cast<size_t>(h) * DV + col0);
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
       const int t = ct0 + it * NT;
       const int r = t / PPR, col = (t % PPR) * EP;
-      if (t < C * PPR && r < Lc)
-        *reinterpret_cast<frag*>(og + static_cast<size_t>(cs + r) * v_tok + static_cast<size_t>(h) * DV + col0 + col) =
-            *reinterpret_cast<const frag*>(sO + o_off<T, BV>(r, col));
+      const uint32_t off = (static_cast<uint32_t>(r) * static_cast<uint32_t>(v_tok) + col) * sizeof(T);
+      if (r < Lc) *reinterpret_cast<frag*>(obase + off) = rows[it];
     }
   };
 
