@@ -17,7 +17,12 @@
  *  - States are stored transposed, M = S^T, as fp32 [N, Hv, dk, dv] row-major:
  *    element (n, h, i, j) = S_{n,h}[j][i], i over the key dim, j over the value dim.
  *  - g is log(alpha) (fp32, <= 0 for a decaying gate); beta is the write strength
- *    after any sigmoid (fp32).  Both are per value head.
+ *    after any sigmoid (fp32).  Both are per value head.  g = -inf (alpha = 0, a
+ *    full forget) is accepted: the chunked calls floor g at -200 before their
+ *    in-chunk prefix sums, where exp(-200) already rounds to 0 in fp32, so the
+ *    history before such a token is erased as for alpha = 0 (and the backward's
+ *    gradient with respect to such a g is that of g = -200: zero up to rounding).
+ *    NaN or +inf gates are not valid input.
  *  - Value head h reads query/key head h / (Hv / Hqk)  (Hv must be a multiple of Hqk).
  *  - q, k, v, o are dtype (fp32 or bf16, see gdn_dtype_t); o is rounded from fp32
  *    accumulators to nearest even.  All tensors are dense, row-major and contiguous.

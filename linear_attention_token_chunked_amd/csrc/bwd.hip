@@ -173,7 +173,7 @@ struct RowsInFlight {
 // beta = 0), and exp(G_C) in vec[4C].
 enum { V_GL, V_GAM, V_KF, V_BETA, V_N };
 __device__ __forceinline__ void gate_vectors_from(float* vec, float gt, float bt, int lane) {
-  const float Gl = wave_inclusive_sum(gt) * kLog2e;
+  const float Gl = wave_inclusive_sum(fmaxf(gt, kGateFloor)) * kLog2e;
   const float GlC = rdlane(Gl, 63);
   vec[V_GL * C + lane] = Gl;
   vec[V_GAM * C + lane] = __builtin_amdgcn_exp2f(Gl);

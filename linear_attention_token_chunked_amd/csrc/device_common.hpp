@@ -133,6 +133,15 @@ __device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f};
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Floor of a log-gate g = log(alpha) before it enters an in-chunk prefix sum.
+// alpha = 0 (a full forget) arrives as g = -inf, and differences of prefix sums
+// would then be -inf - (-inf) = NaN.  exp(-200) is below the smallest fp32
+// value, so every decay factor that spans a floored token is still exactly 0,
+// as for alpha = 0, while the sums stay finite (a few floored tokens in a chunk
+// keep them within a few thousand, where fp32 resolves differences to 1e-3 or
+// better).  Gates at or above the floor are unchanged.
+constexpr float kGateFloor = -200.f;
+
 // Inclusive prefix sum over the 64 lanes of a wavefront with DPP row shifts
 // and row broadcasts (no LDS round trips).
 __device__ __forceinline__ float wave_inclusive_sum(float x) {

@@ -469,7 +469,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
       const bool live = lane < Lc;  // tokens past the end act as g = 0, beta = 0 (exact no-ops)
       const float bt = live ? pre.b : 0.f;
       // inclusive prefix sum of the log-gates over the chunk
-      const float Gl = wave_inclusive_sum(live ? pre.g : 0.f) * kLog2e;
+      const float Gl = wave_inclusive_sum(live ? fmaxf(pre.g, kGateFloor) : 0.f) * kLog2e;
       const float GlC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, Gl), 63));
       float* vec = reinterpret_cast<float*>(S + L::sVec);
       vec[VEC_EG * C + lane] = __builtin_amdgcn_exp2f(Gl);

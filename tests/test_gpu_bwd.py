@@ -87,6 +87,22 @@ def test_bwd_many_units_wide_launch(gdn, d):
     check(got, ref, TOL[torch.bfloat16])
 
 
+def test_bwd_zero_gates(gdn):
+    """Gradients through full forgets (g = -inf): finite everywhere, and matching the autograd oracle, whose
+    gradient with respect to such a g is exactly zero (the kernels' is zero up to rounding)."""
+    flush("bwd zero gates")
+    B, T, Hqk, Hv, d = 2, 200, 2, 4, 128
+    inp = make_prefill(B, T, Hqk, Hv, d, d, "bf16", init_state=True, seed=81)
+    for b, t, h in [(0, 0, 0), (0, 37, 1), (0, 64, 2), (1, 150, 3), (1, 160, 3), (1, 199, 0)]:
+        inp["g"][b, t, h] = -float("inf")
+    cot = make_cotangents(B, T, Hv, d, B, d, "bf16", seed=82)
+    got, ref = run_case(gdn, inp, cot, scale=d ** -0.5)
+    for name in NAMES:
+        if got[name] is not None:
+            assert np.all(np.isfinite(f64(got[name]))), name
+    check(got, ref, TOL[torch.bfloat16])
+
+
 def test_bwd_without_initial_state_gradient(gdn):
     flush("bwd want_d_initial_state=False")
     inp = make_prefill(1, 100, 1, 2, 64, 64, "bf16", init_state=True, seed=8)

@@ -46,6 +46,29 @@ def test_decode_small_matches_oracle(gdn, dtype, dk, dv, Hqk, Hv):
     assert_close("state", f64(state), ref_state, tol)
 
 
+def test_decode_zero_gates(gdn):
+    """alpha = 0 (g = -inf) for some (sequence, head) units at some steps: their state is replaced by
+    beta v k^T, exactly as the token recurrence says, and nothing becomes NaN."""
+    flush("decode zero gates")
+    steps, N = 4, 5
+    inp = make_decode(N, 2, 4, 128, 128, steps, "bf16", seed=12)
+    for t, n, h in [(0, 0, 0), (1, 2, 3), (2, 4, 1), (3, 0, 0)]:
+        inp["g"][t, n, h] = -float("inf")
+    dev = to_dev(inp)
+    state = dev["state"].clone()
+    ref_state = f64(inp["state"])
+    outs, refs = [], []
+    for t in range(steps):
+        o = gdn.decode_step(dev["q"][t], dev["k"][t], dev["v"][t], dev["g"][t], dev["beta"][t], state)
+        ro, ref_state = oracle_decode(inp["q"][t], inp["k"][t], inp["v"][t], inp["g"][t], inp["beta"][t], ref_state)
+        outs.append(f64(o))
+        refs.append(ro)
+    got_o, got_s = np.stack(outs), f64(state)
+    assert np.all(np.isfinite(got_o)) and np.all(np.isfinite(got_s))
+    assert_close("o", got_o, np.stack(refs), TOL[torch.bfloat16])
+    assert_close("state", got_s, ref_state, TOL[torch.bfloat16])
+
+
 def test_decode_full_workload_whole_tensors(gdn, oracle_pool):
     """256 sequences x 32 value heads, 64 separate decode calls updating the 512 MiB state in place: every
     element of o at every step and of the state after step 64 against 64 oracle decode steps per sequence

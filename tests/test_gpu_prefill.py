@@ -155,6 +155,35 @@ def test_query_equal_key_beta_one_reads_back_value(gdn):
     assert_close("o", f64(o), f64(inp["v"]), 1e-5)
 
 
+# (batch row, token, value head) of the full-forget gates: a sequence's first token, inside a chunk, both sides
+# of a chunk boundary, twice in one chunk, the last token
+ZERO_GATES = [(0, 0, 0), (0, 37, 1), (0, 63, 2), (0, 64, 2), (1, 150, 3), (1, 160, 3), (1, 299, 0), (1, 100, 1)]
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("fp32", 64)])
+def test_zero_gates_erase_history(gdn, dtype, d):
+    """alpha = 0 (g = -inf, the full forget) on tokens of every kind of place, and one finite gate far below
+    the kernels' floor: o and the final states stay finite and match the token recurrence."""
+    flush(f"prefill zero gates {dtype} d={d}")
+    inp = make_prefill(2, 300, 2, 4, d, d, dtype, init_state=True, seed=77 + d)
+    for b, t, h in ZERO_GATES:
+        inp["g"][b, t, h] = -float("inf")
+    inp["g"][0, 200, 3] = -1e4
+    go, gf = check_against_oracle(gdn, inp, dtype, scale=0.9)
+    assert np.all(np.isfinite(go)) and np.all(np.isfinite(gf))
+
+
+def test_zero_gates_packed(gdn):
+    """The same in a packed batch: a full forget on a sequence's first token, at a chunk boundary and last."""
+    lens = [70, 0, 130, 64]
+    flush(f"prefill zero gates packed lens={lens}")
+    inp = make_prefill(1, 0, 2, 4, 128, 128, "bf16", init_state=True, lengths=lens, seed=78)
+    for t, h in [(0, 0), (70, 1), (70 + 64, 2), (199, 3), (200, 0), (263, 1)]:
+        inp["g"][0, t, h] = -float("inf")
+    go, gf = check_against_oracle(gdn, inp, "bf16")
+    assert np.all(np.isfinite(go)) and np.all(np.isfinite(gf))
+
+
 def test_in_place_state_and_no_final_state(gdn):
     inp = make_prefill(2, 100, 1, 2, 128, 128, "bf16", init_state=True, seed=6)
     dev = to_dev(inp)

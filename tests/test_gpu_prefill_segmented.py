@@ -67,6 +67,26 @@ def test_segmented_slow_decay_carries_state(gdn):
     assert_close("final_state", f64(fin), rf, TOL[torch.bfloat16])
 
 
+def test_segmented_zero_gates(gdn):
+    """Full forgets (g = -inf) in the first segment, on a segment boundary and inside the last segment: the
+    zero-start and transition runs and the correction stay finite and match the token recurrence."""
+    B, T, Hqk, Hv = 1, 4096, 1, 2
+    assert segmented(gdn, B, T, Hv), "this shape takes the segmented path"
+    flush("segmented zero gates")
+    inp = make_prefill(B, T, Hqk, Hv, 128, 128, "bf16", init_state=True, seed=79)
+    for t, h in [(500, 0), (1024, 1), (1024, 0), (3000, 1), (4095, 0)]:
+        inp["g"][0, t, h] = -float("inf")
+    dev = to_dev(inp)
+    o, fin = gdn.fwd_chunked(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], initial_state=dev["initial_state"])
+    torch.cuda.synchronize()
+    ro, rf = recurrent(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], initial_state=inp["initial_state"])
+    tol = TOL[torch.bfloat16]
+    go, gf = f64(o), f64(fin)
+    assert np.all(np.isfinite(go)) and np.all(np.isfinite(gf))
+    assert_close("o", go, ro, tol)
+    assert_close("final_state", gf, rf, tol)
+
+
 def test_segmented_equals_unsegmented_path(gdn):
     """The same row through the segmented path and, as one of several rows, through the fused path."""
     flush("segmented vs fused")

@@ -1,6 +1,7 @@
 """GPU parity of gdn_decode_verify (multi-token verify from a live state) against the fp64 oracle,
 through the C ABI, and its agreement with repeated gdn_decode_step calls."""
 
+import numpy as np
 import pytest
 import torch
 
@@ -41,6 +42,24 @@ def test_verify_small_matches_oracle(gdn, dtype, Tv, dk, dv, Hqk, Hv):
     assert_close("o", f64(o), ref_o, tol)
     assert_close("token states", f64(states), ref_states, tol)
     assert_close("state in place", f64(state), ref_states[:, -1], tol)
+
+
+def test_verify_zero_gates(gdn):
+    """A drafted token with alpha = 0 (g = -inf) erases its unit's live state, the first drafted token included."""
+    flush("verify zero gates")
+    N, Tv = 5, 4
+    inp = make_verify(N, Tv, 2, 4, 128, 128, "bf16", seed=22)
+    for n, t, h in [(0, 0, 0), (1, 2, 3), (4, 3, 1)]:
+        inp["g"][n, t, h] = -float("inf")
+    dev = to_dev(inp)
+    state = dev["state"].clone()
+    states = torch.empty((N, Tv, 4, 128, 128), dtype=torch.float32, device="cuda")
+    o = gdn.decode_verify(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], state, token_states=states)
+    ref_o, ref_states = oracle_verify(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["state"])
+    tol = TOL[torch.bfloat16]
+    assert np.all(np.isfinite(f64(o))) and np.all(np.isfinite(f64(states)))
+    assert_close("o", f64(o), ref_o, tol)
+    assert_close("token states", f64(states), ref_states, tol)
 
 
 def test_verify_equals_repeated_decode_steps(gdn):

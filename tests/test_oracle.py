@@ -478,6 +478,24 @@ def test_p14_zero_values_contract_the_state():
         assert np.linalg.norm(state) <= np.exp(g[0, t, 0]) * prev * (1 + 1e-12)
 
 
+# ------------------------------------------------------------------ P20 ----
+def test_p20_zero_gate_erases_the_history():
+    """alpha_t0 = 0 (g = -inf): S_t0 = beta v k^T whatever came before, so every output from t0 on and the final
+    state equal a fresh run over tokens t0.. from the zero state; the outputs before t0 are untouched."""
+    rng = np.random.default_rng(95)
+    q, k, v, g, beta = rand_inputs(rng, T=21, Hqk=1, Hv=2, dk=5, dv=4)
+    S0 = rng.standard_normal((1, 2, 5, 4))
+    t0 = 9
+    g[0, t0, :] = -np.inf
+    o, fin = recurrent(q, k, v, g, beta, initial_state=S0)
+    o_tail, fin_tail = recurrent(q[:, t0:], k[:, t0:], v[:, t0:], g[:, t0:], beta[:, t0:])
+    close(o[:, t0:], o_tail)
+    close(fin, fin_tail)
+    o_head, _ = recurrent(q[:, :t0], k[:, :t0], v[:, :t0], g[:, :t0], beta[:, :t0], initial_state=S0)
+    close(o[:, :t0], o_head)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(fin))
+
+
 def test_inputs_module_recipe():
     """The shared generator: unit q/k, beta in (0,1), g <= 0, lengths in range, determinism."""
     import torch
