@@ -103,6 +103,17 @@ def test_bwd_zero_gates(gdn):
     check(got, ref, TOL[torch.bfloat16])
 
 
+def test_bwd_rows_without_tokens(gdn):
+    """B rows of zero tokens: the final state is the initial state, so its gradient passes through unchanged,
+    bit for bit."""
+    flush("bwd rows without tokens")
+    inp = make_prefill(2, 0, 1, 2, 128, 128, "bf16", init_state=True, seed=16)
+    cot = make_cotangents(2, 0, 2, 128, 2, 128, "bf16", seed=17)
+    got, _ = run_case(gdn, inp, cot, scale=1.0)
+    assert torch.equal(got["d_initial_state"].cpu(), cot["d_final"])
+    assert got["dq"].numel() == 0 and got["dv"].numel() == 0
+
+
 def test_bwd_without_initial_state_gradient(gdn):
     flush("bwd want_d_initial_state=False")
     inp = make_prefill(1, 100, 1, 2, 64, 64, "bf16", init_state=True, seed=8)

@@ -184,6 +184,18 @@ def test_zero_gates_packed(gdn):
     assert np.all(np.isfinite(go)) and np.all(np.isfinite(gf))
 
 
+@pytest.mark.parametrize("dtype,d,init", [("bf16", 128, True), ("bf16", 128, False), ("fp32", 64, True)])
+def test_rows_without_tokens(gdn, dtype, d, init):
+    """B rows of zero tokens: nothing to run, and every final state is the initial one, bit for bit (zeros
+    without an initial state)."""
+    flush(f"prefill rows without tokens {dtype} d={d} init={init}")
+    inp = make_prefill(2, 0, 1, 2, d, d, dtype, init_state=init, seed=15)
+    o, fin = run_gpu(gdn, inp)
+    assert o.shape == (2, 0, 2, d)
+    expect = inp["initial_state"] if init else torch.zeros((2, 2, d, d))
+    assert torch.equal(fin.cpu(), expect)
+
+
 def test_in_place_state_and_no_final_state(gdn):
     inp = make_prefill(2, 100, 1, 2, 128, 128, "bf16", init_state=True, seed=6)
     dev = to_dev(inp)
