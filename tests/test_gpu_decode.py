@@ -69,6 +69,29 @@ def test_decode_zero_gates(gdn):
     assert_close("state", got_s, ref_state, TOL[torch.bfloat16])
 
 
+def test_decode_max_value_heads(gdn):
+    """4096 value heads over 2048 q/k heads (the largest head count the boundary accepts), two steps: every
+    output finite, and the first and last heads match the oracle (run on those heads alone)."""
+    N, Hqk, Hv, steps = 2, 2048, 4096, 2
+    flush(f"decode max heads N={N} Hqk={Hqk} Hv={Hv}")
+    inp = make_decode(N, Hqk, Hv, 128, 128, steps, "bf16", seed=13)
+    dev = to_dev(inp)
+    state = dev["state"].clone()
+    heads = [0, 1, 2047, 2048, 4094, 4095]
+    qk = [h // (Hv // Hqk) for h in heads]
+    ref_state = f64(inp["state"][:, heads])
+    for t in range(steps):
+        o = gdn.decode_step(dev["q"][t], dev["k"][t], dev["v"][t], dev["g"][t], dev["beta"][t], state)
+        ro, ref_state = oracle_decode(inp["q"][t][:, qk], inp["k"][t][:, qk], inp["v"][t][:, heads],
+                                      inp["g"][t][:, heads], inp["beta"][t][:, heads], ref_state)
+        go = f64(o)
+        assert np.all(np.isfinite(go))
+        assert_close(f"o step {t}", go[:, heads], ro, TOL[torch.bfloat16])
+    gs = f64(state)
+    assert np.all(np.isfinite(gs))
+    assert_close("state", gs[:, heads], ref_state, TOL[torch.bfloat16])
+
+
 def test_decode_full_workload_whole_tensors(gdn, oracle_pool):
     """256 sequences x 32 value heads, 64 separate decode calls updating the 512 MiB state in place: every
     element of o at every step and of the state after step 64 against 64 oracle decode steps per sequence

@@ -196,6 +196,27 @@ def test_rows_without_tokens(gdn, dtype, d, init):
     assert torch.equal(fin.cpu(), expect)
 
 
+def test_max_value_heads(gdn):
+    """The largest head count the boundary accepts, 4096 value heads over 2048 q/k heads, d = 128: a token row
+    of v and o is 1 MB, the largest stride the kernels' 32-bit row offsets take.  Two chunks with a ragged tail;
+    every output is finite, and the first and last heads (the largest offsets) match the oracle element by
+    element (the oracle runs on those heads alone: the heads are independent recurrences)."""
+    Hqk, Hv, T = 2048, 4096, 70
+    flush(f"prefill max heads Hqk={Hqk} Hv={Hv} T={T}")
+    inp = make_prefill(1, T, Hqk, Hv, 128, 128, "bf16", init_state=True, seed=19)
+    o, fin = run_gpu(gdn, inp, scale=0.9)
+    go, gf = f64(o), f64(fin)
+    assert np.all(np.isfinite(go)) and np.all(np.isfinite(gf))
+    heads = [0, 1, 2047, 2048, 4094, 4095]
+    qk = [h // (Hv // Hqk) for h in heads]
+    ro, rf = recurrent(inp["q"][:, :, qk], inp["k"][:, :, qk], inp["v"][:, :, heads], inp["g"][:, :, heads],
+                       inp["beta"][:, :, heads], initial_state=inp["initial_state"][:, heads], scale=0.9)
+    tol = TOL[torch.bfloat16]
+    for i, h in enumerate(heads):
+        assert rel_l2(go[:, :, h], ro[:, :, i]) <= tol, f"o head {h}"
+        assert rel_l2(gf[:, h], rf[:, i]) <= tol, f"state head {h}"
+
+
 def test_in_place_state_and_no_final_state(gdn):
     inp = make_prefill(2, 100, 1, 2, 128, 128, "bf16", init_state=True, seed=6)
     dev = to_dev(inp)
