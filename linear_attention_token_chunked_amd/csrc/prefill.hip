@@ -180,8 +180,10 @@ struct Layout {
   static constexpr size_t sQ = sK + sizeof(T) * C * LDK;
   static constexpr size_t sV = sQ + sizeof(T) * C * LDK;
   static constexpr size_t sKn = sV + sizeof(T) * C * LDV;   // [C][DK] K, column-read copy (bf16)
-  // per-token vectors (VEC_*): exp G, beta, exp(G_C - G), exp G_C (uniform),
-  // G log2(e), and the decay to or from the last token of 16-token tiles 0-2
+  // per-token vectors (VEC_*): exp G, beta, exp(G_C - G) (the first and third
+  // with the state's carried scale folded in), the state's factor and scale
+  // (VEC_EGC lanes 0 and 1), G log2(e), and the decay to or from the last token
+  // of 16-token tiles 0-2
   static constexpr size_t sVec = sKn + (KNAT ? sizeof(T) * C * DK : 0);
   static constexpr size_t stage_bytes = (sVec + VEC_N * 4 * C + 15) / 16 * 16;
   // Single-buffered, written by the producers in segment 1 after the
@@ -457,6 +459,19 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
              min(C, eos - cs), tid, SEG && phi);
   };
 
+  // The state's decay is applied lazily (not in a saving run, whose stored
+  // chunk-start states are the state itself): the consumers hold Ms with
+  // M = 2^L Ms, and the gate-scan wave carries L from chunk to chunk, folding
+  // 2^L into exp(G) (Y = K M and Q M read Ms) and 2^-L into U's decay before the
+  // update, so that Ms' = Ms + K^T (2^(-G - L) U) needs no multiply of the
+  // state; 2^L then takes the chunk's decay exp(G_C).  When L would leave
+  // [-64, 64] the state is renormalised instead: Ms is multiplied by 2^(G_C + L)
+  // (the eager update) and L restarts at 0.  VEC_EGC holds the state's factor
+  // for the chunk (lane 0: 1, or the renormalising factor) and the scale after
+  // it (lane 1), which the end-state writes apply.
+  constexpr bool LAZY = !SAVE;
+  float lazyL = 0.f;  // the gate-scan wave's copy of L
+
   // Stage the chunk's K, Q, V and gates; issue the next chunk's loads.  (The
   // loads sit in this segment because here the producers have slack: the
   // consumers' segment 2 is the longer one.)
@@ -472,11 +487,21 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
       const float Gl = wave_inclusive_sum(live ? fmaxf(pre.g, kGateFloor) : 0.f) * kLog2e;
       const float GlC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, Gl), 63));
       float* vec = reinterpret_cast<float*>(S + L::sVec);
-      vec[VEC_EG * C + lane] = __builtin_amdgcn_exp2f(Gl);
       vec[VEC_BETA * C + lane] = bt;
-      vec[VEC_EGC_G * C + lane] = __builtin_amdgcn_exp2f(GlC - Gl);
-      vec[VEC_EGC * C + lane] = __builtin_amdgcn_exp2f(GlC);
       vec[VEC_GL * C + lane] = Gl;
+      if constexpr (LAZY) {
+        const float aL = GlC + lazyL;                      // log2 of the state's factor after this chunk
+        const bool renorm = !(aL >= -64.f && aL <= 64.f);  // (uniform)
+        const float fac = __builtin_amdgcn_exp2f(aL);
+        vec[VEC_EG * C + lane] = __builtin_amdgcn_exp2f(Gl + lazyL);
+        vec[VEC_EGC_G * C + lane] = __builtin_amdgcn_exp2f(renorm ? GlC - Gl : -Gl - lazyL);
+        vec[VEC_EGC * C + lane] = lane == 1 ? (renorm ? 1.f : fac) : (renorm ? fac : 1.f);
+        lazyL = renorm ? 0.f : aL;
+      } else {
+        vec[VEC_EG * C + lane] = __builtin_amdgcn_exp2f(Gl);
+        vec[VEC_EGC_G * C + lane] = __builtin_amdgcn_exp2f(GlC - Gl);
+        vec[VEC_EGC * C + lane] = lane == 1 ? 1.f : __builtin_amdgcn_exp2f(GlC);
+      }
 #pragma unroll
       for (int b = 0; b < 3; ++b) {  // exp(-|G - G_r|), r = 16b + 15
         const float Gr = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, Gl), 16 * b + 15));
@@ -940,10 +965,12 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
 #pragma unroll
         for (int j = 0; j < NTW; ++j) Z[r][j][s4] *= f;
       }
+    if (eGC != 1.f) {  // (1 in every chunk of a lazy run that does not renormalise)
 #pragma unroll
-    for (int a = 0; a < KT; ++a)
+      for (int a = 0; a < KT; ++a)
 #pragma unroll
-      for (int j = 0; j < NTW; ++j) Ms[a][j] *= eGC;
+        for (int j = 0; j < NTW; ++j) Ms[a][j] *= eGC;
+    }
     const KnCols<DK> kcols(reinterpret_cast<const bf16*>(sKn), olane);  // bf16 only (unused for fp32)
 #pragma unroll
     for (int kgi = 0; kgi < KGC; ++kgi) {
@@ -1124,6 +1151,15 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
     }
   }
 
+  if (consumer && nch > 0) {  // the state's scale after the last chunk
+    const float lam = reinterpret_cast<const float*>(stage(NSTAGE == 2 ? (nch - 1) & 1 : 0) + L::sVec)[VEC_EGC * C + 1];
+    if (lam != 1.f) {
+#pragma unroll
+      for (int a = 0; a < KT; ++a)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) Ms[a][j] *= lam;
+    }
+  }
   if constexpr (SEG) {  // every run's end state, for the scan over segments
     if (consumer) {
       float* e = (phi ? p.seg_phi : p.seg_fin) + ((static_cast<size_t>(seg) * p.batch + b) * p.Hv + h) * DK * DV;
