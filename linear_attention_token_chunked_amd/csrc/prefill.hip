@@ -19,12 +19,14 @@
 // different chunks at the same time:
 //   producers (waves 0-3) prepare chunk n+1 into one half of a double-buffered
 //     LDS stage: K (rows), K^T, V^T, the gates, the Gram products K K^T and
-//     Q K^T masked with the decay (-A below the diagonal, P on and below it),
-//     and the inverses of the four 16x16 diagonal blocks of I + A;
+//     Q K^T masked with the decay (-A below the diagonal blocks, without the
+//     row factor beta, and P on and below the diagonal), and the inverses
+//     T_bb of the four 16x16 diagonal blocks of I + A, times diag(beta_b);
 //   consumers (waves 4-7) run chunk n from the other half, each on its own
-//     16-column tiles of the state: Y = K M, Z, the block forward substitution
-//     U_b = T_bb (Z_b - sum_{m<b} A_bm U_m), the output tile O^T, and the
-//     state update.
+//     16-column tiles of the state: Y = K M, Z' = V - exp(G) Y, the block
+//     forward substitution U_b = T_bb diag(beta_b) (Z'_b - sum_{m<b} A~_bm U_m)
+//     (A_bm = diag(beta_b) A~_bm, so this is T_bb (Z_b - sum A_bm U_m) with
+//     Z = diag(beta) Z'), the output tile O^T, and the state update.
 // Each chunk takes three segments separated by workgroup barriers that order
 // LDS only, so the producers' global loads, issued a chunk ahead, stay in
 // flight.  P, -A and the block inverses are single-buffered: producers write
@@ -560,7 +562,11 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
         for (int s4 = 0; s4 < 4; ++s4) {
           const int j = 16 * GT::tj[t] + 4 * lg + s4;
           const float d = dd[s4];
-          akeep[t][s4] = j < i ? bi * d * kk[t][s4] : 0.f;
+          // The diagonal blocks keep beta (their inverses are formed from
+          // them); below them A_bm = diag(beta_b) A~_bm, and the factor moves
+          // onto the columns of the inverses (see prod_finish).
+          if (GT::ti[t] == GT::tj[t]) akeep[t][s4] = j < i ? bi * d * kk[t][s4] : 0.f;
+          else akeep[t][s4] = d * kk[t][s4];
           if (PROD_P || (PMASK && (GT::pmask >> t & 1))) pkeep[t][s4] = d * qk[t][s4];
         }
         if (GT::ti[t] == GT::tj[t]) {
@@ -595,7 +601,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
             pack4_neg<T>(akeep[t][0], akeep[t][1], akeep[t][2], akeep[t][3]);
     }
   };
-  auto prod_finish = [&]() __attribute__((always_inline)) {
+  auto prod_finish = [&](int s) __attribute__((always_inline)) {
     // With output waves, the inverses are the longest chain of segment 1:
     // they get the top issue priority while they run.
     if constexpr (OUTW) __builtin_amdgcn_s_setprio(3);
@@ -612,6 +618,10 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
 #pragma unroll
       for (int t = 0; t < 4; ++t) x[t] = (4 * q + t == cc) ? 1.f : 0.f;
       unit_lower_inverse_column(x, At, LDA, q, std::make_integer_sequence<int, 15>());
+      // The consumers solve U_b = T_bb diag(beta_b) (Z'_b - sum_{m<b} A~_bm U_m)
+      // with Z' = V - exp(G) K M: beta scales column cc of the inverse here,
+      // once per chunk, instead of every consumer's Z.
+      x *= reinterpret_cast<const float*>(stage(s) + L::sVec)[VEC_BETA * C + 16 * wave + cc];
       // T[4q + t][cc] belongs to operand lane 16 (cc / 4) + 4q + t, element cc % 4
       T* Tb = reinterpret_cast<T*>(smem + L::oTbf);
 #pragma unroll
@@ -665,7 +675,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
         for (int s = 0; s < 4; ++s) d[slane + MM::state_row(a, 0, s) * DV + 16 * j] = from_float<T>(Ms[a][j][s]);
   };
 
-  // seg 1: Y = K M; Z = beta (V - exp(G) Y).  With one state tile per wave the
+  // seg 1: Y = K M; Z' = V - exp(G) Y (beta is applied through the inverses).  With one state tile per wave the
   // state part of the output, O^T = diag-scaled (Q M)^T, is formed here too,
   // next to K M which takes the same operands; with two, holding it until
   // seg 2 would exceed the register budget, and seg 2 forms it instead.
@@ -767,12 +777,9 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
     if constexpr (QM_EARLY) q_times_state(sQ, vec);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float eg[4], bt[4];
+      float eg[4];
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        eg[s4] = vec[VEC_EG * C + 16 * r + 4 * lg + s4];
-        bt[s4] = vec[VEC_BETA * C + 16 * r + 4 * lg + s4];
-      }
+      for (int s4 = 0; s4 < 4; ++s4) eg[s4] = vec[VEC_EG * C + 16 * r + 4 * lg + s4];
 #pragma unroll
       for (int j = 0; j < NTW; ++j) {
         V4 v4;
@@ -781,7 +788,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
         else
           v4 = lds_col4<T>(sV, LDV, 16 * r, (cw * NTW + j) * 16, lane);
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) Z[r][j][s4] = bt[s4] * (to_float(v4[s4]) - eg[s4] * Z[r][j][s4]);
+        for (int s4 = 0; s4 < 4; ++s4) Z[r][j][s4] = to_float(v4[s4]) - eg[s4] * Z[r][j][s4];  // Z' (beta is in T)
       }
     }
   };
@@ -1064,7 +1071,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
       }
       for (int c = 0; c < nch; ++c) {
         const bool more = c + 1 < nch;
-        prod_finish();
+        prod_finish(c & 1);
         lds_barrier();
         if (more) prod_stores(c + 1, (c + 1) & 1);
         lds_barrier();
@@ -1077,7 +1084,7 @@ __global__ __launch_bounds__(64 * (NP + NCW * (OUTW ? 2 : 1))) void prefill_kern
         lds_barrier();
         prod_gram(0);
         lds_barrier();
-        prod_finish();
+        prod_finish(0);
         lds_barrier();
         lds_barrier();
         lds_barrier();
