@@ -32,13 +32,14 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "linear_attention_token_chunked_amd", "csrc")
 
 # Source files of each family of kernels the bench measures.
+# Every file a family's kernels are compiled from counts, the shared headers included.
 SOURCES = {
-    "prefill": ["prefill.hip", "seg.hip", "device_common.hpp", "plan.cpp"],
-    "bwd": ["prefill.hip", "bwd.hip", "device_common.hpp", "plan.cpp"],
-    "decode": ["decode.hip", "lane_sums.hpp"],
-    "verify": ["verify.hip", "lane_sums.hpp"],
-    "epilogue": ["epilogue.hip"],
-    "short_conv": ["conv.hip"],
+    "prefill": ["prefill.hip", "seg.hip", "device_common.hpp", "launch.hpp", "plan.cpp"],
+    "bwd": ["prefill.hip", "bwd.hip", "device_common.hpp", "launch.hpp", "plan.cpp"],
+    "decode": ["decode.hip", "lane_sums.hpp", "device_common.hpp", "launch.hpp"],
+    "verify": ["verify.hip", "lane_sums.hpp", "device_common.hpp", "launch.hpp"],
+    "epilogue": ["epilogue.hip", "device_common.hpp", "launch.hpp"],
+    "short_conv": ["conv.hip", "device_common.hpp", "launch.hpp"],
 }
 # The kernel whose dispatches count the family's calls.
 MAIN = {"prefill": ("prefill", "prefill_seg"), "bwd": ("bwd_dlocal",), "decode": ("decode",), "verify": ("verify",),
