@@ -210,7 +210,8 @@ struct BwdParams {
 template <class T, int DK, int BV>
 struct DsLayout {
   static constexpr int PAD = sizeof(T) == 2 ? 16 : 4;  // row padding: 32 bytes (bf16), 16 (fp32, to fit twice)
-  static constexpr int LDK = DK + PAD, LDB = BV + PAD, LDC = C + PAD, LDD = 16 + PAD, LDF = BV + 4, LDT = 20;
+  static constexpr int LDK = DK + PAD, LDB = BV + PAD, LDC = C + (sizeof(T) == 2 ? 8 : PAD), LDD = 16 + PAD, LDF = BV + 4,
+                       LDT = 20;
   // a chunk's inputs, double-buffered: K, Q, the dO slice, the gate vectors
   static constexpr int iK = 0;
   static constexpr int iQ = iK + C * LDK * sizeof(T);
@@ -494,7 +495,7 @@ __global__ __launch_bounds__(512) void dstate_kernel(BwdParams p) {
 template <class T, int DK, int DV>
 struct DlLayout {
   static constexpr int PAD = 32 / sizeof(T);
-  static constexpr int LDK = DK + PAD, LDV = DV + PAD, LDC = C + PAD;
+  static constexpr int LDK = DK + PAD, LDV = DV + PAD, LDC = C + PAD / 2;
   static constexpr int KTL = DK / 16;             // key-dim tiles (16-column blocks of dq and dk)
   static constexpr int NOT = (C / 16) * KTL / 8;  // dq (and dk) tiles per wavefront
   static constexpr int oQ = 0;
